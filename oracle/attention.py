@@ -1,0 +1,331 @@
+"""Vectorised float64 reference for decode attention (test infrastructure only).
+
+This module is the plain definition of what one decode step computes; the
+package docstring lists the pages cited here and who may import it.
+
+Conventions (the readings of the pages this reference takes):
+
+* One query token per sequence.  The cache of sequence ``b`` holds ``T_b``
+  tokens including the current one, so the query sits at position
+  ``t = T_b - 1`` and full causal attention sees positions ``0..t``
+  [attention-head section 5.3: single-token causal decode, cache holds only the
+  valid tokens up to the current position].
+* Mask ``M``: a position is either visible (adds 0) or masked (adds -inf and
+  drops out of the softmax); there is no other additive bias
+  [attention-head section 1, attention equation; toolsku MHA module,
+  masked_fill with -inf].
+* Query head ``h`` reads KV head ``floor(h / n)`` with ``n = H_q / H_kv``:
+  equal-size groups numbered contiguously [attention-head section 2;
+  toolsku GQA module, ``_repeat_kv`` repeats each KV head n times in a row].
+* Sliding window ``w > 0``: the query at ``t`` sees ``t-w+1 .. t`` (w keys
+  including itself) [attention-head section 3, worked example w=3, row 8 sees
+  6, 7, 8].
+* Ring buffer (the pages say only that a pure sliding-window layer may recycle
+  out-of-window slots in a ring buffer, attention-head section 3): the cache
+  has ``S_cap = T_cap`` slots; ``ring_head[b]`` is the slot that holds the
+  newest position ``t``; position ``j`` lives in slot
+  ``(ring_head[b] - (t - j)) mod S_cap``; resident positions are
+  ``max(0, T_b - S_cap) .. t``; visible = resident and inside the window,
+  where ``window == 0`` means the whole resident set.
+* Softmax scale defaults to ``1/sqrt(d)`` [attention-head section 1].
+* An empty visible set yields ``out = 0`` and ``lse = -inf`` (the pages are
+  silent; chosen so empty partial results merge uniformly).
+* ``lse`` is the natural-log log-sum-exp of the scaled scores.
+"""
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "kv_cache_bytes",
+    "mla_cache_bytes",
+    "mla_explicit_cache_bytes",
+    "visible_positions",
+    "ring_slot",
+    "attend",
+    "gqa_decode_ref",
+    "mla_decode_ref",
+    "mla_explicit_ref",
+    "combine_ref",
+    "partial_ref",
+]
+
+
+# --------------------------------------------------------------------------
+# Byte accounting
+# --------------------------------------------------------------------------
+def kv_cache_bytes(B, T, H_kv, d, s, layers=1):
+    """Bytes of the K and V cache: ``2 * B * T * H_kv * d * s`` per layer.
+
+    [attention-head section 1, the Bytes_KV equation: the factor 2 is K plus V;
+    section 2 restates it for the [batch, head, sequence, head_dim] layout.]
+    """
+    return 2 * B * T * H_kv * d * s * layers
+
+
+def mla_cache_bytes(B, T, r, d_rope, s, layers=1):
+    """Bytes of an MLA latent cache: ``B * T * (r + d_R) * s`` per layer.
+
+    No factor 2: the latent row carries both keys and values, the second term
+    is the shared RoPE key [attention-head section 5.4, Bytes_MLA].
+    """
+    return B * T * (r + d_rope) * s * layers
+
+
+def mla_explicit_cache_bytes(B, T, H, d_c, d_rope, d_v, s, layers=1):
+    """Bytes of caching every head's expanded K and V: ``B*T*H*(d_c+d_R+d_v)*s``.
+
+    [attention-head section 5.4, the element count of the explicit per-head
+    cache used as the comparison point.]
+    """
+    return B * T * H * (d_c + d_rope + d_v) * s * layers
+
+
+# --------------------------------------------------------------------------
+# Index logic
+# --------------------------------------------------------------------------
+def _kv_head_for_query(h, n):
+    """KV head read by query head ``h`` when ``n`` query heads share one.
+
+    [attention-head section 2: equal-size, contiguously numbered groups;
+    toolsku GQA module: ``_repeat_kv`` expands KV head g into query heads
+    g*n .. g*n+n-1.]
+    """
+    return h // n
+
+
+def _window_low(t, window):
+    """First visible position of the query at ``t`` under window ``window``.
+
+    [attention-head section 3: a window of width w keeps the current position
+    and the w-1 before it.]  ``window == 0`` means no window.
+    """
+    if window > 0:
+        return max(0, t - window + 1)
+    return 0
+
+
+def visible_positions(T_b, window=0, ring_capacity=None):
+    """Logical positions visible to the decode query of a length-``T_b`` sequence.
+
+    With ``ring_capacity`` set, only the last ``ring_capacity`` positions are
+    still resident in the ring buffer [attention-head section 3, ring-buffer
+    reuse of out-of-window slots].
+    """
+    if T_b <= 0:
+        return np.zeros(0, dtype=np.int64)
+    t = T_b - 1
+    lo = _window_low(t, window)
+    if ring_capacity is not None:
+        lo = max(lo, T_b - ring_capacity)
+    return np.arange(lo, t + 1, dtype=np.int64)
+
+
+def ring_slot(positions, t, ring_head, capacity):
+    """Slot of logical position(s) ``positions`` in a ring whose newest
+    position ``t`` sits in slot ``ring_head``."""
+    return (ring_head - (t - np.asarray(positions, dtype=np.int64))) % capacity
+
+
+# --------------------------------------------------------------------------
+# The attention definition
+# --------------------------------------------------------------------------
+def attend(q_rows, k_rows, v_rows, scale):
+    """softmax(scale * q K^T) V over an explicit key set, in float64.
+
+    ``q_rows`` [n, d_k], ``k_rows`` [m, d_k], ``v_rows`` [m, d_v].  Returns
+    ``(o [n, d_v], lse [n])``.  With ``m == 0``: ``o = 0``, ``lse = -inf``.
+
+    [attention-head section 1, attention equation, with the mask already
+    applied by passing only the visible keys; the softmax normalises along
+    the key positions.]
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k_rows = np.asarray(k_rows, dtype=np.float64)
+    v_rows = np.asarray(v_rows, dtype=np.float64)
+    n = q_rows.shape[0]
+    d_v = v_rows.shape[1]
+    if k_rows.shape[0] == 0:
+        return np.zeros((n, d_v)), np.full(n, -np.inf)
+    s = scale * (q_rows @ k_rows.T)                      # [n, m]
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    o = (p @ v_rows) / l
+    lse = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def _as_f64(x):
+    if hasattr(x, "detach"):  # a torch tensor: exact upcast through float32
+        x = x.detach().cpu().float().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _as_int(x, B, default):
+    if x is None:
+        return [default] * B
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return [int(v) for v in np.asarray(x).reshape(-1)]
+
+
+def gqa_decode_ref(q, k, v, seq_lens=None, ring_head=None, window=0,
+                   scale=None, batches=None, kv_heads=None):
+    """One decode step of MHA / GQA / MQA attention.
+
+    q [B, H_q, d], k [B, H_kv, T_cap, d], v [B, H_kv, T_cap, d_v].
+    ``seq_lens[b]`` is the logical length T_b (default T_cap); ``ring_head``
+    switches the cache to ring-buffer addressing with T_cap slots;
+    ``window`` is the sliding-window width (0 = full causal, and in ring mode
+    0 = the whole resident set).  Returns ``(out [B, H_q, d_v], lse [B, H_q])``
+    in float64.  ``batches`` / ``kv_heads`` restrict the work to a subset
+    (other entries stay 0 / -inf), for sampled checks on large inputs.
+
+    H_kv = H_q is MHA, H_kv = 1 is MQA, anything between that divides H_q is
+    GQA [attention-head sections 2.1 and 2.2].
+    """
+    q = _as_f64(q)
+    B, H_q, d = q.shape
+    k_shape = tuple(k.shape)
+    _, H_kv, T_cap, d_k = k_shape
+    d_v = tuple(v.shape)[3]
+    if d_k != d:
+        raise ValueError("q and k head dims differ")
+    if H_q % H_kv != 0:
+        raise ValueError("H_q must be divisible by H_kv")
+    if window < 0:
+        raise ValueError("window must be >= 0")
+    if ring_head is not None and window > T_cap:
+        raise ValueError("window larger than the ring")
+    n = H_q // H_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lens = _as_int(seq_lens, B, T_cap)
+    heads = _as_int(ring_head, B, 0) if ring_head is not None else None
+    group_of = np.array([_kv_head_for_query(h, n) for h in range(H_q)])
+
+    out = np.zeros((B, H_q, d_v))
+    lse = np.full((B, H_q), -np.inf)
+    for b in (range(B) if batches is None else batches):
+        T_b = lens[b]
+        if heads is None:
+            if T_b > T_cap:
+                raise ValueError("seq_len exceeds the cache capacity")
+            pos = visible_positions(T_b, window)
+            slots = pos
+        else:
+            pos = visible_positions(T_b, window, ring_capacity=T_cap)
+            slots = ring_slot(pos, T_b - 1, heads[b], T_cap)
+        for g in (range(H_kv) if kv_heads is None else kv_heads):
+            hs = np.nonzero(group_of == g)[0]
+            if hs.size == 0:
+                continue
+            k_rows = _as_f64(k[b, g])[slots]
+            v_rows = _as_f64(v[b, g])[slots]
+            o, l = attend(q[b, hs], k_rows, v_rows, scale)
+            out[b, hs] = o
+            lse[b, hs] = l
+    return out, lse
+
+
+def mla_decode_ref(q, latent, d_c, scale, seq_lens=None, batches=None):
+    """Absorbed MLA decode over a latent cache [B, T_cap, d_c + d_rope].
+
+    Each latent row is ``[c_j | k^R_j]`` and each query row is
+    ``[q~ | q^R]`` (content part first).  The score of position j is
+    ``scale * (q~ . c_j + q^R . k^R_j)`` -- one dot product over the full
+    row -- with a single softmax over the summed scores, and the result is
+    the latent ``z = sum_j p_j c_j`` (the per-head value up-projection is
+    applied after this step) [attention-head section 5.2: keys absorbed into
+    the query, values projected after the weighted sum; section 5.3: the RoPE
+    part adds a second score term and contributes no value].
+
+    ``scale`` has no default: it is ``1/sqrt(d_c_head + d_R)`` with the
+    per-head content-key width, which the latent shape does not carry
+    [attention-head section 5.3: the denominator is not r + d_R].
+    Returns ``(z [B, H, d_c], lse [B, H])``.
+    """
+    q = _as_f64(q)
+    B, H, dk = q.shape
+    _, T_cap, dk2 = tuple(latent.shape)
+    if dk != dk2:
+        raise ValueError("q and latent widths differ")
+    if not (0 < d_c <= dk):
+        raise ValueError("bad d_c")
+    lens = _as_int(seq_lens, B, T_cap)
+    z = np.zeros((B, H, d_c))
+    lse = np.full((B, H), -np.inf)
+    for b in (range(B) if batches is None else batches):
+        T_b = lens[b]
+        if T_b > T_cap:
+            raise ValueError("seq_len exceeds the cache capacity")
+        pos = visible_positions(T_b)
+        rows = _as_f64(latent[b])[pos]
+        o, l = attend(q[b], rows, rows[:, :d_c], scale)
+        z[b] = o
+        lse[b] = l
+    return z, lse
+
+
+def mla_explicit_ref(C, K_rope, q_content, q_rope, U_K, U_V, scale):
+    """Non-absorbed MLA: expand every head's keys and values, then attend.
+
+    C [B, T, r] latents, K_rope [B, T, d_R] shared RoPE keys,
+    q_content [B, H, d_c_head], q_rope [B, H, d_R], U_K [H, r, d_c_head],
+    U_V [H, r, d_v].  Head h uses keys ``[C U_K[h] | K_rope]`` and values
+    ``C U_V[h]`` [attention-head section 5.1, per-head content keys and values
+    from one shared latent; section 5.3, the RoPE key concatenated to the
+    content key].  Full causal over all T positions.  Returns o [B, H, d_v].
+    """
+    C = _as_f64(C)
+    K_rope = _as_f64(K_rope)
+    q_content = _as_f64(q_content)
+    q_rope = _as_f64(q_rope)
+    U_K = _as_f64(U_K)
+    U_V = _as_f64(U_V)
+    B, T, r = C.shape
+    H = q_content.shape[1]
+    d_v = U_V.shape[2]
+    out = np.zeros((B, H, d_v))
+    for b in range(B):
+        for h in range(H):
+            keys = np.concatenate([C[b] @ U_K[h], K_rope[b]], axis=1)
+            vals = C[b] @ U_V[h]
+            qh = np.concatenate([q_content[b, h], q_rope[b, h]])[None, :]
+            o, _ = attend(qh, keys, vals, scale)
+            out[b, h] = o[0]
+    return out
+
+
+# --------------------------------------------------------------------------
+# Split results and their merge
+# --------------------------------------------------------------------------
+def partial_ref(q_rows, k_rows, v_rows, scale):
+    """(o, lse) of attention restricted to one part of the key set; the same
+    definition as ``attend``, named for its use on disjoint key subsets."""
+    return attend(q_rows, k_rows, v_rows, scale)
+
+
+def combine_ref(o_part, lse_part):
+    """Merge results computed over disjoint key subsets.
+
+    o_part [..., S, d_v], lse_part [..., S].  Softmax over a union of disjoint
+    key sets: with ``L = max_s lse_s`` and ``w_s = exp(lse_s - L)``,
+    ``out = sum_s w_s o_s / sum_s w_s`` and ``lse = L + log(sum_s w_s)``;
+    all-empty gives out 0 and lse -inf.  This follows from the attention
+    equation [attention-head section 1]: each part's normaliser is exp(lse_s).
+    """
+    o_part = _as_f64(o_part)
+    lse_part = _as_f64(lse_part)
+    L = lse_part.max(axis=-1, keepdims=True)
+    empty = ~np.isfinite(L)
+    Ls = np.where(empty, 0.0, L)
+    w = np.where(np.isfinite(lse_part), np.exp(lse_part - Ls), 0.0)
+    tot = w.sum(axis=-1, keepdims=True)
+    safe = np.where(empty, 1.0, tot)
+    out = (w[..., None] * o_part).sum(axis=-2) / safe
+    out = np.where(empty, 0.0, out)
+    lse = np.where(empty[..., 0], -np.inf, (Ls + np.log(safe))[..., 0])
+    return out, lse

@@ -1,0 +1,564 @@
+"""Pins of the CPU reference (``oracle/``) to things other than itself.
+
+Each ``check_*`` function states one fact fixed by the pages or by the
+mathematics and raises AssertionError if the reference disagrees.  The
+``test_*`` functions run them; ``test_planted_*`` plants a plausible mistake
+in the reference (on the CPU, through monkeypatch) and asserts that at least
+one pin catches it.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention as A
+from oracle import bruteforce as BF
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- byte sizes
+def check_kv_bytes_golden():
+    g = json.load(open(os.path.join(GOLD, "kv_bytes.json")))
+    for e in g["kv"]:
+        got = oracle.kv_cache_bytes(e["B"], e["T"], e["H_kv"], e["d"], e["s"],
+                                    e["layers"])
+        assert got == e["bytes"], (e["cite"], got)
+    for e in g["mla"]:
+        got = oracle.mla_cache_bytes(e["B"], e["T"], e["r"], e["d_rope"], e["s"])
+        assert got == e["bytes"], (e["cite"], got)
+    for e in g["mla_explicit"]:
+        got = oracle.mla_explicit_cache_bytes(e["B"], e["T"], e["H"], e["d_c"],
+                                              e["d_rope"], e["d_v"], e["s"])
+        assert got == e["bytes"], (e["cite"], got)
+    el = g["mla_elements_per_token"]
+    lat = oracle.mla_cache_bytes(1, 1, 512, 64, 1)
+    exp = oracle.mla_explicit_cache_bytes(1, 1, 128, 128, 64, 128, 1)
+    assert lat == el[0]["value"] and exp == el[1]["value"]
+    assert round(exp / lat, 1) == el[2]["value"]
+
+
+def test_kv_bytes_golden():
+    check_kv_bytes_golden()
+
+
+def test_astro_blog_printed_sizes_are_half_its_formula():
+    """The astro-blog helper multiplies T*H*d*2*dtype_bytes (K and V, bf16)
+    but its printed results (32/8/1 MB for 4096 tokens, 32/8/1 heads, d=128)
+    are half of that; the reference follows the formula, which agrees with
+    attention-head section 1 and the llmdeepdive accounting."""
+    printed_mb = {32: 32, 8: 8, 1: 1}
+    for h, mb in printed_mb.items():
+        got = oracle.kv_cache_bytes(1, 4096, h, 128, 2) / 2**20
+        assert got == 2 * mb
+
+
+# -------------------------------------------------------------- visibility
+def check_window_golden():
+    g = json.load(open(os.path.join(GOLD, "window_example.json")))
+    for e in g["cases"]:
+        got = oracle.visible_positions(e["T_b"], e["window"]).tolist()
+        assert got == e["visible"], (e["cite"], got)
+        bf = [p for _, p in BF.visible_slots_brute(e["T_b"], e["T_b"] + 4,
+                                                    e["window"])]
+        assert bf == e["visible"], (e["cite"], bf)
+
+
+def test_window_golden():
+    check_window_golden()
+
+
+def check_ring_hand_enumerated():
+    """Ring of 4 slots, newest position t=5 in slot 1.  Walking back from the
+    head: slot 1 -> 5, slot 0 -> 4, slot 3 -> 3, slot 2 -> 2 (enumerated by
+    hand); positions 0 and 1 were overwritten."""
+    pos = oracle.visible_positions(6, 0, ring_capacity=4).tolist()
+    assert pos == [2, 3, 4, 5], pos
+    slots = oracle.ring_slot(np.array(pos), 5, 1, 4).tolist()
+    assert slots == [2, 3, 0, 1], slots
+    # window 2 inside the same ring: positions 4, 5 in slots 0, 1
+    pos = oracle.visible_positions(6, 2, ring_capacity=4).tolist()
+    assert pos == [4, 5]
+    # not yet wrapped: T_b=3 with head at slot 3 -> positions 0,1,2 in slots 1,2,3
+    pos = oracle.visible_positions(3, 0, ring_capacity=4).tolist()
+    assert pos == [0, 1, 2]
+    assert oracle.ring_slot(np.array(pos), 2, 3, 4).tolist() == [1, 2, 3]
+    bf = BF.visible_slots_brute(6, 4, 0, ring_head=1)
+    assert bf == [(2, 2), (3, 3), (0, 4), (1, 5)], bf
+
+
+def test_ring_hand_enumerated():
+    check_ring_hand_enumerated()
+
+
+# ------------------------------------------------------------- brute force
+def _tiny_case(rng, B, H_q, H_kv, T_cap, d, d_v=None, ring=False, ragged=True):
+    d_v = d if d_v is None else d_v
+    q = rng.standard_normal((B, H_q, d))
+    k = rng.standard_normal((B, H_kv, T_cap, d))
+    v = rng.standard_normal((B, H_kv, T_cap, d_v))
+    if ring:
+        lens = rng.integers(0, 3 * T_cap, size=B)
+        heads = rng.integers(0, T_cap, size=B)
+    else:
+        lens = rng.integers(0, T_cap + 1, size=B) if ragged else np.full(B, T_cap)
+        heads = None
+    return q, k, v, lens, heads
+
+
+def check_brute_force(seed=0, n_cases=60):
+    rng = _rng(seed)
+    combos = [(1, 1), (2, 1), (4, 2), (6, 3), (8, 2), (8, 8), (6, 1), (4, 4)]
+    for c in range(n_cases):
+        H_q, H_kv = combos[c % len(combos)]
+        B = 1 + c % 2
+        T_cap = int(rng.integers(1, 25))
+        d = int(rng.choice([2, 4, 8]))
+        ring = bool(c % 3 == 2)
+        window = int(rng.choice([0, 1, 2, 3, 5, T_cap]))
+        if ring:
+            window = min(window, T_cap)
+        q, k, v, lens, heads = _tiny_case(rng, B, H_q, H_kv, T_cap, d, ring=ring)
+        scale = float(rng.choice([0.3, 1.0 / math.sqrt(d), 2.0]))
+        o, l = oracle.gqa_decode_ref(q, k, v, lens, heads, window, scale)
+        ob, lb = BF.gqa_decode_brute(q, k, v, lens, heads, window, scale)
+        ob, lb = np.array(ob), np.array(lb)
+        assert np.array_equal(np.isinf(l), np.isinf(lb)), c
+        assert np.allclose(o, ob, rtol=0, atol=1e-12), c
+        fin = np.isfinite(l)
+        assert np.allclose(l[fin], lb[fin], rtol=0, atol=1e-12), c
+
+
+def test_brute_force_agreement():
+    check_brute_force()
+
+
+def check_mla_brute_force(seed=1):
+    rng = _rng(seed)
+    for c in range(12):
+        B, H, T = 1 + c % 2, int(rng.integers(1, 5)), int(rng.integers(1, 12))
+        d_c, d_r = int(rng.choice([2, 4, 6])), int(rng.choice([1, 2, 3]))
+        q = rng.standard_normal((B, H, d_c + d_r))
+        lat = rng.standard_normal((B, T, d_c + d_r))
+        lens = rng.integers(0, T + 1, size=B)
+        z, l = oracle.mla_decode_ref(q, lat, d_c, 0.7, lens)
+        zb, lb = BF.mla_decode_brute(q, lat, d_c, 0.7, lens)
+        assert np.allclose(z, np.array(zb), atol=1e-12)
+        lb = np.array(lb)
+        assert np.array_equal(np.isinf(l), np.isinf(lb))
+        fin = np.isfinite(l)
+        assert np.allclose(l[fin], lb[fin], atol=1e-12)
+
+
+def test_mla_brute_force_agreement():
+    check_mla_brute_force()
+
+
+# --------------------------------------------------------- closed forms
+def check_identical_keys_give_mean(seed=2):
+    """All keys equal -> every visible weight is 1/n_vis -> output is the mean
+    of the visible values, lse = s + ln(n_vis) (from the attention equation)."""
+    rng = _rng(seed)
+    for ring in (False, True):
+        for window in (0, 1, 3, 7):
+            B, H_q, H_kv, T_cap, d = 2, 4, 2, 12, 4
+            q = rng.standard_normal((B, H_q, d))
+            krow = rng.standard_normal(d)
+            k = np.broadcast_to(krow, (B, H_kv, T_cap, d)).copy()
+            v = rng.standard_normal((B, H_kv, T_cap, d))
+            lens = np.array([5, 30]) if ring else np.array([5, 12])
+            heads = np.array([3, 7]) if ring else None
+            o, l = oracle.gqa_decode_ref(q, k, v, lens, heads, window, 0.5)
+            for b in range(B):
+                sl = BF.visible_slots_brute(int(lens[b]), T_cap, window,
+                                            None if heads is None else int(heads[b]))
+                slots = [s for s, _ in sl]
+                for h in range(H_q):
+                    g = h // (H_q // H_kv)
+                    mean = v[b, g, slots].mean(axis=0)
+                    assert np.allclose(o[b, h], mean, atol=1e-13), (ring, window)
+                    s = 0.5 * q[b, h] @ krow
+                    assert abs(l[b, h] - (s + math.log(len(slots)))) < 1e-12
+
+
+def test_identical_keys_give_mean():
+    check_identical_keys_give_mean()
+
+
+def check_single_visible_key(seed=3):
+    """One visible key -> weight exactly 1 -> output equals that value row."""
+    rng = _rng(seed)
+    q = rng.standard_normal((1, 4, 8))
+    k = rng.standard_normal((1, 2, 10, 8))
+    v = rng.standard_normal((1, 2, 10, 8))
+    o, _ = oracle.gqa_decode_ref(q, k, v, np.array([1]))          # T_b = 1
+    assert np.array_equal(o[0, :2], np.repeat(v[0, 0, :1], 2, 0))
+    assert np.array_equal(o[0, 2:], np.repeat(v[0, 1, :1], 2, 0))
+    o, _ = oracle.gqa_decode_ref(q, k, v, np.array([7]), window=1)  # w = 1
+    assert np.array_equal(o[0, 0], v[0, 0, 6]) and np.array_equal(o[0, 3], v[0, 1, 6])
+    o, _ = oracle.gqa_decode_ref(q, k, v, np.array([25]), np.array([4]), window=1)
+    assert np.array_equal(o[0, 1], v[0, 0, 4]) and np.array_equal(o[0, 2], v[0, 1, 4])
+
+
+def test_single_visible_key():
+    check_single_visible_key()
+
+
+def check_two_key_closed_form(seed=4):
+    """Two visible keys: weights are the logistic of the score difference,
+    evaluated here in its overflow-free form for large score gaps."""
+    rng = _rng(seed)
+    for scale in (0.1, 1.0, 100.0, 1e4):
+        q = rng.standard_normal((1, 1, 3))
+        k = rng.standard_normal((1, 1, 2, 3))
+        v = rng.standard_normal((1, 1, 2, 3))
+        o, l = oracle.gqa_decode_ref(q, k, v, scale=scale)
+        s0, s1 = scale * q[0, 0] @ k[0, 0, 0], scale * q[0, 0] @ k[0, 0, 1]
+        x = s0 - s1
+        w0 = 1 / (1 + math.exp(-x)) if x >= 0 else math.exp(x) / (1 + math.exp(x))
+        want = w0 * v[0, 0, 0] + (1 - w0) * v[0, 0, 1]
+        assert np.allclose(o[0, 0], want, rtol=1e-12, atol=1e-12), scale
+        big = max(s0, s1)
+        want_l = big + math.log1p(math.exp(-abs(x)))
+        assert abs(l[0, 0] - want_l) <= 1e-12 * max(1.0, abs(want_l)), scale
+
+
+def test_two_key_closed_form():
+    check_two_key_closed_form()
+
+
+def test_large_scores_stay_finite():
+    """Scale 100 on N(0,1) data: scores reach the hundreds; the reference must
+    not overflow and must agree with the scalar loops."""
+    rng = _rng(5)
+    q, k, v, lens, _ = _tiny_case(rng, 2, 4, 2, 20, 8, ragged=False)
+    o, l = oracle.gqa_decode_ref(q, k, v, lens, scale=100.0)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    ob, lb = BF.gqa_decode_brute(q, k, v, lens, scale=100.0)
+    assert np.allclose(o, ob, atol=1e-12) and np.allclose(l, lb, rtol=1e-14)
+
+
+def test_empty_visible_set():
+    q = np.ones((2, 2, 4))
+    k = np.ones((2, 1, 5, 4))
+    v = np.ones((2, 1, 5, 4))
+    o, l = oracle.gqa_decode_ref(q, k, v, np.array([0, 3]))
+    assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
+    assert np.allclose(o[1], 1.0) and np.all(np.isfinite(l[1]))
+
+
+# ---------------------------------------------------- reductions / invariants
+def check_repeat_kv_equivalence(seed=6):
+    """GQA equals MHA on K/V whose heads are repeated n times in a row (the
+    toolsku ``_repeat_kv`` expansion)."""
+    rng = _rng(seed)
+    for H_q, H_kv in ((8, 2), (6, 3), (4, 1), (24, 4)):
+        n = H_q // H_kv
+        q, k, v, lens, _ = _tiny_case(rng, 2, H_q, H_kv, 16, 8)
+        o, l = oracle.gqa_decode_ref(q, k, v, lens, window=5)
+        kr = np.repeat(k, n, axis=1)
+        vr = np.repeat(v, n, axis=1)
+        o2, l2 = oracle.gqa_decode_ref(q, kr, vr, lens, window=5)
+        assert np.allclose(o, o2, atol=1e-13) and np.allclose(l, l2, atol=1e-13)
+
+
+def test_repeat_kv_equivalence():
+    check_repeat_kv_equivalence()
+
+
+def check_mqa_and_mha_degenerate(seed=7):
+    """MQA (one KV head) equals MHA whose KV heads are all that head; GQA with
+    as many KV heads as query heads is MHA, head by head."""
+    rng = _rng(seed)
+    q, k, v, lens, _ = _tiny_case(rng, 2, 6, 1, 10, 4)
+    o, _ = oracle.gqa_decode_ref(q, k, v, lens)
+    o2, _ = oracle.gqa_decode_ref(q, np.repeat(k, 6, 1), np.repeat(v, 6, 1), lens)
+    assert np.allclose(o, o2, atol=1e-13)
+    q, k, v, lens, _ = _tiny_case(rng, 1, 3, 3, 10, 4)
+    o, _ = oracle.gqa_decode_ref(q, k, v, lens)
+    for h in range(3):
+        oh, _ = oracle.gqa_decode_ref(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], lens)
+        assert np.allclose(o[:, h], oh[:, 0], atol=1e-13)
+
+
+def test_mqa_and_mha_degenerate():
+    check_mqa_and_mha_degenerate()
+
+
+def check_torch_sdpa(seed=8):
+    """Compare with torch's own scaled_dot_product_attention (float64, CPU,
+    grouped heads, boolean visibility mask): an independent library routine."""
+    rng = _rng(seed)
+    for H_q, H_kv, window in ((8, 2, 0), (6, 3, 4), (4, 4, 0), (4, 1, 2)):
+        q, k, v, lens, _ = _tiny_case(rng, 2, H_q, H_kv, 18, 8, ragged=False)
+        lens = np.array([18, 11])
+        o, _ = oracle.gqa_decode_ref(q, k, v, lens, window=window, scale=0.4)
+        mask = np.zeros((2, 1, 1, 18), dtype=bool)
+        for b in range(2):
+            t = lens[b] - 1
+            for j in range(18):
+                mask[b, 0, 0, j] = j <= t and (window == 0 or t - j < window)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[:, :, None, :], torch.from_numpy(k),
+            torch.from_numpy(v), attn_mask=torch.from_numpy(mask),
+            scale=0.4, enable_gqa=True)[:, :, 0, :].numpy()
+        assert np.allclose(o, ref, atol=1e-12), (H_q, H_kv, window)
+
+
+def test_torch_sdpa():
+    check_torch_sdpa()
+
+
+def check_split_invariance(seed=9):
+    """Results over disjoint parts of the key set, merged by the log-sum-exp
+    rule, equal the single pass -- for any partition, empty parts included."""
+    rng = _rng(seed)
+    for trial in range(20):
+        n, m, d = 3, int(rng.integers(1, 40)), 5
+        qr = rng.standard_normal((n, d))
+        kr = rng.standard_normal((m, d))
+        vr = rng.standard_normal((m, d))
+        o, l = A.attend(qr, kr, vr, 0.6)
+        S = int(rng.integers(1, 9))
+        cuts = np.sort(rng.integers(0, m + 1, size=S - 1))
+        bounds = [0, *cuts.tolist(), m]
+        perm = rng.permutation(m) if trial % 2 else np.arange(m)
+        op, lp = [], []
+        for s in range(S):
+            idx = perm[bounds[s]:bounds[s + 1]]
+            a, b = oracle.partial_ref(qr, kr[idx], vr[idx], 0.6)
+            op.append(a)
+            lp.append(b)
+        op = np.stack(op, axis=1)[None]      # [1, n, S, d]
+        lp = np.stack(lp, axis=1)[None]      # [1, n, S]
+        oc, lc = oracle.combine_ref(op, lp)
+        assert np.allclose(oc[0], o, atol=1e-13) and np.allclose(lc[0], l, atol=1e-13)
+        ob, lb = BF.combine_brute(op, lp)
+        assert np.allclose(np.array(ob)[0], o, atol=1e-13)
+        assert np.allclose(np.array(lb)[0], l, atol=1e-13)
+    oc, lc = oracle.combine_ref(np.ones((1, 1, 3, 2)), np.full((1, 1, 3), -np.inf))
+    assert np.all(oc == 0) and np.all(np.isneginf(lc))
+
+
+def test_split_invariance():
+    check_split_invariance()
+
+
+def check_ring_equals_linear(seed=10):
+    """A ring cache unrolled into a linear cache gives the same result; the
+    unrolling here places position j at index j directly from the slot walk."""
+    rng = _rng(seed)
+    for trial in range(30):
+        cap = int(rng.integers(1, 12))
+        T_b = int(rng.integers(0, 3 * cap + 2))
+        head = int(rng.integers(0, cap))
+        window = int(rng.choice([0, 1, 2, cap]))
+        window = min(window, cap)
+        q = rng.standard_normal((1, 2, 4))
+        k = rng.standard_normal((1, 1, cap, 4))
+        v = rng.standard_normal((1, 1, cap, 4))
+        o, l = oracle.gqa_decode_ref(q, k, v, np.array([T_b]), np.array([head]),
+                                     window)
+        L = max(T_b, 1)
+        kl = np.full((1, 1, L, 4), 1e6)       # positions no longer resident
+        vl = np.full((1, 1, L, 4), np.nan)
+        for slot, pos in BF.visible_slots_brute(T_b, cap, 0, ring_head=head):
+            kl[0, 0, pos] = k[0, 0, slot]
+            vl[0, 0, pos] = v[0, 0, slot]
+        o2, l2 = oracle.gqa_decode_ref(q, kl, vl, np.array([T_b]),
+                                       window=window if window else cap)
+        assert np.allclose(o, o2, atol=1e-13, equal_nan=False), trial
+        assert np.allclose(l, l2, atol=1e-13), trial
+
+
+def test_ring_equals_linear():
+    check_ring_equals_linear()
+
+
+def check_integer_recovery(seed=11):
+    """Index logic to the bit: zero keys make every visible weight exactly
+    1/n_vis, and V[slot, i] = bit i of the logical position in that slot (last
+    column 1).  Then out[i] * n_vis rounds to the count of visible positions
+    with bit i set and exp(lse) to n_vis -- integers fixed by counting."""
+    rng = _rng(seed)
+    d = 16
+    for trial in range(40):
+        ring = trial % 2 == 1
+        cap = int(rng.integers(1, 200))
+        T_b = int(rng.integers(0, 3 * cap + 1)) if ring else int(rng.integers(0, cap + 1))
+        window = int(rng.choice([0, 1, 7, cap]))
+        if ring:
+            window = min(window, cap)
+        head = int(rng.integers(0, cap)) if ring else None
+        k = np.zeros((1, 1, cap, d))
+        v = np.zeros((1, 1, cap, d))
+        for slot in range(cap):
+            pos = BF._slot_position(slot, T_b - 1, head, cap) if ring else slot
+            for i in range(d - 1):
+                v[0, 0, slot, i] = (pos >> i) & 1 if pos >= 0 else 0
+            v[0, 0, slot, d - 1] = 1.0
+        q = rng.standard_normal((1, 1, d))
+        o, l = oracle.gqa_decode_ref(q, k, v, np.array([T_b]),
+                                     None if head is None else np.array([head]), window)
+        t = T_b - 1
+        lo = 0 if not window else t - window + 1
+        if ring:
+            lo = max(lo, T_b - cap)
+        want = list(range(max(lo, 0), t + 1))
+        n_vis = len(want)
+        if n_vis == 0:
+            assert np.all(o == 0) and np.isneginf(l[0, 0])
+            continue
+        counts = [sum((p >> i) & 1 for p in want) for i in range(d - 1)] + [n_vis]
+        got = np.rint(o[0, 0] * n_vis).astype(int).tolist()
+        assert got == counts, (trial, got, counts)
+        assert int(round(math.exp(l[0, 0]))) == n_vis
+
+
+def test_integer_recovery():
+    check_integer_recovery()
+
+
+# ----------------------------------------------------------------- MLA pins
+def check_mla_absorbed_equals_explicit(seed=12):
+    """Absorbed MLA (query times U_K^T against the latent, values projected
+    after the weighted sum) equals explicit per-head K/V attention
+    [attention-head sections 5.2-5.3], with scale 1/sqrt(d_c_head + d_R)."""
+    rng = _rng(seed)
+    B, T, H, r, dch, dR, dv = 2, 9, 3, 16, 6, 4, 5
+    C = rng.standard_normal((B, T, r))
+    KR = rng.standard_normal((B, T, dR))
+    qc = rng.standard_normal((B, H, dch))
+    qr = rng.standard_normal((B, H, dR))
+    UK = rng.standard_normal((H, r, dch))
+    UV = rng.standard_normal((H, r, dv))
+    scale = 1 / math.sqrt(dch + dR)
+    explicit = oracle.mla_explicit_ref(C, KR, qc, qr, UK, UV, scale)
+    qt = np.einsum("bhc,hrc->bhr", qc, UK)            # q~ = q^C U_K^T
+    q = np.concatenate([qt, qr], axis=2)
+    lat = np.concatenate([C, KR], axis=2)
+    z, _ = oracle.mla_decode_ref(q, lat, r, scale)
+    absorbed = np.einsum("bhr,hrv->bhv", z, UV)        # o = z U_V
+    assert np.allclose(absorbed, explicit, atol=1e-12, rtol=1e-12)
+
+
+def test_mla_absorbed_equals_explicit():
+    check_mla_absorbed_equals_explicit()
+
+
+def check_mla_is_shared_head_attention(seed=13):
+    """MLA decode is the single-KV-head attention with K = the whole latent
+    row and V = its first d_c columns."""
+    rng = _rng(seed)
+    q = rng.standard_normal((2, 4, 10))
+    lat = rng.standard_normal((2, 7, 10))
+    lens = np.array([7, 3])
+    z, l = oracle.mla_decode_ref(q, lat, 8, 0.3, lens)
+    o, l2 = oracle.gqa_decode_ref(q, lat[:, None], lat[:, None, :, :8], lens,
+                                  scale=0.3)
+    assert np.allclose(z, o, atol=1e-13) and np.allclose(l, l2, atol=1e-13)
+
+
+def test_mla_is_shared_head_attention():
+    check_mla_is_shared_head_attention()
+
+
+# ------------------------------------------------------ planted mistakes
+ALL_CHECKS = [
+    check_kv_bytes_golden, check_window_golden, check_ring_hand_enumerated,
+    check_brute_force, check_mla_brute_force, check_identical_keys_give_mean,
+    check_single_visible_key, check_two_key_closed_form,
+    check_repeat_kv_equivalence, check_mqa_and_mha_degenerate, check_torch_sdpa,
+    check_split_invariance, check_ring_equals_linear, check_integer_recovery,
+    check_mla_absorbed_equals_explicit, check_mla_is_shared_head_attention,
+]
+
+
+def _caught():
+    for chk in ALL_CHECKS:
+        try:
+            chk()
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+MUTANTS = {
+    "group_interleaved": ("_kv_head_for_query", lambda h, n: h % max(1, n)),
+    "window_off_by_one": ("_window_low", lambda t, w: max(0, t - w) if w > 0 else 0),
+    "window_too_narrow": ("_window_low", lambda t, w: max(0, t - w + 2) if w > 0 else 0),
+    "ring_wrong_direction": ("ring_slot",
+                             lambda p, t, h, c: (h + (t - np.asarray(p))) % c),
+    "kv_bytes_no_factor_2": ("kv_cache_bytes",
+                             lambda B, T, H, d, s, layers=1: B * T * H * d * s * layers),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_index_mistakes_are_caught(monkeypatch, name):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(A, attr, fn)
+    if attr == "kv_cache_bytes":
+        monkeypatch.setattr(oracle, attr, fn)
+    if attr == "ring_slot":
+        monkeypatch.setattr(oracle, attr, fn)
+    assert _caught(), name
+
+
+def _attend_no_max(q_rows, k_rows, v_rows, scale):
+    q_rows, k_rows, v_rows = (np.asarray(x, float) for x in (q_rows, k_rows, v_rows))
+    if k_rows.shape[0] == 0:
+        return np.zeros((q_rows.shape[0], v_rows.shape[1])), np.full(q_rows.shape[0], -np.inf)
+    with np.errstate(over="ignore", invalid="ignore"):
+        p = np.exp(scale * q_rows @ k_rows.T)
+        l = p.sum(1, keepdims=True)
+        return (p @ v_rows) / l, np.log(l)[:, 0]
+
+
+def _attend_wrong_sign(q_rows, k_rows, v_rows, scale):
+    o, l = oracle.partial_ref(q_rows, -np.asarray(k_rows), v_rows, scale)
+    return o, l
+
+
+def _attend_no_scale(q_rows, k_rows, v_rows, scale):
+    return oracle.partial_ref(q_rows, k_rows, v_rows, 1.0)
+
+
+def _attend_transposed_value(q_rows, k_rows, v_rows, scale):
+    v = np.asarray(v_rows, float)
+    return oracle.partial_ref(q_rows, k_rows, v[::-1], scale)
+
+
+@pytest.mark.parametrize("mutant", [_attend_no_max, _attend_wrong_sign,
+                                    _attend_no_scale, _attend_transposed_value])
+def test_planted_arithmetic_mistakes_are_caught(monkeypatch, mutant):
+    # partial_ref keeps the true definition so that the mutant differs from it
+    true_attend = A.attend
+    monkeypatch.setattr(A, "partial_ref", true_attend)
+    monkeypatch.setattr(oracle, "partial_ref", true_attend)
+    monkeypatch.setattr(A, "attend", mutant)
+    assert _caught(), mutant.__name__
+
+
+def test_planted_mla_value_columns_are_caught(monkeypatch):
+    orig = A.mla_decode_ref
+
+    def wrong(q, latent, d_c, scale, seq_lens=None, batches=None):
+        lat = np.asarray(latent, float)
+        rolled = np.concatenate([lat[..., -d_c:], lat[..., :-d_c]], axis=-1)
+        z, l = orig(q, lat, d_c, scale, seq_lens, batches)
+        z2, _ = orig(q, rolled, d_c, scale, seq_lens, batches)
+        return z2 if lat.shape[-1] > d_c else z, l
+
+    monkeypatch.setattr(A, "mla_decode_ref", wrong)
+    monkeypatch.setattr(oracle, "mla_decode_ref", wrong)
+    assert _caught()
