@@ -1,0 +1,239 @@
+"""Decode-attention benchmark: KV-read GB/s (% of HBM peak) and us/step.
+
+One step = one library call = one layer's decode attention for every
+sequence of the batch.  Inputs are seeded synthetic tensors drawn on the GPU
+(``synth``), already resident in HBM when timing starts; several copies of
+the cache are rotated so the working set exceeds the 256 MB Infinity Cache.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+prints ONE JSON line.  The default workload is the Llama-3-8B-shaped GQA
+layer (B=32, 32 query heads over 8 KV heads, d=128, T=4096, bf16).
+
+``value`` = algorithmic KV bytes per step / measured step time, where the
+algorithmic bytes are 2 * s * d * H_kv * (visible positions summed over the
+batch) -- only what the method must read (xuesongtap "attention-head" note,
+section 1, Bytes_KV), never masked or padded capacity.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+METRIC = "decode-attention KV-read GB/s (% of HBM peak) and µs/step per layer"
+DEFAULT_WORKLOAD = "llama3_8b_gqa_t4096"
+KERNEL_SOURCES = ["gqa_valu.hip", "visible.h", "device_common.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--rotate-bytes", type=float, default=1.0,
+                    help="GiB of rotating cache copies (defeats the MALL)")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def visible_counts(w, seq_lens):
+    """Visible positions per sequence, from the lengths, window and ring."""
+    import numpy as np
+    T_cap, window, ring = w["T_cap"], w.get("window", 0), bool(w.get("ring"))
+    lens = (np.full(w["B"], T_cap) if seq_lens is None
+            else seq_lens.cpu().numpy().astype(np.int64))
+    lens = np.maximum(lens, 0)
+    if not ring:
+        lens = np.minimum(lens, T_cap)
+    lo = np.zeros_like(lens)
+    if window > 0:
+        lo = np.maximum(lo, lens - window)
+    if ring:
+        lo = np.maximum(lo, lens - T_cap)
+    return lens - lo
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_attention_kv_attn_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload):
+    """HBM bytes per launch from committed rocprofv3 --pmc results, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, seconds):
+    """Time the float64 oracle on the host over a bounded sample of the same
+    workload: whole (b, KV-head) units, repeated until `seconds` have passed."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    q = inp["q"].cpu()
+    k = inp["k"].cpu()
+    v = inp["v"].cpu()
+    sl = None if inp["seq_lens"] is None else inp["seq_lens"].cpu()
+    rh = None if inp["ring_head"] is None else inp["ring_head"].cpu()
+    vis = visible_counts(w, sl)
+    s = 2 if w.get("dtype", "bf16") == "bf16" else 4
+    unit_bytes = 2 * s * w["d"]
+    B, H_kv = w["B"], w["H_kv"]
+    units = [(b, g) for b in range(B) for g in range(H_kv)]
+    done_bytes = 0
+    n_units = 0
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        b, g = units[i % len(units)]
+        oracle.gqa_decode_ref(q, k, v, sl, rh, inp["window"], inp["scale"],
+                              batches=[b], kv_heads=[g])
+        done_bytes += unit_bytes * int(vis[b])
+        n_units += 1
+        i += 1
+        if time.perf_counter() - t0 >= seconds and n_units >= 1:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_units} (sequence, KV-head) units of {w['name']} "
+                      f"({len(units)} per step) in {dt:.1f} s, float64 numpy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path runs on a single GPU).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import decode_attention_kv_attn_amd as L
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.workload(args.workload)
+    if w["kind"] != "gqa":
+        raise SystemExit("only GQA-family workloads are benchmarked here")
+    print(f"bench: workload {w['name']}: drawing inputs", file=sys.stderr, flush=True)
+    inp = synth.gqa_inputs(w, dev)
+    s = 2 if w.get("dtype", "bf16") == "bf16" else 4
+    kv_bytes_cap = inp["k"].numel() * s * 2
+    R = max(1, math.ceil(args.rotate_bytes * 2**30 / kv_bytes_cap))
+    ks = [inp["k"]] + [inp["k"].clone() for _ in range(R - 1)]
+    vs = [inp["v"]] + [inp["v"].clone() for _ in range(R - 1)]
+    B, H_q, H_kv, d, T = w["B"], w["H_q"], w["H_kv"], w["d"], w["T_cap"]
+    vis = visible_counts(w, inp["seq_lens"])
+    alg_bytes = int(2 * s * d * H_kv * int(vis.sum()))
+    out = torch.empty(B, H_q, d, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, H_q, dtype=torch.float32, device=dev)
+    dt_code = L.ATTN_BF16 if s == 2 else L.ATTN_F32
+    ring = inp["ring_head"] is not None
+    S = L.attn_decode_gqa_splits(B, H_q, H_kv, T, d, dt_code, inp["window"],
+                                 ring, args.num_splits)
+    wsb = L.attn_decode_gqa_workspace_bytes(B, H_q, H_kv, T, d, dt_code,
+                                            inp["window"], ring, args.num_splits)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        L.attn_decode_gqa(inp["q"], ks[i % R], vs[i % R], inp["seq_lens"],
+                          inp["ring_head"], inp["window"], inp["scale"],
+                          args.num_splits, out=out, lse=lse, workspace=ws)
+
+    print(f"bench: {R} cache copies, {S} split(s); warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per_call = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    ms_per_step = total_ms / args.steps
+    call_ms = float(per_call.mean())
+    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_bytes / (call_ms * 1e-3) / 1e9
+    print(f"bench: {ms_per_step * 1e3:.1f} us/step, call {call_ms * 1e3:.1f} us "
+          f"(median {np.median(per_call) * 1e3:.1f}), {value:.0f} GB/s",
+          file=sys.stderr, flush=True)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if s == 2 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w["name"], "B": B, "H_q": H_q, "H_kv": H_kv,
+                   "d": d, "T": T, "window": inp["window"], "ring": ring,
+                   "splits": S, "cache_copies": R,
+                   "kv_bytes_per_step": alg_bytes},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profile(w["name"]),
+            "kernel": "gqa_decode_valu" + ("" if S == 1 else " + lse_combine"),
+            "kernel_us": round(call_ms * 1e3, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+"""Python binding of the MI355X decode-attention library (``libattn_decode.so``).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, passes their device pointers and the current HIP stream to
+the C ABI declared in ``include/attn_decode.h``, and raises on a non-zero
+status.  All arithmetic runs in the library's HIP kernels; there is no
+fallback -- if the shared library is missing, every call raises.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "ATTN_F32", "ATTN_BF16", "AttnError", "library", "library_path",
+    "attn_decode_gqa", "attn_decode_mla", "attn_combine",
+    "attn_decode_gqa_splits", "attn_decode_gqa_workspace_bytes",
+    "attn_decode_mla_splits", "attn_decode_mla_workspace_bytes",
+    "attn_decode_workspace_bytes", "attn_status_string",
+]
+
+ATTN_F32 = 0
+ATTN_BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libattn_decode.so")
+_LIB = None
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "attn_decode_gqa": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                             _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "attn_decode_gqa_splits": (_i, [_i] * 9),
+    "attn_decode_gqa_workspace_bytes": (_sz, [_i] * 9),
+    "attn_decode_mla": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
+                             _i, _vp, _sz, _vp]),
+    "attn_decode_mla_splits": (_i, [_i] * 6),
+    "attn_decode_mla_workspace_bytes": (_sz, [_i] * 6),
+    "attn_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
+    "attn_decode_workspace_bytes": (_sz, [_i] * 4),
+    "attn_status_string": (ctypes.c_char_p, [_i]),
+}
+
+
+class AttnError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: status {status} "
+                         f"({library().attn_status_string(status).decode()})")
+
+
+def library():
+    """The loaded ``libattn_decode.so`` (ctypes handle); raises if absent."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                f"{library_path} is missing: build it with "
+                "`python -m decode_attention_kv_attn_amd.build`")
+        lib = ctypes.CDLL(library_path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, st):
+    if st != 0:
+        raise AttnError(fn, st)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need_dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def attn_decode_gqa_splits(B, H_q, H_kv, T_cap, d, dtype, window=0, ring=False,
+                           num_splits=0):
+    return library().attn_decode_gqa_splits(B, H_q, H_kv, T_cap, d, dtype,
+                                            window, int(bool(ring)), num_splits)
+
+
+def attn_decode_gqa_workspace_bytes(B, H_q, H_kv, T_cap, d, dtype, window=0,
+                                    ring=False, num_splits=0):
+    return library().attn_decode_gqa_workspace_bytes(
+        B, H_q, H_kv, T_cap, d, dtype, window, int(bool(ring)), num_splits)
+
+
+def attn_decode_workspace_bytes(B, H, d_v, num_splits):
+    return library().attn_decode_workspace_bytes(B, H, d_v, num_splits)
+
+
+def attn_status_string(status):
+    return library().attn_status_string(status).decode()
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return workspace
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def attn_decode_gqa(q, k, v, seq_lens=None, ring_head=None, window=0,
+                    scale=None, num_splits=0, out=None, lse=None,
+                    workspace=None, want_lse=True, stream=None):
+    """One decode step of MHA/GQA/MQA attention.
+
+    q [B, H_q, d], k/v [B, H_kv, T_cap, d] (float32 or bfloat16, same dtype),
+    seq_lens / ring_head int32 [B] or None.  Returns ``(out, lse)`` float32
+    tensors ([B, H_q, d], [B, H_q] or None).  See include/attn_decode.h.
+    """
+    _need_dev(q, k, v, seq_lens, ring_head, out, lse)
+    B, H_q, d = q.shape
+    _, H_kv, T_cap, _ = k.shape
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    ring = ring_head is not None
+    nbytes = attn_decode_gqa_workspace_bytes(B, H_q, H_kv, T_cap, d, dt,
+                                             window, ring, num_splits)
+    if nbytes == 2**64 - 1:
+        nbytes = 0  # invalid arguments: the call below reports the status
+    workspace = _workspace(nbytes, q.device, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = library().attn_decode_gqa(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seq_lens),
+        _ptr(ring_head), B, H_q, H_kv, T_cap, d, dt, window,
+        0.0 if scale is None else float(scale), num_splits, _ptr(workspace),
+        ws_bytes, _stream(stream, q.device))
+    _check("attn_decode_gqa", st)
+    return out, lse
+
+
+def attn_decode_mla_splits(B, H, T_cap, d_c, d_rope, num_splits=0):
+    return library().attn_decode_mla_splits(B, H, T_cap, d_c, d_rope, num_splits)
+
+
+def attn_decode_mla_workspace_bytes(B, H, T_cap, d_c, d_rope, num_splits=0):
+    return library().attn_decode_mla_workspace_bytes(B, H, T_cap, d_c, d_rope,
+                                                     num_splits)
+
+
+def attn_decode_mla(q, latent, d_c, scale, seq_lens=None, num_splits=0,
+                    out=None, lse=None, workspace=None, want_lse=True,
+                    stream=None):
+    """Absorbed MLA decode: q [B, H, d_c+d_rope], latent [B, T_cap, d_c+d_rope]
+    (bfloat16).  Returns ``(z [B, H, d_c], lse [B, H])`` float32."""
+    _need_dev(q, latent, seq_lens, out, lse)
+    B, H, dk = q.shape
+    _, T_cap, _ = latent.shape
+    d_rope = dk - d_c
+    if out is None:
+        out = torch.empty((B, H, d_c), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    nbytes = attn_decode_mla_workspace_bytes(B, H, T_cap, d_c, d_rope, num_splits)
+    if nbytes == 2**64 - 1:
+        nbytes = 0
+    workspace = _workspace(nbytes, q.device, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = library().attn_decode_mla(
+        _ptr(q), _ptr(latent), _ptr(out), _ptr(lse), _ptr(seq_lens), B, H,
+        T_cap, d_c, d_rope, float(scale), num_splits, _ptr(workspace), ws_bytes,
+        _stream(stream, q.device))
+    _check("attn_decode_mla", st)
+    return out, lse
+
+
+def attn_combine(o_part, lse_part, out=None, lse=None, want_lse=True,
+                 stream=None):
+    """Merge split results: o_part [B, H, S, d_v], lse_part [B, H, S]."""
+    _need_dev(o_part, lse_part, out, lse)
+    B, H, S, d_v = o_part.shape
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=torch.float32, device=o_part.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=o_part.device)
+    st = library().attn_combine(_ptr(o_part), _ptr(lse_part), _ptr(out),
+                                _ptr(lse), B, H, S, d_v,
+                                _stream(stream, o_part.device))
+    _check("attn_combine", st)
+    return out, lse
+
+
+def default_scale(d):
+    """1/sqrt(d), the default softmax scale of the attention equation."""
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,216 @@
+// Host side of the C ABI declared in include/attn_decode.h: argument checks
+// (host values only, before any HIP call), split planning, launches.
+
+#include <math.h>
+#include <stdlib.h>
+
+#include "../../include/attn_decode.h"
+#include "internal.h"
+
+namespace attn {
+namespace {
+
+inline bool aligned(const void* p, size_t a) {
+  return ((uintptr_t)p % a) == 0;
+}
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Waves the planner aims to keep resident over the grid before it cuts the
+// visible range into more splits (8 per CU: two per SIMD).  Overridable for
+// tuning sweeps through ATTN_DECODE_TARGET_WAVES.
+int target_waves() {
+  static const int v = [] {
+    const char* e = getenv("ATTN_DECODE_TARGET_WAVES");
+    const int x = e ? atoi(e) : 0;
+    return x > 0 ? x : kNumCUs * 8;
+  }();
+  return v;
+}
+
+struct GqaPlan {
+  int N;            // heads per work item
+  int head_chunks;  // work items per KV head along the heads
+  int S;            // splits
+  int chunk;        // positions per split
+  int waves;        // waves per work group
+  size_t ws_bytes;  // workspace needed
+};
+
+// Largest number of positions any sequence can have visible.
+int max_visible(int T_cap, int window, int ring) {
+  if (ring) return window > 0 ? window : T_cap;
+  return window > 0 ? (window < T_cap ? window : T_cap) : T_cap;
+}
+
+int check_gqa_shape(int B, int H_q, int H_kv, int T_cap, int d, int dtype,
+                    int window, int ring) {
+  if (B < 0 || H_q <= 0 || H_kv <= 0 || T_cap <= 0) return ATTN_ERR_SHAPE;
+  if (H_q % H_kv != 0) return ATTN_ERR_SHAPE;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
+  if (window < 0) return ATTN_ERR_WINDOW;
+  if (ring && window > T_cap) return ATTN_ERR_WINDOW;
+  // 32-bit indices inside the kernels: positions and (row * H) products.
+  if ((long long)B * H_q > (1LL << 30)) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+int plan_gqa(int B, int H_q, int H_kv, int T_cap, int d, int dtype, int window,
+             int ring, int num_splits, GqaPlan* p) {
+  int st = check_gqa_shape(B, H_q, H_kv, T_cap, d, dtype, window, ring);
+  if (st != ATTN_OK) return st;
+  if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_ARG;
+  const int n = H_q / H_kv;
+  ValuGeometry geo;
+  if (!valu_geometry(dtype, d, n, &geo)) return ATTN_ERR_UNSUPPORTED;
+  p->N = geo.heads_per_item;
+  p->head_chunks = (n + geo.heads_per_item - 1) / geo.heads_per_item;
+  p->waves = geo.waves;
+  const int mv = max_visible(T_cap, window, ring);
+  long long S;
+  if (num_splits > 0) {
+    S = num_splits;
+  } else {
+    const long long units = (long long)(B > 0 ? B : 1) * H_kv * p->head_chunks;
+    const long long per_item = (long long)geo.waves;
+    S = (target_waves() + units * per_item - 1) / (units * per_item);
+    // keep at least two tiles per wave
+    long long smax = mv / ((long long)geo.waves * geo.tile_rows * 2);
+    if (smax < 1) smax = 1;
+    if (S > smax) S = smax;
+  }
+  if (S < 1) S = 1;
+  if (S > ATTN_MAX_SPLITS) S = ATTN_MAX_SPLITS;
+  if (S > mv) S = mv;
+  p->chunk = (int)((mv + S - 1) / S);
+  p->S = (mv + p->chunk - 1) / p->chunk;
+  p->ws_bytes = attn_decode_workspace_bytes(B, H_q, d, p->S);
+  return ATTN_OK;
+}
+
+}  // namespace
+}  // namespace attn
+
+using namespace attn;
+
+extern "C" {
+
+size_t attn_decode_workspace_bytes(int B, int H, int d_v, int num_splits) {
+  if (B <= 0 || H <= 0 || d_v <= 0 || num_splits <= 1) return 0;
+  const size_t rows = (size_t)B * H * num_splits;
+  return round_up(rows * d_v * sizeof(float), 256) +
+         round_up(rows * sizeof(float), 256);
+}
+
+int attn_decode_gqa_splits(int B, int H_q, int H_kv, int T_cap, int d,
+                           int dtype, int window, int ring, int num_splits) {
+  GqaPlan p;
+  const int st = plan_gqa(B, H_q, H_kv, T_cap, d, dtype, window, ring,
+                          num_splits, &p);
+  return st == ATTN_OK ? p.S : st;
+}
+
+size_t attn_decode_gqa_workspace_bytes(int B, int H_q, int H_kv, int T_cap,
+                                       int d, int dtype, int window, int ring,
+                                       int num_splits) {
+  GqaPlan p;
+  const int st = plan_gqa(B, H_q, H_kv, T_cap, d, dtype, window, ring,
+                          num_splits, &p);
+  return st == ATTN_OK ? p.ws_bytes : (size_t)-1;
+}
+
+int attn_decode_gqa(const void* q, const void* k, const void* v, float* out,
+                    float* lse_out, const int32_t* seq_lens,
+                    const int32_t* ring_head, int B, int H_q, int H_kv,
+                    int T_cap, int d, int dtype, int window, float scale,
+                    int num_splits, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  const int ring = ring_head != nullptr;
+  GqaPlan p;
+  int st = plan_gqa(B, H_q, H_kv, T_cap, d, dtype, window, ring, num_splits, &p);
+  if (st != ATTN_OK) return st;
+  if (B == 0) return ATTN_OK;  // empty batch: nothing to read or write
+  if (!q || !k || !v || !out) return ATTN_ERR_NULL;
+  if (isinf(scale)) return ATTN_ERR_ARG;
+  if (!(scale > 0.f)) scale = 1.0f / sqrtf((float)d);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 4) ||
+      (lse_out && !aligned(lse_out, 4)) || (seq_lens && !aligned(seq_lens, 4)) ||
+      (ring_head && !aligned(ring_head, 4)))
+    return ATTN_ERR_ALIGN;
+  if (p.S > 1) {
+    if (!workspace || workspace_bytes < p.ws_bytes) return ATTN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+  }
+
+  GqaArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse_out;
+  a.seq_lens = seq_lens;
+  a.ring_head = ring_head;
+  a.B = B;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.T_cap = T_cap;
+  a.window = window;
+  a.n = H_q / H_kv;
+  a.head_chunks = p.head_chunks;
+  a.S = p.S;
+  a.chunk = p.chunk;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.o_part = nullptr;
+  a.lse_part = nullptr;
+  if (p.S > 1) {
+    const size_t rows = (size_t)B * H_q * p.S;
+    a.o_part = (float*)workspace;
+    a.lse_part = (float*)((char*)workspace + round_up(rows * d * sizeof(float), 256));
+  }
+  const long long grid = (long long)B * H_kv * p.head_chunks * p.S;
+  if (grid > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  a.xcd_remap = (p.head_chunks > 1 && grid % kNumXCDs == 0) ? 1 : 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_gqa_valu(a, dtype, d, (int)grid, s) != hipSuccess) return ATTN_ERR_HIP;
+  if (p.S > 1) {
+    if (launch_combine(a.o_part, a.lse_part, out, lse_out, B, H_q, p.S, d, s) !=
+        hipSuccess)
+      return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+int attn_combine(const float* o_part, const float* lse_part, float* out,
+                 float* lse_out, int B, int H, int S, int d_v, void* stream) {
+  if (B < 0 || H <= 0 || d_v <= 0 || d_v > 4096) return ATTN_ERR_SHAPE;
+  if (S < 1 || S > ATTN_MAX_SPLITS) return ATTN_ERR_ARG;
+  if ((long long)B * H > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  if (B == 0) return ATTN_OK;
+  if (!o_part || !lse_part || !out) return ATTN_ERR_NULL;
+  if (!aligned(o_part, 4) || !aligned(lse_part, 4) || !aligned(out, 4) ||
+      (lse_out && !aligned(lse_out, 4)))
+    return ATTN_ERR_ALIGN;
+  if (launch_combine(o_part, lse_part, out, lse_out, B, H, S, d_v,
+                     (hipStream_t)stream) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape";
+    case ATTN_ERR_DTYPE: return "unknown dtype";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension or widths";
+    case ATTN_ERR_WINDOW: return "invalid window";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_ALIGN: return "misaligned pointer";
+    case ATTN_ERR_HIP: return "HIP launch error";
+    case ATTN_ERR_ARG: return "invalid scalar argument";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

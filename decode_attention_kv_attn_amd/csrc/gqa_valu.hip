@@ -1,0 +1,403 @@
+// Split-T decode attention on the vector ALUs (MHA / GQA, groups of <= 8).
+//
+// One work group owns (sequence b, KV head g, up to N query heads of g's
+// group, split s of the visible range).  Its waves take the split's tiles in
+// turn.  Each tile is TR consecutive visible positions; a wave reads the K
+// and V rows of a tile once with 16-byte loads and serves all N query heads
+// from them (the group's heads share one K/V head: xuesongtap
+// "attention-head" note, section 2.2).
+//
+// Lane layout inside a wave: LPR lanes cover one cache row, each owning E
+// elements (CPL 16-byte chunks; chunk c + k*LPR for k < CPL), so one load
+// instruction covers RPI = 64/LPR whole rows -- LPR*16 contiguous bytes per
+// row.  Dot products are finished with DPP sums inside the LPR-lane group.
+// Every row group (the LPR lanes of one row) keeps its own running softmax
+// state (max m in the log2 domain, sum l, value sums acc), so the main loop
+// needs no wave-wide communication; the states are merged by the
+// log-sum-exp rule at the end, first across row groups (DPP / swizzle), then
+// across waves through LDS.
+//
+// Online softmax with a lazy maximum: a state keeps its reference max until a
+// tile raises the max by more than 8 (log2 units), so weights stay <= 2^8 and
+// the rescale of acc is rare.  The result is the same softmax: every weight
+// and the normaliser use the same reference.
+//
+// Rows of a tile past the end of the split are not loaded from their own
+// address: they re-read the tile's first row (always visible) and get weight
+// 0, so no masked cache row is ever read (attention-head section 3).
+
+#include "device_common.h"
+#include "internal.h"
+#include "visible.h"
+
+namespace attn {
+namespace {
+
+template <typename T>
+struct ElemTraits;
+
+template <>
+struct ElemTraits<float> {
+  static constexpr int EPC = 4;  // elements per 16-byte chunk
+  static ATTN_DEV float dot(const uint4& q, const uint4& k, float acc) {
+    acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
+    acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+    acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+    acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+    return acc;
+  }
+  static ATTN_DEV void unpack(const uint4& c, float (&f)[4]) {
+    f[0] = __uint_as_float(c.x);
+    f[1] = __uint_as_float(c.y);
+    f[2] = __uint_as_float(c.z);
+    f[3] = __uint_as_float(c.w);
+  }
+};
+
+// bf16 stored as raw 16-bit patterns, two per dword (element 2j in the low
+// half of dword j).
+template <>
+struct ElemTraits<uint16_t> {
+  static constexpr int EPC = 8;
+  static ATTN_DEV float dot(const uint4& q, const uint4& k, float acc) {
+    acc = dot2_bf16(q.x, k.x, acc);
+    acc = dot2_bf16(q.y, k.y, acc);
+    acc = dot2_bf16(q.z, k.z, acc);
+    acc = dot2_bf16(q.w, k.w, acc);
+    return acc;
+  }
+  static ATTN_DEV void unpack(const uint4& c, float (&f)[8]) {
+    f[0] = bf16_lo(c.x);
+    f[1] = bf16_hi(c.x);
+    f[2] = bf16_lo(c.y);
+    f[3] = bf16_hi(c.y);
+    f[4] = bf16_lo(c.z);
+    f[5] = bf16_hi(c.z);
+    f[6] = bf16_lo(c.w);
+    f[7] = bf16_hi(c.w);
+  }
+};
+
+// Geometry of one instantiation.
+template <typename T, int D, int N>
+struct Cfg {
+  static constexpr int EPC = ElemTraits<T>::EPC;
+  static constexpr int E = (N <= 4) ? 16 : 8;  // elements per lane per row
+  static constexpr int CPL = E / EPC;          // chunks per lane per row
+  static constexpr int LPR = D / E;            // lanes per row
+  static constexpr int RPI = 64 / LPR;         // rows per load instruction
+  static constexpr int TR_BYTES = N <= 4 ? 16384 : 8192;  // K+V bytes per wave per tile
+  static constexpr int TR0 = TR_BYTES / (2 * D * (int)sizeof(T));
+  static constexpr int TR = TR0 > RPI ? TR0 : RPI;  // rows per tile
+  static constexpr int RPL = TR / RPI;              // rows per lane per tile
+  static constexpr int NW0 = 15360 / (N * D);       // LDS cap for the merge
+  static constexpr int NW = NW0 >= 8 ? 8 : (NW0 >= 4 ? 4 : 2);
+  static_assert(E % EPC == 0 && D % E == 0, "lane split");
+  static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "lanes per row");
+  static_assert(TR % RPI == 0, "tile rows");
+};
+
+// Fold the state held RPI_STEP row groups away into this lane's state.
+template <int CTRL, int N, int E>
+ATTN_DEV void merge_dpp(float (&m)[N], float (&l)[N], float (&acc)[N][E]) {
+#pragma unroll
+  for (int h = 0; h < N; ++h) {
+    float a1, a2;
+    lse_merge_scalars(m[h], l[h], dpp<CTRL>(m[h]), dpp<CTRL>(l[h]), a1, a2);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[h][e] = a1 * acc[h][e] + a2 * dpp<CTRL>(acc[h][e]);
+  }
+}
+
+template <int N, int E, typename F>
+ATTN_DEV void merge_fn(float (&m)[N], float (&l)[N], float (&acc)[N][E], F mv) {
+#pragma unroll
+  for (int h = 0; h < N; ++h) {
+    float a1, a2;
+    lse_merge_scalars(m[h], l[h], mv(m[h]), mv(l[h]), a1, a2);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[h][e] = a1 * acc[h][e] + a2 * mv(acc[h][e]);
+  }
+}
+
+template <typename T, int D, int N>
+__global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
+    GqaArgs a) {
+  using C = Cfg<T, D, N>;
+  using ET = ElemTraits<T>;
+  constexpr int EPC = C::EPC, E = C::E, CPL = C::CPL, LPR = C::LPR;
+  constexpr int RPI = C::RPI, TR = C::TR, RPL = C::RPL, NW = C::NW;
+
+  __shared__ float sm_acc[NW][N][D];
+  __shared__ float sm_m[NW][N];
+  __shared__ float sm_l[NW][N];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rg = lane / LPR;  // row group
+  const int cl = lane % LPR;  // lane inside the row
+
+  // ---- work item: hc fastest, then split, KV head, sequence ---------------
+  int bid = blockIdx.x;
+  if (a.xcd_remap) {
+    const int per = gridDim.x / kNumXCDs;
+    bid = (bid % kNumXCDs) * per + bid / kNumXCDs;
+  }
+  const int hc = bid % a.head_chunks;
+  bid /= a.head_chunks;
+  const int s = bid % a.S;
+  bid /= a.S;
+  const int g = bid % a.H_kv;
+  const int b = bid / a.H_kv;
+
+  const VisibleRange vr =
+      visible_range(a.seq_lens, a.ring_head, b, a.T_cap, a.window);
+  const bool ring = a.ring_head != nullptr;
+  int p0, p1;
+  split_range(vr, s, a.chunk, p0, p1);
+  const int h0 = g * a.n + hc * N;       // first query head served
+  const int nh = min(N, a.n - hc * N);   // heads actually present
+
+  const size_t kv_off = (size_t)(b * a.H_kv + g) * (size_t)a.T_cap * D;
+  const T* __restrict__ Kbg = (const T*)a.k + kv_off;
+  const T* __restrict__ Vbg = (const T*)a.v + kv_off;
+
+  // ---- query chunks for this lane's elements ------------------------------
+  uint4 qr[N][CPL];
+  {
+    const T* qb = (const T*)a.q + ((size_t)b * a.H_q + h0) * D;
+#pragma unroll
+    for (int h = 0; h < N; ++h)
+#pragma unroll
+      for (int k = 0; k < CPL; ++k)
+        qr[h][k] = (h < nh) ? *(const uint4*)(qb + h * D + (cl + k * LPR) * EPC)
+                            : make_uint4(0, 0, 0, 0);
+  }
+
+  float m[N], l[N], acc[N][E];
+#pragma unroll
+  for (int h = 0; h < N; ++h) {
+    m[h] = neg_inf();
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+  }
+
+  const int span = p1 - p0;
+  const int ntiles = span > 0 ? (span + TR - 1) / TR : 0;
+  for (int it = wave; it < ntiles; it += NW) {
+    const int base = p0 + it * TR;
+    uint4 kr[RPL][CPL], vv[RPL][CPL];
+    bool valid[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const int pos = base + rg + i * RPI;
+      valid[i] = pos < p1;
+      const int slot = slot_of(vr, ring, valid[i] ? pos : base, a.T_cap);
+      const T* kp = Kbg + (size_t)slot * D + cl * EPC;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) kr[i][k] = *(const uint4*)(kp + k * LPR * EPC);
+    }
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const int pos = base + rg + i * RPI;
+      const int slot = slot_of(vr, ring, valid[i] ? pos : base, a.T_cap);
+      const T* vp = Vbg + (size_t)slot * D + cl * EPC;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) vv[i][k] = *(const uint4*)(vp + k * LPR * EPC);
+    }
+
+    // scores (log2 domain)
+    float sc[RPL][N];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+#pragma unroll
+      for (int h = 0; h < N; ++h) {
+        float x = 0.f;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) x = ET::dot(qr[h][k], kr[i][k], x);
+        sc[i][h] = x;
+      }
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+#pragma unroll
+      for (int h = 0; h < N; ++h) {
+        const float x = group_sum<LPR>(sc[i][h]) * a.scale_log2;
+        sc[i][h] = valid[i] ? x : neg_inf();
+      }
+
+    // lazy maximum
+#pragma unroll
+    for (int h = 0; h < N; ++h) {
+      float mt = sc[0][h];
+#pragma unroll
+      for (int i = 1; i < RPL; ++i) mt = fmaxf(mt, sc[i][h]);
+      if (mt > m[h] + 8.f) {
+        const float al = fast_exp2(m[h] - mt);
+        l[h] *= al;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] *= al;
+        m[h] = mt;
+      }
+    }
+
+    // weights and value sums
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      float vf[CPL][EPC];
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) ET::unpack(vv[i][k], vf[k]);
+#pragma unroll
+      for (int h = 0; h < N; ++h) {
+        const float p = valid[i] ? fast_exp2(sc[i][h] - m[h]) : 0.f;
+        l[h] += p;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e)
+            acc[h][k * EPC + e] = fmaf(p, vf[k][e], acc[h][k * EPC + e]);
+      }
+    }
+  }
+
+  // ---- merge the row groups of this wave ----------------------------------
+  // Partners are RPI_k = LPR * 2^k lanes away; rotations inside a 16-lane row
+  // reach every row group of the row, swizzles cross rows.
+  if constexpr (LPR <= 1) merge_dpp<0x121, N, E>(m, l, acc);
+  if constexpr (LPR <= 2) merge_dpp<0x122, N, E>(m, l, acc);
+  if constexpr (LPR <= 4) merge_dpp<kDppRowRor4, N, E>(m, l, acc);
+  if constexpr (LPR <= 8) merge_dpp<kDppRowRor8, N, E>(m, l, acc);
+  if constexpr (LPR <= 16) merge_fn<N, E>(m, l, acc, [](float x) { return xor16(x); });
+  if constexpr (LPR <= 32) merge_fn<N, E>(m, l, acc, [](float x) { return xor32(x); });
+
+  if (rg == 0) {
+#pragma unroll
+    for (int h = 0; h < N; ++h)
+#pragma unroll
+      for (int k = 0; k < CPL; ++k)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+          sm_acc[wave][h][(cl + k * LPR) * EPC + e] = acc[h][k * EPC + e];
+    if (cl == 0) {
+#pragma unroll
+      for (int h = 0; h < N; ++h) {
+        sm_m[wave][h] = m[h];
+        sm_l[wave][h] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- merge the waves and write ------------------------------------------
+  for (int idx = threadIdx.x; idx < nh * D; idx += NW * 64) {
+    const int h = idx / D;
+    const int e = idx - h * D;
+    float M = neg_inf();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+    float L = 0.f, O = 0.f;
+    if (M != neg_inf()) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = sm_m[w][h];
+        const float wt = (mw == neg_inf()) ? 0.f : fast_exp2(mw - M);
+        L = fmaf(wt, sm_l[w][h], L);
+        O = fmaf(wt, sm_acc[w][h][e], O);
+      }
+    }
+    const bool empty = !(L > 0.f);
+    const float o = empty ? 0.f : O / L;
+    const float lse = empty ? neg_inf() : (M + fast_log2(L)) * kLn2;
+    const size_t row = (size_t)b * a.H_q + h0 + h;
+    if (a.S == 1) {
+      a.out[row * D + e] = o;
+      if (e == 0 && a.lse) a.lse[row] = lse;
+    } else {
+      a.o_part[(row * a.S + s) * D + e] = o;
+      if (e == 0) a.lse_part[row * a.S + s] = lse;
+    }
+  }
+}
+
+template <typename T, int D, int N>
+hipError_t launch_one(const GqaArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((gqa_decode_valu<T, D, N>), dim3(grid),
+                     dim3(Cfg<T, D, N>::NW * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int N>
+void geometry_one(ValuGeometry* g) {
+  g->heads_per_item = N;
+  g->tile_rows = Cfg<T, D, N>::TR;
+  g->waves = Cfg<T, D, N>::NW;
+}
+
+template <typename T, int D>
+hipError_t launch_d(const GqaArgs& a, int N, int grid, hipStream_t st) {
+  switch (N) {
+    case 1: return launch_one<T, D, 1>(a, grid, st);
+    case 2: return launch_one<T, D, 2>(a, grid, st);
+    case 3: return launch_one<T, D, 3>(a, grid, st);
+    case 4: return launch_one<T, D, 4>(a, grid, st);
+    case 5: return launch_one<T, D, 5>(a, grid, st);
+    case 6: return launch_one<T, D, 6>(a, grid, st);
+    case 7: return launch_one<T, D, 7>(a, grid, st);
+    case 8: return launch_one<T, D, 8>(a, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int D>
+void geometry_d(int N, ValuGeometry* g) {
+  switch (N) {
+    case 1: geometry_one<T, D, 1>(g); break;
+    case 2: geometry_one<T, D, 2>(g); break;
+    case 3: geometry_one<T, D, 3>(g); break;
+    case 4: geometry_one<T, D, 4>(g); break;
+    case 5: geometry_one<T, D, 5>(g); break;
+    case 6: geometry_one<T, D, 6>(g); break;
+    case 7: geometry_one<T, D, 7>(g); break;
+    default: geometry_one<T, D, 8>(g); break;
+  }
+}
+
+}  // namespace
+
+// Heads per work item: the whole group when it has <= 8 heads, else chunks
+// of 8 (each chunk re-reads the group's K/V rows).
+bool valu_geometry(int dtype, int d, int n, ValuGeometry* g) {
+  const int N = n <= 8 ? n : 8;
+  if (N < 1) return false;
+  if (dtype == 0) {
+    if (d == 64) geometry_d<float, 64>(N, g);
+    else if (d == 128) geometry_d<float, 128>(N, g);
+    else if (d == 256) geometry_d<float, 256>(N, g);
+    else return false;
+  } else if (dtype == 1) {
+    if (d == 64) geometry_d<uint16_t, 64>(N, g);
+    else if (d == 128) geometry_d<uint16_t, 128>(N, g);
+    else if (d == 256) geometry_d<uint16_t, 256>(N, g);
+    else return false;
+  } else {
+    return false;
+  }
+  return true;
+}
+
+hipError_t launch_gqa_valu(const GqaArgs& a, int dtype, int d, int grid,
+                           hipStream_t st) {
+  const int N = a.n <= 8 ? a.n : 8;
+  if (dtype == 0) {
+    if (d == 64) return launch_d<float, 64>(a, N, grid, st);
+    if (d == 128) return launch_d<float, 128>(a, N, grid, st);
+    if (d == 256) return launch_d<float, 256>(a, N, grid, st);
+  } else if (dtype == 1) {
+    if (d == 64) return launch_d<uint16_t, 64>(a, N, grid, st);
+    if (d == 128) return launch_d<uint16_t, 128>(a, N, grid, st);
+    if (d == 256) return launch_d<uint16_t, 256>(a, N, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attn

@@ -1,0 +1,49 @@
+// Launch-side interface between the host API and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+constexpr int kNumCUs = 256;  // MI355X: 8 XCDs x 32 CUs
+constexpr int kNumXCDs = 8;
+
+// Arguments of one MHA/GQA/MQA decode launch.
+struct GqaArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* out;        // final output when S == 1
+  float* lse;        // final lse when S == 1 (nullable)
+  float* o_part;     // [B, H_q, S, d] when S > 1
+  float* lse_part;   // [B, H_q, S]    when S > 1
+  const int32_t* seq_lens;   // nullable
+  const int32_t* ring_head;  // nullable: linear addressing
+  int B, H_q, H_kv, T_cap, window;
+  int n;            // query heads per KV head
+  int head_chunks;  // work items per KV head along the query heads
+  int S;            // splits of the visible range
+  int chunk;        // positions per split
+  int xcd_remap;    // 1: map consecutive work items onto one XCD
+  float scale_log2; // softmax scale * log2(e)
+};
+
+// Per-instantiation geometry of the VALU kernel, reported to the planner.
+struct ValuGeometry {
+  int heads_per_item;  // N: query heads one work item serves
+  int tile_rows;       // positions per wave per tile
+  int waves;           // waves per work group
+};
+
+// dtype: 0 = float32, 1 = bf16.  Returns false if no instantiation exists.
+bool valu_geometry(int dtype, int d, int n, ValuGeometry* g);
+hipError_t launch_gqa_valu(const GqaArgs& a, int dtype, int d, int grid,
+                           hipStream_t stream);
+
+hipError_t launch_combine(const float* o_part, const float* lse_part,
+                          float* out, float* lse, int B, int H, int S, int d_v,
+                          hipStream_t stream);
+
+}  // namespace attn

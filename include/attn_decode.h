@@ -1,0 +1,194 @@
+/*
+ * attn_decode.h -- C ABI of the MI355X (gfx950) decode-attention library.
+ *
+ * One call computes one decode step of attention for one layer: a single new
+ * query token per sequence attends to that sequence's KV cache,
+ *
+ *     out[b,h] = softmax(scale * q[b,h] . K[b,g(h)]^T + M) . V[b,g(h)]
+ *
+ * (attention equation, xuesongtap.github.io "attention-head" note, section 1).
+ * The layout of the cache follows from head sharing: [B, H_kv, T, d] with
+ * H_kv == H_q (MHA), 1 < H_kv < H_q (GQA) or H_kv == 1 (MQA); query head h
+ * reads KV head g(h) = floor(h / (H_q / H_kv)) -- equal, contiguously
+ * numbered groups (attention-head sections 2, 2.1, 2.2; the toolsku article's
+ * GQA module expands KV heads the same way).  MLA reads a latent cache
+ * [B, T, d_c + d_rope] with the key up-projection absorbed into the query and
+ * the value up-projection left to the caller (attention-head sections
+ * 5.2-5.3).
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named q, k, v, latent, out, lse_out, seq_lens, ring_head,
+ *    o_part, lse_part and workspace are DEVICE pointers owned by the caller.
+ *    The library never allocates, frees or synchronises; every call only
+ *    enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ *    returns.  The caller keeps inputs alive and unmodified until the stream
+ *    reaches the work.  Calls are thread-safe; there is no global state.
+ *  - Tensors are dense, row-major, in exactly the shapes given.  q, k, v,
+ *    latent and workspace must be 16-byte aligned; out, lse_out and the
+ *    partial buffers 4-byte aligned.
+ *  - Sequence b's cache holds T_b = seq_lens[b] tokens including the current
+ *    one; the query is position t = T_b - 1 and full causal attention sees
+ *    positions 0..t (attention-head section 5.3, single-token causal decode
+ *    over the valid cached tokens).  seq_lens == NULL means T_b = T_cap.
+ *  - Masked positions drop out of the softmax (M = -inf), visible ones add 0.
+ *    Masked cache rows are never read: the kernels load only the visible
+ *    range (attention-head section 3: a window pays off only when the kernel
+ *    skips masked positions).
+ *  - Results are float32.  lse_out (nullable) receives the natural-log
+ *    log-sum-exp of the scaled visible scores.  A query with no visible key
+ *    gets out = 0 and lse = -inf.
+ *  - All argument checks use host values only and happen before any HIP
+ *    call; a failing check returns its code and enqueues nothing.  Values
+ *    inside device arrays are not checked on the host; see each function for
+ *    how out-of-range values are treated.
+ */
+#ifndef ATTN_DECODE_H
+#define ATTN_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q / k / v.  Accumulation is always float32. */
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Status codes returned by every int-returning entry point. */
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,        /* a required pointer is NULL                     */
+  ATTN_ERR_SHAPE = -2,       /* H <= 0, T_cap <= 0, B < 0, H_q % H_kv != 0     */
+  ATTN_ERR_DTYPE = -3,       /* dtype not an attn_dtype value                  */
+  ATTN_ERR_UNSUPPORTED = -4, /* head dim / latent widths / dtype combo absent  */
+  ATTN_ERR_WINDOW = -5,      /* window < 0, or ring mode with window > T_cap   */
+  ATTN_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required        */
+  ATTN_ERR_ALIGN = -7,       /* a pointer misses its alignment                 */
+  ATTN_ERR_HIP = -8,         /* the HIP runtime reported an error on launch    */
+  ATTN_ERR_ARG = -9          /* bad scalar: scale not finite, num_splits range */
+};
+
+/* Largest accepted num_splits. */
+#define ATTN_MAX_SPLITS 1024
+
+/*
+ * attn_decode_gqa -- one decode step of MHA / GQA / MQA attention.
+ *
+ *   q         [B, H_q, d]           dtype
+ *   k, v      [B, H_kv, T_cap, d]   dtype   (row (b, g, slot) is d contiguous
+ *                                            elements: attention-head section 2
+ *                                            layout [batch, head, seq, dim])
+ *   out       [B, H_q, d]           float32
+ *   lse_out   [B, H_q]              float32, may be NULL
+ *   seq_lens  [B] int32 logical lengths T_b, may be NULL (all T_cap).
+ *             Linear mode: values are clamped to [0, T_cap].
+ *             Ring mode: any value >= 0 (the ring keeps the newest T_cap);
+ *             negative values are treated as 0.
+ *   ring_head [B] int32, may be NULL.  Non-NULL selects ring-buffer
+ *             addressing (attention-head section 3: a pure sliding-window
+ *             layer may reuse out-of-window slots as a ring): the cache has
+ *             T_cap slots, ring_head[b] is the slot holding the newest
+ *             position t, and position j sits in slot
+ *             (ring_head[b] - (t - j)) mod T_cap.  Only the last T_cap
+ *             positions are resident.  Values are reduced mod T_cap.
+ *   B, H_q, H_kv, T_cap, d   shapes; d in {64, 128, 256}; H_q % H_kv == 0;
+ *             B == 0 is a no-op (pointers may then be NULL).
+ *   dtype     ATTN_F32 or ATTN_BF16 (all of q, k, v).
+ *   window    0: no window (in ring mode: every resident position).
+ *             w > 0: the query at t sees t-w+1 .. t (attention-head section
+ *             3, worked example w = 3: row 8 sees 6, 7, 8).  Ring mode
+ *             requires w <= T_cap.
+ *   scale     softmax scale; <= 0 or NaN selects 1/sqrt(d) (section 1).
+ *   num_splits  number of pieces the visible range of a sequence is cut into
+ *             (their results are merged by attn_combine's rule);
+ *             0 = chosen by the library (attn_decode_gqa_splits tells which).
+ *   workspace, workspace_bytes  scratch for split results; required when the
+ *             split count is > 1, size from attn_decode_gqa_workspace_bytes.
+ *             Contents on entry are ignored.
+ *   stream    hipStream_t.
+ */
+int attn_decode_gqa(const void* q, const void* k, const void* v, float* out,
+                    float* lse_out, const int32_t* seq_lens,
+                    const int32_t* ring_head, int B, int H_q, int H_kv,
+                    int T_cap, int d, int dtype, int window, float scale,
+                    int num_splits, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Split count attn_decode_gqa would use for these arguments (>= 1), or a
+ * negative status if the shape arguments are invalid. */
+int attn_decode_gqa_splits(int B, int H_q, int H_kv, int T_cap, int d,
+                           int dtype, int window, int ring, int num_splits);
+
+/* Workspace bytes attn_decode_gqa needs for these arguments (0 when no
+ * workspace is needed, (size_t)-1 when the arguments are invalid). */
+size_t attn_decode_gqa_workspace_bytes(int B, int H_q, int H_kv, int T_cap,
+                                       int d, int dtype, int window, int ring,
+                                       int num_splits);
+
+/*
+ * attn_decode_mla -- one decode step of absorbed multi-head latent attention.
+ *
+ *   q       [B, H, d_c + d_rope]  bf16: each row is [q~ | q^R], the content
+ *           query already multiplied by the head's key up-projection
+ *           transposed (attention-head section 5.2), followed by the RoPE
+ *           query (section 5.3).
+ *   latent  [B, T_cap, d_c + d_rope]  bf16: each row is [c_j | k^R_j], the
+ *           normalised latent followed by the shared RoPE key (the one-tensor
+ *           cache [batch, seq, compressed_kv_dim + rope_dim] of the baidu
+ *           article, section 二).
+ *   out     [B, H, d_c] float32: z = sum_j p_j c_j, the latent-space result
+ *           before the value up-projection (attention-head section 5.2).
+ *   lse_out [B, H] float32, may be NULL.
+ *   seq_lens [B] int32, may be NULL (all T_cap); clamped to [0, T_cap].
+ *   Scores are scale * (q~ . c_j + q^R . k^R_j): one dot product over the
+ *   whole row, one softmax over the sum (section 5.3).
+ *   (d_c, d_rope) = (512, 64) is supported.
+ *   scale   must be > 0 and finite: 1/sqrt(d_head_content + d_rope) with the
+ *           model's per-head content width (section 5.3 keeps that
+ *           denominator; the latent width r does not enter it).
+ *   The value columns are used in float16 inside the matrix-core product:
+ *   |c| must stay below 65504; magnitudes under 2^-17 lose relative
+ *   precision (absolute error below 2^-25).
+ *   num_splits / workspace / stream as for attn_decode_gqa, with
+ *   attn_decode_mla_workspace_bytes giving the size.
+ */
+int attn_decode_mla(const void* q, const void* latent, float* out,
+                    float* lse_out, const int32_t* seq_lens, int B, int H,
+                    int T_cap, int d_c, int d_rope, float scale,
+                    int num_splits, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+int attn_decode_mla_splits(int B, int H, int T_cap, int d_c, int d_rope,
+                           int num_splits);
+
+size_t attn_decode_mla_workspace_bytes(int B, int H, int T_cap, int d_c,
+                                       int d_rope, int num_splits);
+
+/*
+ * attn_combine -- merge results computed over S disjoint parts of each key
+ * set.  With L = max_s lse_part[s] and w_s = exp(lse_part[s] - L):
+ *     out = sum_s w_s o_part[s] / sum_s w_s,   lse = L + ln(sum_s w_s).
+ * This is the softmax of the attention equation (attention-head section 1)
+ * taken over a union of disjoint key sets.  Parts with lse = -inf are empty;
+ * if all are, out = 0 and lse = -inf.
+ *
+ *   o_part   [B, H, S, d_v] float32     lse_part [B, H, S] float32
+ *   out      [B, H, d_v]    float32     lse_out  [B, H] float32, may be NULL
+ *   S in 1..ATTN_MAX_SPLITS, d_v in 1..4096; B == 0 is a no-op.
+ */
+int attn_combine(const float* o_part, const float* lse_part, float* out,
+                 float* lse_out, int B, int H, int S, int d_v, void* stream);
+
+/* Bytes of the split buffers for S splits: o_part [B,H,S,d_v] and lse_part
+ * [B,H,S], float32, each 256-byte aligned inside the workspace (0 if S<=1). */
+size_t attn_decode_workspace_bytes(int B, int H, int d_v, int num_splits);
+
+/* Static, human-readable text for a status code. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_DECODE_H */

@@ -1,0 +1,124 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_kv_attn_amd as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_decode.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.library_path):
+        from decode_attention_kv_attn_amd import build
+        build.build()
+    return L.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(attn_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("attn_decode_gqa", "attn_decode_mla", "attn_combine",
+                 "attn_decode_workspace_bytes", "attn_status_string"):
+        assert want in names, names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in L._SIGS, f"binding lacks {name}"
+
+
+P16 = ctypes.c_void_p(4096)      # aligned, never dereferenced: calls fail first
+
+
+def gqa(lib, q=P16, k=P16, v=P16, out=P16, lse=None, sl=None, rh=None, B=1,
+        H_q=8, H_kv=2, T=512, d=64, dt=1, window=0, scale=0.0, S=0, ws=None,
+        wsb=0):
+    return lib.attn_decode_gqa(q, k, v, out, lse, sl, rh, B, H_q, H_kv, T, d,
+                               dt, window, scale, S, ws, wsb, None)
+
+
+def test_gqa_host_errors(lib):
+    assert gqa(lib, q=None) == -1
+    assert gqa(lib, out=None) == -1
+    assert gqa(lib, H_kv=3) == -2            # 8 % 3 != 0
+    assert gqa(lib, H_q=0) == -2
+    assert gqa(lib, T=0) == -2
+    assert gqa(lib, B=-1) == -2
+    assert gqa(lib, dt=7) == -3
+    assert gqa(lib, d=96) == -4
+    assert gqa(lib, window=-1) == -5
+    assert gqa(lib, rh=P16, window=513) == -5  # ring: window > slots
+    assert gqa(lib, q=ctypes.c_void_p(4098)) == -7
+    assert gqa(lib, out=ctypes.c_void_p(4098)) == -7
+    assert gqa(lib, scale=float("inf")) == -9
+    assert gqa(lib, S=-1) == -9
+    assert gqa(lib, S=2000) == -9
+    # two splits need a workspace of the reported size
+    need = lib.attn_decode_gqa_workspace_bytes(1, 8, 2, 512, 64, 1, 0, 0, 4)
+    assert need > 0
+    assert gqa(lib, S=4) == -6
+    assert gqa(lib, S=4, ws=P16, wsb=need - 1) == -6
+    assert gqa(lib, S=4, ws=ctypes.c_void_p(4100), wsb=need) == -7
+    # B == 0 is a no-op that succeeds without launching, NULL pointers allowed
+    assert gqa(lib, B=0) == 0
+    assert gqa(lib, B=0, q=None, k=None, v=None, out=None) == 0
+
+
+def test_combine_and_mla_host_errors(lib):
+    assert lib.attn_combine(None, P16, P16, None, 1, 1, 2, 8, None) == -1
+    assert lib.attn_combine(P16, P16, P16, None, 1, 1, 0, 8, None) == -9
+    assert lib.attn_combine(P16, P16, P16, None, 1, 0, 2, 8, None) == -2
+    assert lib.attn_combine(P16, P16, P16, None, 0, 1, 2, 8, None) == 0
+    assert lib.attn_combine(None, None, None, None, 0, 1, 2, 8, None) == 0
+    assert lib.attn_decode_mla(None, P16, P16, None, None, 1, 128, 64, 512, 64,
+                               0.07, 0, None, 0, None) == -1
+    assert lib.attn_decode_mla(P16, P16, P16, None, None, 1, 128, 64, 512, 64,
+                               0.0, 0, None, 0, None) == -9
+    assert lib.attn_decode_mla(P16, P16, P16, None, None, 1, 128, 64, 500, 64,
+                               0.07, 0, None, 0, None) == -4
+
+
+def test_status_strings(lib):
+    for st in range(-9, 1):
+        assert L.attn_status_string(st) != "unknown status"
+
+
+def test_planner(lib):
+    # splits never leave a structurally empty piece and fit the visible range
+    for args in [(32, 32, 8, 4096, 128, 1, 0, 0), (1, 32, 32, 32768, 128, 1, 0, 0),
+                 (4, 24, 4, 131072, 256, 1, 0, 0), (16, 32, 8, 4096, 128, 1, 4096, 1),
+                 (1, 8, 2, 512, 64, 0, 0, 0), (64, 32, 1, 32768, 128, 1, 0, 0)]:
+        S = lib.attn_decode_gqa_splits(*args, 0)
+        assert 1 <= S <= 1024
+        T, window = args[3], args[6]
+        mv = window if window else T
+        chunk = -(-mv // S)
+        assert (S - 1) * chunk < mv
+        ws = lib.attn_decode_gqa_workspace_bytes(*args, 0)
+        assert ws == (0 if S == 1 else lib.attn_decode_workspace_bytes(args[0], args[1], args[4], S))
+    for S in (1, 2, 7, 64, 1024):
+        got = lib.attn_decode_gqa_splits(4, 16, 4, 2000, 128, 1, 0, 0, S)
+        assert 1 <= got <= S
+    assert lib.attn_decode_workspace_bytes(2, 3, 64, 1) == 0
+    assert lib.attn_decode_workspace_bytes(2, 3, 64, 5) % 256 == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "_LIB", None)
+    monkeypatch.setattr(L, "library_path", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        L.library()
