@@ -41,6 +41,8 @@ _SIGS = {
     "attn_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "attn_decode_workspace_bytes": (_sz, [_i] * 4),
     "attn_status_string": (ctypes.c_char_p, [_i]),
+    "attn_probe_read": (_i, [_vp, _sz, _vp, _i, _vp]),
+    "attn_probe_copy": (_i, [_vp, _vp, _sz, _vp]),
 }
 
 
@@ -211,6 +213,21 @@ def attn_combine(o_part, lse_part, out=None, lse=None, want_lse=True,
                                 _stream(stream, o_part.device))
     _check("attn_combine", st)
     return out, lse
+
+
+def attn_probe_read(src, sink, blocks=0, stream=None):
+    """Stream-read every byte of ``src`` once (HBM read-rate probe)."""
+    st = library().attn_probe_read(_ptr(src), src.numel() * src.element_size(),
+                                   _ptr(sink), blocks, _stream(stream, src.device))
+    _check("attn_probe_read", st)
+
+
+def attn_probe_copy(dst, src, stream=None):
+    """dst <- src byte for byte (a copy of known size)."""
+    st = library().attn_probe_copy(_ptr(dst), _ptr(src),
+                                   src.numel() * src.element_size(),
+                                   _stream(stream, src.device))
+    _check("attn_probe_copy", st)
 
 
 def default_scale(d):

@@ -16,19 +16,20 @@ inline bool aligned(const void* p, size_t a) {
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Waves the planner aims to keep resident over the grid before it cuts the
-// visible range into more splits (8 per CU: two per SIMD).  Overridable for
-// tuning sweeps through ATTN_DECODE_TARGET_WAVES.
-int target_waves() {
+// Work groups the planner aims for before it cuts the visible range into
+// more splits: one per CU, each a full CU's worth of waves.  Overridable for
+// tuning sweeps through ATTN_DECODE_TARGET_GROUPS.
+int target_groups() {
   static const int v = [] {
-    const char* e = getenv("ATTN_DECODE_TARGET_WAVES");
+    const char* e = getenv("ATTN_DECODE_TARGET_GROUPS");
     const int x = e ? atoi(e) : 0;
-    return x > 0 ? x : kNumCUs * 8;
+    return x > 0 ? x : kNumCUs;
   }();
   return v;
 }
 
 struct GqaPlan {
+  int mfma;         // 1: matrix-core kernel, 0: vector kernel
   int N;            // heads per work item
   int head_chunks;  // work items per KV head along the heads
   int S;            // splits
@@ -63,7 +64,15 @@ int plan_gqa(int B, int H_q, int H_kv, int T_cap, int d, int dtype, int window,
   if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_ARG;
   const int n = H_q / H_kv;
   ValuGeometry geo;
-  if (!valu_geometry(dtype, d, n, &geo)) return ATTN_ERR_UNSUPPORTED;
+  const int nh_mfma = mfma_heads_per_item(dtype, d, n);
+  if (nh_mfma > 0) {
+    geo.heads_per_item = nh_mfma;
+    geo.tile_rows = mfma_tile_rows();
+    geo.waves = mfma_waves();
+  } else if (!valu_geometry(dtype, d, n, &geo)) {
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  p->mfma = nh_mfma > 0;
   p->N = geo.heads_per_item;
   p->head_chunks = (n + geo.heads_per_item - 1) / geo.heads_per_item;
   p->waves = geo.waves;
@@ -73,8 +82,7 @@ int plan_gqa(int B, int H_q, int H_kv, int T_cap, int d, int dtype, int window,
     S = num_splits;
   } else {
     const long long units = (long long)(B > 0 ? B : 1) * H_kv * p->head_chunks;
-    const long long per_item = (long long)geo.waves;
-    S = (target_waves() + units * per_item - 1) / (units * per_item);
+    S = (target_groups() + units - 1) / units;
     // keep at least two tiles per wave
     long long smax = mv / ((long long)geo.waves * geo.tile_rows * 2);
     if (smax < 1) smax = 1;
@@ -172,7 +180,9 @@ int attn_decode_gqa(const void* q, const void* k, const void* v, float* out,
   if (grid > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   a.xcd_remap = (p.head_chunks > 1 && grid % kNumXCDs == 0) ? 1 : 0;
   hipStream_t s = (hipStream_t)stream;
-  if (launch_gqa_valu(a, dtype, d, (int)grid, s) != hipSuccess) return ATTN_ERR_HIP;
+  const hipError_t e = p.mfma ? launch_gqa_mfma(a, d, p.N, (int)grid, s)
+                              : launch_gqa_valu(a, dtype, d, (int)grid, s);
+  if (e != hipSuccess) return ATTN_ERR_HIP;
   if (p.S > 1) {
     if (launch_combine(a.o_part, a.lse_part, out, lse_out, B, H_q, p.S, d, s) !=
         hipSuccess)

@@ -48,15 +48,20 @@ ATTN_DEV float dpp(float x) {
       __builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
-// Value of lane (i ^ 16).  ds_swizzle bit mode: and 0x1f, xor 0x10.
+// Value of lane (i ^ 16).  v_permlane16_swap(x, x) returns, per 16-lane row
+// r, the pair (x of row r&~1, x of row r|1) (checked on gfx950): the partner
+// row is the second element on even rows and the first on odd rows.
 ATTN_DEV float xor16(float x) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+  const unsigned u = __float_as_uint(x);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float((__lane_id() & 16) ? p[0] : p[1]);
 }
-// Value of lane (i ^ 32).
+// Value of lane (i ^ 32): v_permlane32_swap(x, x) returns (x of the low half,
+// x of the high half) in both halves.
 ATTN_DEV float xor32(float x) {
-  const int lane = __lane_id();
-  return __int_as_float(
-      __builtin_amdgcn_ds_bpermute(((lane ^ 32) << 2), __float_as_int(x)));
+  const unsigned u = __float_as_uint(x);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float((__lane_id() & 32) ? p[0] : p[1]);
 }
 
 // Sum over aligned groups of L consecutive lanes; every lane of the group

@@ -1,0 +1,370 @@
+// Decode attention on the matrix cores for large head groups (MQA-like).
+//
+// When many query heads share one KV head (H_q/H_kv >= 9; MQA at 32 heads is
+// the extreme: xuesongtap "attention-head" note, section 2.1), every K and V
+// row serves all of them, and the scores of a tile are a dense product
+// [tokens x d] . [d x heads].  The vector ALUs cannot keep up with HBM there
+// (32 flop/byte at 32 heads), so both products run on MFMA 16x16x32 (bf16 in,
+// fp32 accumulate):
+//
+//   S^T[tokens, heads] = K_tile[tokens, d] . Q^T[d, heads]
+//       A = K rows straight from HBM (each lane's 8 elements are 16
+//       contiguous bytes of one row), B = Q^T fragments kept in registers.
+//   O^T[d, heads] += V_tile^T[d, tokens] . P^T[tokens, heads]
+//       A = V^T fragments read from an LDS copy of the V tile with
+//       ds_read_b64_tr_b16 (a 4x16 transpose per 16-lane group), B = the
+//       softmax weights, which the S^T result already holds in the right
+//       lanes (token order inside the 32-token k-block is permuted the same
+//       way on both operands).
+//
+// The weights keep ~16 significant bits: P = P_hi + P_lo with both parts in
+// bf16, so the second product costs two MFMAs per block; P in bf16 alone
+// would carry a relative error of about 2^-9 per weight.
+//
+// Work item = (sequence, KV head, head chunk of NH query heads, split);
+// four waves take the split's 32-token tiles in turn and are merged by the
+// log-sum-exp rule through LDS.  Softmax state is per head and lives in the
+// lanes that own that head (lane % 16), so rescaling O^T is lane-local.
+
+#include "device_common.h"
+#include "internal.h"
+#include "visible.h"
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kTT = 32;  // tokens per tile
+constexpr int kNW = 4;   // waves per work group
+
+ATTN_DEV uint4 nt_load16(const void* p) {
+  const u32x4_t x = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
+ATTN_DEV bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// Round-to-nearest-even float -> bf16 bits (finite inputs).
+ATTN_DEV uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Chunk swizzle of the V tile in LDS: 16-byte chunk c of row t is stored at
+// chunk c ^ swz(t), so the four rows a transposed read touches fall on
+// distinct banks.
+template <int D>
+ATTN_DEV int vt_swz(int t) {
+  if constexpr (D == 64) return 2 * ((t >> 1) & 1);
+  else return 2 * (t & 3);
+}
+
+template <int D, int NH>
+struct MfmaCfg {
+  static constexpr int KS = D / 32;   // k-steps of the score product
+  static constexpr int HB = NH / 16;  // head blocks
+  static constexpr int DB = D / 16;   // d blocks of the value product
+  static constexpr int VT_BYTES = kTT * D * 2;
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;         // rows per load instruction
+  static constexpr int VLD = kTT / RPI;        // V loads per lane per tile
+  static constexpr int MERGE_BYTES = kNW * NH * (D + 2) * 4;
+  static constexpr int LOOP_BYTES = kNW * VT_BYTES;
+  static constexpr int SMEM = MERGE_BYTES > LOOP_BYTES ? MERGE_BYTES : LOOP_BYTES;
+};
+
+template <int D, int NH>
+__global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
+  using C = MfmaCfg<D, NH>;
+  constexpr int KS = C::KS, HB = C::HB, DB = C::DB, CPR = C::CPR;
+  constexpr int RPI = C::RPI, VLD = C::VLD;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int li = lane & 15;   // column inside a 16-wide block
+  const int lg = lane >> 4;   // 16-lane group
+
+  int bid = blockIdx.x;
+  if (a.xcd_remap) {
+    const int per = gridDim.x / kNumXCDs;
+    bid = (bid % kNumXCDs) * per + bid / kNumXCDs;
+  }
+  const int hc = bid % a.head_chunks;
+  bid /= a.head_chunks;
+  const int s = bid % a.S;
+  bid /= a.S;
+  const int g = bid % a.H_kv;
+  const int b = bid / a.H_kv;
+
+  const VisibleRange vr =
+      visible_range(a.seq_lens, a.ring_head, b, a.T_cap, a.window);
+  const bool ring = a.ring_head != nullptr;
+  int p0, p1;
+  split_range(vr, s, a.chunk, p0, p1);
+  const int h0 = g * a.n + hc * NH;
+  const int nh = min(NH, a.n - hc * NH);
+
+  const size_t kv_off = (size_t)(b * a.H_kv + g) * (size_t)a.T_cap * D;
+  const uint16_t* __restrict__ Kbg = (const uint16_t*)a.k + kv_off;
+  const uint16_t* __restrict__ Vbg = (const uint16_t*)a.v + kv_off;
+
+  // Q^T fragments: head li of block hb, elements 32*ks + 8*lg .. +7.
+  uint4 qf[HB][KS];
+  {
+    const uint16_t* qb = (const uint16_t*)a.q + ((size_t)b * a.H_q + h0) * D;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int h = hb * 16 + li;
+        qf[hb][ks] = h < nh ? *(const uint4*)(qb + (size_t)h * D + 32 * ks + 8 * lg)
+                            : make_uint4(0, 0, 0, 0);
+      }
+  }
+
+  f32x4_t o[DB][HB];  // O^T blocks: d rows 16*db + 4*lg + r, head column li
+  float m[HB], l[HB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    m[hb] = neg_inf();
+    l[hb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  unsigned char* vt = smem + wave * C::VT_BYTES;
+  const int span = p1 - p0;
+  const int ntiles = span > 0 ? (span + kTT - 1) / kTT : 0;
+
+  auto row_slot = [&](int base, int t) {
+    const int pos = base + t;
+    return slot_of(vr, ring, pos < p1 ? pos : base, a.T_cap);
+  };
+
+  // K fragments (token 16*tb + li, elements 32*ks + 8*lg..) and this lane's
+  // share of the V tile (rows RPI*i + lane/CPR, chunk lane%CPR).
+  auto load_tile = [&](int it, uint4 (&kf)[2][KS], uint4 (&vr_)[VLD]) {
+    const int base = p0 + it * kTT;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const uint16_t* kp = Kbg + (size_t)row_slot(base, 16 * tb + li) * D + 8 * lg;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[tb][ks] = nt_load16(kp + 32 * ks);
+    }
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+      const int t = RPI * i + lane / CPR;
+      const uint16_t* vp = Vbg + (size_t)row_slot(base, t) * D + 8 * (lane % CPR);
+      vr_[i] = nt_load16(vp);
+    }
+  };
+
+  auto compute_tile = [&](int it, const uint4 (&kf)[2][KS], const uint4 (&vr_)[VLD]) {
+    const int base = p0 + it * kTT;
+    // V tile -> LDS (row t, chunk c stored at chunk c ^ swz(t))
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+      const int t = RPI * i + lane / CPR;
+      const int c = lane % CPR;
+      *(uint4*)(vt + t * (2 * D) + 16 * (c ^ vt_swz<D>(t))) = vr_[i];
+    }
+
+    // scores S^T: token rows 16*tb + 4*lg + r, head column li of block hb
+    f32x4_t sc[2][HB];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[tb][ks]),
+                                                         as_bf16x8(qf[hb][ks]), acc,
+                                                         0, 0, 0);
+        sc[tb][hb] = acc;
+      }
+
+    bool valid[2][4];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) valid[tb][r] = base + 16 * tb + 4 * lg + r < p1;
+
+    // online softmax per head (lazy maximum, as in the vector kernel)
+    uint32_t phi[HB][4], plo[HB][4];  // packed bf16 pairs of P_hi / P_lo
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      float x[8];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          x[4 * tb + r] = valid[tb][r] ? sc[tb][hb][r] * a.scale_log2 : neg_inf();
+      float mt = x[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
+      mt = fmaxf(mt, xor16(mt));
+      mt = fmaxf(mt, xor32(mt));
+      if (mt > m[hb] + 8.f) {
+        const float al = fast_exp2(m[hb] - mt);
+        l[hb] *= al;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db][hb] *= al;
+        m[hb] = mt;
+      }
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p[j] = (x[j] == neg_inf()) ? 0.f : fast_exp2(x[j] - m[hb]);
+        l[hb] += p[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t h0b = bf16_bits(p[2 * j]), h1b = bf16_bits(p[2 * j + 1]);
+        const float r0 = p[2 * j] - __uint_as_float(h0b << 16);
+        const float r1 = p[2 * j + 1] - __uint_as_float(h1b << 16);
+        phi[hb][j] = h0b | (h1b << 16);
+        plo[hb][j] = bf16_bits(r0) | (bf16_bits(r1) << 16);
+      }
+    }
+
+    // O^T += V^T . P^T over the 32 tokens of the tile
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      // lane j of group lg addresses row 4*lg + j/4 (+16), columns 16*db + 4*(j%4)
+      const int t0 = 4 * lg + (li >> 2);
+      const int col = 16 * db + 4 * (li & 3);
+      const int c = col >> 3, half = (col & 7) * 2;
+      const unsigned char* a0 = vt + t0 * (2 * D) + 16 * (c ^ vt_swz<D>(t0)) + half;
+      const unsigned char* a1 =
+          vt + (t0 + 16) * (2 * D) + 16 * (c ^ vt_swz<D>(t0 + 16)) + half;
+      typedef s16x4_t __attribute__((address_space(3))) * lds_s16x4;
+      const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4)(__attribute__((address_space(3))) unsigned char*)a0);
+      const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4)(__attribute__((address_space(3))) unsigned char*)a1);
+      const uint4 vtu = make_uint4(
+          (uint32_t)(uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16),
+          (uint32_t)(uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16),
+          (uint32_t)(uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16),
+          (uint32_t)(uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16));
+      const bf16x8_t av = as_bf16x8(vtu);
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const uint4 bh = make_uint4(phi[hb][0], phi[hb][1], phi[hb][2], phi[hb][3]);
+        const uint4 bl = make_uint4(plo[hb][0], plo[hb][1], plo[hb][2], plo[hb][3]);
+        o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, as_bf16x8(bh),
+                                                            o[db][hb], 0, 0, 0);
+        o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, as_bf16x8(bl),
+                                                            o[db][hb], 0, 0, 0);
+      }
+    }
+  };
+
+  uint4 kA[2][KS], vA[VLD], kB[2][KS], vB[VLD];
+  int it = wave;
+  if (it < ntiles) load_tile(it, kA, vA);
+  while (it < ntiles) {
+    int nx = it + kNW;
+    if (nx < ntiles) load_tile(nx, kB, vB);
+    compute_tile(it, kA, vA);
+    it = nx;
+    if (it >= ntiles) break;
+    nx = it + kNW;
+    if (nx < ntiles) load_tile(nx, kA, vA);
+    compute_tile(it, kB, vB);
+    it = nx;
+  }
+
+  // per-head partial sums of the four lane groups
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    l[hb] += xor16(l[hb]);
+    l[hb] += xor32(l[hb]);
+  }
+
+  __syncthreads();  // the V tiles are dead; reuse LDS for the merge
+  float* sm_o = (float*)smem;                       // [NW][NH][D]
+  float* sm_m = sm_o + kNW * NH * D;                // [NW][NH]
+  float* sm_l = sm_m + kNW * NH;                    // [NW][NH]
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int h = hb * 16 + li;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *(f32x4_t*)(sm_o + ((size_t)wave * NH + h) * D + 16 * db + 4 * lg) = o[db][hb];
+    if (lg == 0) {
+      sm_m[wave * NH + h] = m[hb];
+      sm_l[wave * NH + h] = l[hb];
+    }
+  }
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < nh * D; idx += kNW * 64) {
+    const int h = idx / D;
+    const int e = idx - h * D;
+    float M = neg_inf();
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) M = fmaxf(M, sm_m[w * NH + h]);
+    float L = 0.f, O = 0.f;
+    if (M != neg_inf()) {
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) {
+        const float mw = sm_m[w * NH + h];
+        const float wt = (mw == neg_inf()) ? 0.f : fast_exp2(mw - M);
+        L = fmaf(wt, sm_l[w * NH + h], L);
+        O = fmaf(wt, sm_o[((size_t)w * NH + h) * D + e], O);
+      }
+    }
+    const bool empty = !(L > 0.f);
+    const float ov = empty ? 0.f : O / L;
+    const float lse = empty ? neg_inf() : (M + fast_log2(L)) * kLn2;
+    const size_t row = (size_t)b * a.H_q + h0 + h;
+    if (a.S == 1) {
+      a.out[row * D + e] = ov;
+      if (e == 0 && a.lse) a.lse[row] = lse;
+    } else {
+      a.o_part[(row * a.S + s) * D + e] = ov;
+      if (e == 0) a.lse_part[row * a.S + s] = lse;
+    }
+  }
+}
+
+template <int D, int NH>
+hipError_t launch_one(const GqaArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((gqa_decode_mfma<D, NH>), dim3(grid), dim3(kNW * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Heads per work item on the matrix-core path (16 or 32), or 0 if the path
+// does not apply (float32 data, d = 256, or groups small enough for the
+// vector kernel).
+int mfma_heads_per_item(int dtype, int d, int n) {
+  if (dtype != 1 || n < 9) return 0;
+  if (d != 64 && d != 128) return 0;
+  const int r = (n + 15) / 16 * 16;
+  return r < 32 ? r : 32;
+}
+
+int mfma_tile_rows() { return kTT; }
+int mfma_waves() { return kNW; }
+
+hipError_t launch_gqa_mfma(const GqaArgs& a, int d, int heads_per_item, int grid,
+                           hipStream_t st) {
+  switch (d * 1000 + heads_per_item) {
+    case 64016: return launch_one<64, 16>(a, grid, st);
+    case 64032: return launch_one<64, 32>(a, grid, st);
+    case 128016: return launch_one<128, 16>(a, grid, st);
+    case 128032: return launch_one<128, 32>(a, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attn

@@ -30,6 +30,17 @@
 #include "internal.h"
 #include "visible.h"
 
+// Tuning knobs (compile-time; defaults are the measured best).
+#ifndef ATTN_VALU_TILE_BYTES
+#define ATTN_VALU_TILE_BYTES 8192
+#endif
+#ifndef ATTN_VALU_E_SMALL  // elements per lane per row when N <= 4
+#define ATTN_VALU_E_SMALL 16
+#endif
+#ifndef ATTN_VALU_NONTEMPORAL  // K/V are read once: stream past the caches
+#define ATTN_VALU_NONTEMPORAL 1
+#endif
+
 namespace attn {
 namespace {
 
@@ -78,15 +89,27 @@ struct ElemTraits<uint16_t> {
   }
 };
 
+// 16-byte global load of K/V data that is streamed once.
+template <typename T>
+ATTN_DEV uint4 load16(const T* p) {
+#if ATTN_VALU_NONTEMPORAL
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+#else
+  return *(const uint4*)p;
+#endif
+}
+
 // Geometry of one instantiation.
 template <typename T, int D, int N>
 struct Cfg {
   static constexpr int EPC = ElemTraits<T>::EPC;
-  static constexpr int E = (N <= 4) ? 16 : 8;  // elements per lane per row
+  static constexpr int E = (N <= 4) ? ATTN_VALU_E_SMALL : 8;  // per lane per row
   static constexpr int CPL = E / EPC;          // chunks per lane per row
   static constexpr int LPR = D / E;            // lanes per row
   static constexpr int RPI = 64 / LPR;         // rows per load instruction
-  static constexpr int TR_BYTES = N <= 4 ? 16384 : 8192;  // K+V bytes per wave per tile
+  static constexpr int TR_BYTES = ATTN_VALU_TILE_BYTES;  // K+V per wave per tile
   static constexpr int TR0 = TR_BYTES / (2 * D * (int)sizeof(T));
   static constexpr int TR = TR0 > RPI ? TR0 : RPI;  // rows per tile
   static constexpr int RPL = TR / RPI;              // rows per lane per tile
@@ -185,27 +208,36 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
 
   const int span = p1 - p0;
   const int ntiles = span > 0 ? (span + TR - 1) / TR : 0;
-  for (int it = wave; it < ntiles; it += NW) {
+
+  // Issue the 16-byte K and V loads of tile `it` (rows past the split's end
+  // re-read the tile's first row; they get weight 0 below).
+  auto load_tile = [&](int it, uint4 (&kr)[RPL][CPL], uint4 (&vv)[RPL][CPL]) {
     const int base = p0 + it * TR;
-    uint4 kr[RPL][CPL], vv[RPL][CPL];
-    bool valid[RPL];
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
       const int pos = base + rg + i * RPI;
-      valid[i] = pos < p1;
-      const int slot = slot_of(vr, ring, valid[i] ? pos : base, a.T_cap);
+      const int slot = slot_of(vr, ring, pos < p1 ? pos : base, a.T_cap);
       const T* kp = Kbg + (size_t)slot * D + cl * EPC;
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) kr[i][k] = *(const uint4*)(kp + k * LPR * EPC);
+      for (int k = 0; k < CPL; ++k) kr[i][k] = load16(kp + k * LPR * EPC);
     }
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
       const int pos = base + rg + i * RPI;
-      const int slot = slot_of(vr, ring, valid[i] ? pos : base, a.T_cap);
+      const int slot = slot_of(vr, ring, pos < p1 ? pos : base, a.T_cap);
       const T* vp = Vbg + (size_t)slot * D + cl * EPC;
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) vv[i][k] = *(const uint4*)(vp + k * LPR * EPC);
+      for (int k = 0; k < CPL; ++k) vv[i][k] = load16(vp + k * LPR * EPC);
     }
+  };
+
+  // Scores, online softmax and value sums of tile `it`.
+  auto compute_tile = [&](int it, const uint4 (&kr)[RPL][CPL],
+                          const uint4 (&vv)[RPL][CPL]) {
+    const int base = p0 + it * TR;
+    bool valid[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) valid[i] = base + rg + i * RPI < p1;
 
     // scores (log2 domain)
     float sc[RPL][N];
@@ -258,6 +290,23 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
             acc[h][k * EPC + e] = fmaf(p, vf[k][e], acc[h][k * EPC + e]);
       }
     }
+  };
+
+  // Two register stages: the loads of a wave's next tile are in flight
+  // while it computes on the current one.
+  uint4 kA[RPL][CPL], vA[RPL][CPL], kB[RPL][CPL], vB[RPL][CPL];
+  int it = wave;
+  if (it < ntiles) load_tile(it, kA, vA);
+  while (it < ntiles) {
+    int nx = it + NW;
+    if (nx < ntiles) load_tile(nx, kB, vB);
+    compute_tile(it, kA, vA);
+    it = nx;
+    if (it >= ntiles) break;
+    nx = it + NW;
+    if (nx < ntiles) load_tile(nx, kA, vA);
+    compute_tile(it, kB, vB);
+    it = nx;
   }
 
   // ---- merge the row groups of this wave ----------------------------------

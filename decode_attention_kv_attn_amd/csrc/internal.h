@@ -42,6 +42,13 @@ bool valu_geometry(int dtype, int d, int n, ValuGeometry* g);
 hipError_t launch_gqa_valu(const GqaArgs& a, int dtype, int d, int grid,
                            hipStream_t stream);
 
+// Matrix-core path for large groups (bf16).
+int mfma_heads_per_item(int dtype, int d, int n);
+int mfma_tile_rows();
+int mfma_waves();
+hipError_t launch_gqa_mfma(const GqaArgs& a, int d, int heads_per_item, int grid,
+                           hipStream_t stream);
+
 hipError_t launch_combine(const float* o_part, const float* lse_part,
                           float* out, float* lse, int B, int H, int S, int d_v,
                           hipStream_t stream);

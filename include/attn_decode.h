@@ -170,8 +170,8 @@ size_t attn_decode_mla_workspace_bytes(int B, int H, int T_cap, int d_c,
  * set.  With L = max_s lse_part[s] and w_s = exp(lse_part[s] - L):
  *     out = sum_s w_s o_part[s] / sum_s w_s,   lse = L + ln(sum_s w_s).
  * This is the softmax of the attention equation (attention-head section 1)
- * taken over a union of disjoint key sets.  Parts with lse = -inf are empty;
- * if all are, out = 0 and lse = -inf.
+ * taken over a union of disjoint key sets.  Parts with lse = -inf are empty
+ * and their o_part rows are not used; if all are, out = 0 and lse = -inf.
  *
  *   o_part   [B, H, S, d_v] float32     lse_part [B, H, S] float32
  *   out      [B, H, d_v]    float32     lse_out  [B, H] float32, may be NULL

@@ -10,7 +10,8 @@ import pytest
 import decode_attention_kv_attn_amd as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "attn_decode.h")
+HEADERS = [os.path.join(ROOT, "include", h)
+           for h in sorted(os.listdir(os.path.join(ROOT, "include"))) if h.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -22,7 +23,7 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(attn_\w+)\s*\(",
                                  text, flags=re.M)))

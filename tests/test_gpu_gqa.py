@@ -108,6 +108,18 @@ def test_ring_head_out_of_range_is_reduced():
     assert_parity(out, ro, "reduced heads")
 
 
+def test_combine_many_splits_one_row():
+    """One (b, h) row with the largest split count and a 512-wide value."""
+    B, H, S, d_v = 1, 1, 1024, 512
+    g = torch.Generator(device="cpu").manual_seed(6510)
+    o = torch.randn(B, H, S, d_v, generator=g)
+    l = torch.randn(B, H, S, generator=g) * 3
+    out, lse = L.attn_combine(o.to(DEV), l.to(DEV))
+    ro, rl = oracle.combine_ref(o.double().numpy(), l.double().numpy())
+    assert_parity(out, ro, "combine S=1024")
+    assert_lse(lse, rl, "combine S=1024")
+
+
 @pytest.mark.parametrize("num_splits", [1, 2, 7, 64, 1024])
 def test_split_invariance(num_splits):
     T_cap = 2000
@@ -128,7 +140,9 @@ def test_combine_entry():
     l[0, 1, 3] = -math.inf
     l[1, 2, :] = -math.inf
     o[1, 2, :] = 0
-    out, lse = L.attn_combine(o.to(DEV), l.to(DEV))
+    o_dev = o.clone()
+    o_dev[0, 1, 3] = float("nan")    # rows of empty parts are never read
+    out, lse = L.attn_combine(o_dev.to(DEV), l.to(DEV))
     ro, rl = oracle.combine_ref(o.double().numpy(), l.double().numpy())
     assert_parity(out, ro, "combine")
     assert_lse(lse, rl, "combine")
