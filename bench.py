@@ -32,7 +32,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 METRIC = "decode-attention KV-read GB/s (% of HBM peak) and µs/step per layer"
 DEFAULT_WORKLOAD = "llama3_8b_gqa_t4096"
-KERNEL_SOURCES = ["gqa_valu.hip", "visible.h", "device_common.h"]
+KERNEL_SOURCES = {"gqa": ["gqa_valu.hip", "gqa_mfma.hip", "visible.h", "device_common.h"],
+                  "mla": ["mla_mfma.hip", "visible.h", "device_common.h"]}
 
 
 def parse():
@@ -66,23 +67,23 @@ def visible_counts(w, seq_lens):
     return lens - lo
 
 
-def kernel_source_hash():
+def kernel_source_hash(kind="gqa"):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_attention_kv_attn_amd", "csrc")
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[kind]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload):
+def traffic_from_profile(workload, kind="gqa"):
     """HBM bytes per launch from committed rocprofv3 --pmc results, if they
     were taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(kind):
         return None
     return rec.get("bytes_per_launch")
 
@@ -142,8 +143,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = synth.workload(args.workload)
-    if w["kind"] != "gqa":
-        raise SystemExit("only GQA-family workloads are benchmarked here")
+    if w["kind"] == "mla":
+        return bench_mla(args, w, dev)
     print(f"bench: workload {w['name']}: drawing inputs", file=sys.stderr, flush=True)
     inp = synth.gqa_inputs(w, dev)
     s = 2 if w.get("dtype", "bf16") == "bf16" else 4
@@ -232,6 +233,81 @@ def main():
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def bench_mla(args, w, dev):
+    """The absorbed-MLA workload: latent bytes (d_c + d_rope) * s per visible
+    position (attention-head section 5.4, Bytes_MLA), both rooflines."""
+    import numpy as np
+    import torch
+
+    import decode_attention_kv_attn_amd as L
+    import synth
+
+    print(f"bench: workload {w['name']}: drawing inputs", file=sys.stderr, flush=True)
+    inp = synth.mla_inputs(w, dev)
+    B, H, T = w["B"], w["H"], w["T_cap"]
+    dk = w["d_c"] + w["d_rope"]
+    lat_bytes = inp["latent"].numel() * 2
+    R = max(1, math.ceil(args.rotate_bytes * 2**30 / lat_bytes))
+    lats = [inp["latent"]] + [inp["latent"].clone() for _ in range(R - 1)]
+    Tsum = B * T if inp["seq_lens"] is None else int(inp["seq_lens"].clamp(0, T).sum())
+    alg_bytes = Tsum * dk * 2
+    flops = 2 * H * (dk + w["d_c"]) * Tsum
+    S = L.attn_decode_mla_splits(B, H, T, w["d_c"], w["d_rope"], args.num_splits)
+    wsb = L.attn_decode_mla_workspace_bytes(B, H, T, w["d_c"], w["d_rope"], args.num_splits)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty(B, H, w["d_c"], dtype=torch.float32, device=dev)
+    lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+
+    def step(i):
+        L.attn_decode_mla(inp["q"], lats[i % R], inp["d_c"], inp["scale"],
+                          inp["seq_lens"], args.num_splits, out=out, lse=lse,
+                          workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    value = alg_bytes / (ms * 1e-3) / 1e9
+    tflops = flops / (call_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "us_per_step": round(ms * 1e3, 2), "tokens_per_s": round(B / (ms * 1e-3), 1),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w["name"], "B": B, "H": H, "T": T, "d_c": w["d_c"],
+                   "d_rope": w["d_rope"], "splits": S, "cache_copies": R,
+                   "latent_bytes_per_step": alg_bytes, "flops_per_step": flops},
+        "roofline": {"bound": "hbm", "achieved": round(alg_bytes / (call_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(alg_bytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile(w["name"], "mla"),
+                     "kernel": "mla_decode_mfma" + ("" if S == 1 else " + lse_combine"),
+                     "kernel_us": round(call_ms * 1e3, 2)},
+        "mfma_roofline": {"achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "note": "algorithmic flops 2*H*(d_c+d_rope+d_c) per position; "
+                                  "the kernel issues 1.47x that (bf16 hi+lo weights)"},
+    }
+    print(f"bench: {ms * 1e3:.1f} us/step, {value:.0f} GB/s, {tflops:.0f} TFLOP/s",
+          file=sys.stderr, flush=True)
     print(json.dumps(res), flush=True)
 
 

@@ -49,6 +49,15 @@ int mfma_waves();
 hipError_t launch_gqa_mfma(const GqaArgs& a, int d, int heads_per_item, int grid,
                            hipStream_t stream);
 
+// Absorbed MLA on the matrix cores (bf16, d_c = 512, d_rope = 64).
+int mla_heads_per_group();
+int mla_tile_rows();
+hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
+                           float* lse, float* o_part, float* lse_part,
+                           const int32_t* seq_lens, int B, int H, int T_cap,
+                           int S, int chunk, int head_chunks, float scale_log2,
+                           hipStream_t stream);
+
 hipError_t launch_combine(const float* o_part, const float* lse_part,
                           float* out, float* lse, int B, int H, int S, int d_v,
                           hipStream_t stream);

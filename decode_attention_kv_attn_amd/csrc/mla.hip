@@ -1,16 +1,53 @@
-// Absorbed MLA decode: host entry points (matrix-core kernel pending).
+// Absorbed MLA decode: host entry points (checks, split planning, launches).
 #include <math.h>
+#include <stdlib.h>
 
 #include "../../include/attn_decode.h"
 #include "internal.h"
 
 namespace {
 
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
 int check_mla(int B, int H, int T_cap, int d_c, int d_rope) {
   if (B < 0 || H <= 0 || T_cap <= 0) return ATTN_ERR_SHAPE;
   if (d_c != 512 || d_rope != 64) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)B * H > (1LL << 30)) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
+
+struct MlaPlan {
+  int head_chunks, S, chunk;
+  size_t ws_bytes;
+};
+
+int plan_mla(int B, int H, int T_cap, int d_c, int d_rope, int num_splits,
+             MlaPlan* p) {
+  const int st = check_mla(B, H, T_cap, d_c, d_rope);
+  if (st != ATTN_OK) return st;
+  if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_ARG;
+  const int hg = attn::mla_heads_per_group();
+  p->head_chunks = (H + hg - 1) / hg;
+  long long S;
+  if (num_splits > 0) {
+    S = num_splits;
+  } else {
+    // one work group per CU; keep at least two tiles per group
+    const long long units = (long long)(B > 0 ? B : 1) * p->head_chunks;
+    S = (attn::kNumCUs + units - 1) / units;
+    long long smax = T_cap / (2LL * attn::mla_tile_rows());
+    if (smax < 1) smax = 1;
+    if (S > smax) S = smax;
+  }
+  if (S < 1) S = 1;
+  if (S > T_cap) S = T_cap;
+  p->chunk = (int)((T_cap + S - 1) / S);
+  p->S = (T_cap + p->chunk - 1) / p->chunk;
+  p->ws_bytes = attn_decode_workspace_bytes(B, H, d_c, p->S);
+  return ATTN_OK;
+}
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
@@ -18,16 +55,16 @@ extern "C" {
 
 int attn_decode_mla_splits(int B, int H, int T_cap, int d_c, int d_rope,
                            int num_splits) {
-  const int st = check_mla(B, H, T_cap, d_c, d_rope);
-  if (st != ATTN_OK) return st;
-  if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_ARG;
-  return ATTN_ERR_UNSUPPORTED;
+  MlaPlan p;
+  const int st = plan_mla(B, H, T_cap, d_c, d_rope, num_splits, &p);
+  return st == ATTN_OK ? p.S : st;
 }
 
 size_t attn_decode_mla_workspace_bytes(int B, int H, int T_cap, int d_c,
                                        int d_rope, int num_splits) {
-  (void)B; (void)H; (void)T_cap; (void)d_c; (void)d_rope; (void)num_splits;
-  return (size_t)-1;
+  MlaPlan p;
+  const int st = plan_mla(B, H, T_cap, d_c, d_rope, num_splits, &p);
+  return st == ATTN_OK ? p.ws_bytes : (size_t)-1;
 }
 
 int attn_decode_mla(const void* q, const void* latent, float* out,
@@ -35,14 +72,34 @@ int attn_decode_mla(const void* q, const void* latent, float* out,
                     int T_cap, int d_c, int d_rope, float scale,
                     int num_splits, void* workspace, size_t workspace_bytes,
                     void* stream) {
-  (void)lse_out; (void)seq_lens; (void)workspace; (void)workspace_bytes;
-  (void)stream;
-  if (!q || !latent || !out) return ATTN_ERR_NULL;
-  int st = check_mla(B, H, T_cap, d_c, d_rope);
+  MlaPlan p;
+  int st = plan_mla(B, H, T_cap, d_c, d_rope, num_splits, &p);
   if (st != ATTN_OK) return st;
   if (!(scale > 0.f) || isinf(scale)) return ATTN_ERR_ARG;
-  if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_ARG;
-  return ATTN_ERR_UNSUPPORTED;
+  if (B == 0) return ATTN_OK;
+  if (!q || !latent || !out) return ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(latent, 16) || !aligned(out, 16) ||
+      (lse_out && !aligned(lse_out, 4)) || (seq_lens && !aligned(seq_lens, 4)))
+    return ATTN_ERR_ALIGN;
+  float* o_part = nullptr;
+  float* lse_part = nullptr;
+  if (p.S > 1) {
+    if (!workspace || workspace_bytes < p.ws_bytes) return ATTN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+    const size_t rows = (size_t)B * H * p.S;
+    o_part = (float*)workspace;
+    lse_part = (float*)((char*)workspace + round_up(rows * d_c * sizeof(float), 256));
+  }
+  if ((long long)B * p.S * p.head_chunks > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  if (attn::launch_mla_mfma(q, latent, out, lse_out, o_part, lse_part, seq_lens, B,
+                            H, T_cap, p.S, p.chunk, p.head_chunks,
+                            scale * 1.4426950408889634f, s) != hipSuccess)
+    return ATTN_ERR_HIP;
+  if (p.S > 1 && attn::launch_combine(o_part, lse_part, out, lse_out, B, H, p.S,
+                                      d_c, s) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
 }
 
 }  // extern "C"

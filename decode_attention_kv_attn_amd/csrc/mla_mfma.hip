@@ -1,0 +1,358 @@
+// Absorbed MLA decode on the matrix cores (kernel 4).
+//
+// Every query head of a sequence reads the same latent rows [c_j | k^R_j]
+// (xuesongtap "attention-head" note, sections 5.2-5.3: keys absorbed into
+// the query, the RoPE key shared by all heads, values projected after the
+// weighted sum), so both products are dense and run on MFMA 16x16x32 bf16:
+//
+//   S^T[tokens, heads] = L[tokens, 0:576] . Q^T[576, heads]
+//   Z^T[0:512, heads] += L[tokens, 0:512]^T . P^T[tokens, heads]
+//
+// One work group = one (sequence, split) and up to 128 heads: four waves,
+// each owning 32 heads, share every latent tile, so the latent is read from
+// HBM once.  Tiles of 32 rows (36 KiB) go straight from HBM into LDS with
+// 16-byte direct-to-LDS loads, two tiles ahead of the one being computed,
+// through three separate stage buffers (the loop is unrolled by three so
+// each stage is a distinct LDS object; the waits on those loads are
+// explicit).  Score operands are read from the row-major tile; value
+// operands come transposed through ds_read_b64_tr_b16.  Rows are swizzled
+// in 16-byte chunks so both read patterns are free of bank conflicts.
+//
+// The weights keep ~16 significant bits as P_hi + P_lo in bf16 (two MFMAs
+// per value block); the value columns stay exactly bf16.
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "internal.h"
+#include "visible.h"
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kDK = 576;                 // latent row: 512 content + 64 rope
+constexpr int kDV = 512;                 // value columns (the content part)
+constexpr int kTT = 32;                  // rows per tile
+constexpr int kNW = 4;                   // waves per group
+constexpr int kHW = 32;                  // heads per wave
+constexpr int kHG = kNW * kHW;           // heads per group
+constexpr int kRowBytes = kDK * 2;       // 1152
+constexpr int kCPR = kRowBytes / 16;     // 72 chunks per row
+constexpr int kTileBytes = kTT * kRowBytes;         // 36864
+constexpr int kDmaPerWave = kTileBytes / (kNW * 1024);  // 9 x 1 KiB per wave
+constexpr int kKS = kDK / 32;            // 18 score k-steps
+constexpr int kDB = kDV / 16;            // 32 value blocks
+static_assert(kTileBytes % (kNW * 1024) == 0, "tile split");
+
+__shared__ __attribute__((aligned(1024))) unsigned char g_stage0[kTileBytes];
+__shared__ __attribute__((aligned(1024))) unsigned char g_stage1[kTileBytes];
+__shared__ __attribute__((aligned(1024))) unsigned char g_stage2[kTileBytes];
+
+template <int I>
+ATTN_DEV unsigned char* stage() {
+  if constexpr (I == 0) return g_stage0;
+  else if constexpr (I == 1) return g_stage1;
+  else return g_stage2;
+}
+
+// Chunk swizzle: logical 16-byte chunk c of row t sits at chunk c ^ swz(t).
+// Sixteen consecutive rows at one chunk (score operand) and four consecutive
+// rows at two adjacent chunks (transposed value operand) land on distinct
+// banks.  The xor stays inside an aligned group of 8 chunks.
+ATTN_DEV int swz(int t) { return 2 * ((t >> 1) & 3) + ((t >> 3) & 1); }
+
+ATTN_DEV bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+ATTN_DEV uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Work-group barrier that is also a compiler memory barrier, without the
+// release fence of __syncthreads (which would wait for the direct-to-LDS
+// loads still in flight for later tiles).  This wave's own LDS reads are
+// drained first, so a stage is never refilled under a pending read.
+ATTN_DEV void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) (other counters unconstrained), gfx9 encoding.
+template <int N>
+ATTN_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+struct MlaArgs {
+  const uint16_t* q;       // [B, H, 576]
+  const uint16_t* latent;  // [B, T_cap, 576]
+  float* out;              // [B, H, 512] when S == 1
+  float* lse;              // [B, H] (nullable) when S == 1
+  float* o_part;           // [B, H, S, 512]
+  float* lse_part;         // [B, H, S]
+  const int32_t* seq_lens;
+  int H, T_cap, S, chunk, head_chunks;
+  float scale_log2;
+};
+
+__global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int li = lane & 15;
+  const int lg = lane >> 4;
+
+  int bid = blockIdx.x;
+  const int hc = bid % a.head_chunks;
+  bid /= a.head_chunks;
+  const int s = bid % a.S;
+  const int b = bid / a.S;
+
+  const VisibleRange vr = visible_range(a.seq_lens, nullptr, b, a.T_cap, 0);
+  int p0, p1;
+  split_range(vr, s, a.chunk, p0, p1);
+  const int hw0 = hc * kHG + wave * kHW;  // first head of this wave
+  const int span = p1 - p0;
+  const int ntiles = span > 0 ? (span + kTT - 1) / kTT : 0;
+  const unsigned char* lat_b = (const unsigned char*)(a.latent + (size_t)b * a.T_cap * kDK);
+
+  // Q^T fragments: head hw0 + 16*hb + li, elements 32*ks + 8*lg .. +7
+  uint4 qf[2][kKS];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int h = hw0 + 16 * hb + li;
+    const uint16_t* qp = a.q + ((size_t)b * a.H + h) * kDK + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks)
+      qf[hb][ks] = h < a.H ? *(const uint4*)(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
+  }
+
+  f32x4_t o[kDB][2];
+  float m[2], l[2];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    m[hb] = neg_inf();
+    l[hb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) o[db][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Direct-to-LDS loads of tile `it` into stage I: this wave's 9 KiB.  LDS
+  // chunk p of the tile holds row p / 72, logical chunk (p % 72) ^ swz(row).
+  auto issue_tile = [&](auto stage_tag, int it) {
+    constexpr int I = decltype(stage_tag)::value;
+    const int base = p0 + it * kTT;
+    const int nvalid = p1 - base;  // rows of this tile inside the split
+    const unsigned char* tbase = lat_b + (size_t)base * kRowBytes;
+    int lv = lane;
+    asm volatile("" : "+v"(lv));  // recompute the offsets here, do not keep them live
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) {
+      const int blk = wave * kDmaPerWave + j;
+      const int p = blk * 64 + lv;
+      const int t = p / kCPR;
+      // a row past the split re-reads the same chunk of the tile's first row
+      const int off = t < nvalid ? ((16 * p) ^ (swz(t) << 4)) : 16 * (p - t * kCPR);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(tbase + off),
+          (__attribute__((address_space(3))) void*)(stage<I>() + blk * 1024), 16, 0,
+          0);
+    }
+  };
+
+  auto compute_tile = [&](auto stage_tag, int it) {
+    constexpr int I = decltype(stage_tag)::value;
+    const unsigned char* tile = stage<I>();
+    const int base = p0 + it * kTT;
+
+    // scores.  Chunk (4*ks + lg) ^ swz(t) = 8*(ks/2) + ((4*(ks&1) + lg) ^ swz(t)):
+    // two base addresses per row block, the rest is an immediate offset.
+    const unsigned char* abase[2][2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int t = 16 * tb + li;
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        abase[tb][e] = tile + t * kRowBytes + 16 * ((4 * e + lg) ^ swz(t));
+    }
+    f32x4_t sc[2][2] = {};
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      uint4 af[2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        af[tb] = *(const uint4*)(abase[tb][ks & 1] + 128 * (ks >> 1));
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          sc[tb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(af[tb]), as_bf16x8(qf[hb][ks]), sc[tb][hb], 0, 0, 0);
+    }
+
+    // online softmax per head (lazy maximum); weights split into bf16 hi+lo
+    uint32_t phi[2][4], plo[2][4];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float x[8];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          x[4 * tb + r] = (base + 16 * tb + 4 * lg + r < p1)
+                              ? sc[tb][hb][r] * a.scale_log2
+                              : neg_inf();
+      float mt = x[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
+      mt = fmaxf(mt, xor16(mt));
+      mt = fmaxf(mt, xor32(mt));
+      if (mt > m[hb] + 8.f) {
+        const float al = fast_exp2(m[hb] - mt);
+        l[hb] *= al;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          // keep the accumulators in AGPRs across this rare VALU update
+          asm volatile("" : "+a"(o[db][hb]));
+          o[db][hb] *= al;
+          asm volatile("" : "+a"(o[db][hb]));
+        }
+        m[hb] = mt;
+      }
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p[j] = (x[j] == neg_inf()) ? 0.f : fast_exp2(x[j] - m[hb]);
+        l[hb] += p[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t h0b = bf16_bits(p[2 * j]), h1b = bf16_bits(p[2 * j + 1]);
+        phi[hb][j] = h0b | (h1b << 16);
+        plo[hb][j] = bf16_bits(p[2 * j] - __uint_as_float(h0b << 16)) |
+                     (bf16_bits(p[2 * j + 1] - __uint_as_float(h1b << 16)) << 16);
+      }
+    }
+
+    // values: transposed 4x16 reads of rows 4*lg + li/4 (and +16), columns
+    // 16*db + 4*(li&3).  Chunk 2*db + ((li&3)>>1) swizzled = 8*(db/4) +
+    // ((2*(db&3) + ((li&3)>>1)) ^ swz(t)): four bases per row, immediate rest.
+    const int t0 = 4 * lg + (li >> 2);
+    const int half = ((li & 3) & 1) * 8;
+    const unsigned char* vbase[2][4];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int t = t0 + 16 * r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        vbase[r][e] = tile + t * kRowBytes + 16 * ((2 * e + ((li & 3) >> 1)) ^ swz(t)) + half;
+    }
+    typedef s16x4_t __attribute__((address_space(3))) * lds_s16x4;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+      const int imm = 128 * (db >> 2);
+      const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4)(__attribute__((address_space(3))) unsigned char*)(vbase[0][db & 3] + imm));
+      const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4)(__attribute__((address_space(3))) unsigned char*)(vbase[1][db & 3] + imm));
+      const uint4 vu = make_uint4(
+          (uint32_t)(uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16),
+          (uint32_t)(uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16),
+          (uint32_t)(uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16),
+          (uint32_t)(uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16));
+      const bf16x8_t av = as_bf16x8(vu);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            av, as_bf16x8(make_uint4(phi[hb][0], phi[hb][1], phi[hb][2], phi[hb][3])),
+            o[db][hb], 0, 0, 0);
+        o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            av, as_bf16x8(make_uint4(plo[hb][0], plo[hb][1], plo[hb][2], plo[hb][3])),
+            o[db][hb], 0, 0, 0);
+      }
+    }
+  };
+
+  // One pipeline step: tile `it` lives in stage I; tile it+2 goes to stage
+  // (I+2)%3, which every wave finished reading before the barrier.
+  auto step = [&](auto stage_tag, int it) {
+    constexpr int I = decltype(stage_tag)::value;
+    if (it >= ntiles) return;
+    if (it + 1 < ntiles) wait_vmcnt<kDmaPerWave>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (it + 2 < ntiles)
+      issue_tile(std::integral_constant<int, (I + 2) % 3>{}, it + 2);
+    compute_tile(stage_tag, it);
+  };
+
+  if (ntiles > 0) issue_tile(std::integral_constant<int, 0>{}, 0);
+  if (ntiles > 1) issue_tile(std::integral_constant<int, 1>{}, 1);
+  for (int it = 0; it < ntiles; it += 3) {
+    step(std::integral_constant<int, 0>{}, it);
+    step(std::integral_constant<int, 1>{}, it + 1);
+    step(std::integral_constant<int, 2>{}, it + 2);
+  }
+
+  // per-head sums of the four lane groups, then write this wave's heads
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    l[hb] += xor16(l[hb]);
+    l[hb] += xor32(l[hb]);
+  }
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int h = hw0 + 16 * hb + li;
+    if (h >= a.H) continue;
+    const bool empty = !(l[hb] > 0.f);
+    const float inv = empty ? 0.f : 1.f / l[hb];
+    const float lse = empty ? neg_inf() : (m[hb] + fast_log2(l[hb])) * kLn2;
+    const size_t row = (size_t)b * a.H + h;
+    float* dst = (a.S == 1) ? a.out + row * kDV : a.o_part + (row * a.S + s) * kDV;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+      *(f32x4_t*)(dst + 16 * db + 4 * lg) = o[db][hb] * inv;
+    if (lg == 0) {
+      if (a.S == 1) {
+        if (a.lse) a.lse[row] = lse;
+      } else {
+        a.lse_part[row * a.S + s] = lse;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int mla_heads_per_group() { return kHG; }
+int mla_tile_rows() { return kTT; }
+
+hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
+                           float* lse, float* o_part, float* lse_part,
+                           const int32_t* seq_lens, int B, int H, int T_cap,
+                           int S, int chunk, int head_chunks, float scale_log2,
+                           hipStream_t stream) {
+  MlaArgs a;
+  a.q = (const uint16_t*)q;
+  a.latent = (const uint16_t*)latent;
+  a.out = out;
+  a.lse = lse;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.seq_lens = seq_lens;
+  a.H = H;
+  a.T_cap = T_cap;
+  a.S = S;
+  a.chunk = chunk;
+  a.head_chunks = head_chunks;
+  a.scale_log2 = scale_log2;
+  const long long grid = (long long)B * S * head_chunks;
+  hipLaunchKernelGGL(mla_decode_mfma, dim3((unsigned)grid), dim3(kNW * 64), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -137,8 +137,9 @@ size_t attn_decode_gqa_workspace_bytes(int B, int H_q, int H_kv, int T_cap,
  *           normalised latent followed by the shared RoPE key (the one-tensor
  *           cache [batch, seq, compressed_kv_dim + rope_dim] of the baidu
  *           article, section 二).
- *   out     [B, H, d_c] float32: z = sum_j p_j c_j, the latent-space result
- *           before the value up-projection (attention-head section 5.2).
+ *   out     [B, H, d_c] float32, 16-byte aligned: z = sum_j p_j c_j, the
+ *           latent-space result before the value up-projection
+ *           (attention-head section 5.2).
  *   lse_out [B, H] float32, may be NULL.
  *   seq_lens [B] int32, may be NULL (all T_cap); clamped to [0, T_cap].
  *   Scores are scale * (q~ . c_j + q^R . k^R_j): one dot product over the
@@ -147,9 +148,9 @@ size_t attn_decode_gqa_workspace_bytes(int B, int H_q, int H_kv, int T_cap,
  *   scale   must be > 0 and finite: 1/sqrt(d_head_content + d_rope) with the
  *           model's per-head content width (section 5.3 keeps that
  *           denominator; the latent width r does not enter it).
- *   The value columns are used in float16 inside the matrix-core product:
- *   |c| must stay below 65504; magnitudes under 2^-17 lose relative
- *   precision (absolute error below 2^-25).
+ *   Scores and values are formed on the matrix cores from the bf16 data
+ *   exactly as given; the softmax weights enter the value product with about
+ *   16 significant bits (a bf16 high part plus a bf16 remainder).
  *   num_splits / workspace / stream as for attn_decode_gqa, with
  *   attn_decode_mla_workspace_bytes giving the size.
  */
