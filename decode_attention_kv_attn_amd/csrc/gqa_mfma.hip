@@ -48,10 +48,17 @@ ATTN_DEV uint4 nt_load16(const void* p) {
 
 ATTN_DEV bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-// Round-to-nearest-even float -> bf16 bits (finite inputs).
-ATTN_DEV uint32_t bf16_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+
+// (a, b) -> packed bf16 high parts (round to nearest even, v_cvt_pk_bf16_f32)
+// and packed bf16 remainders a - hi(a), b - hi(b): hi + lo carries about 16
+// significant bits of each weight.
+ATTN_DEV void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{a, b}, bf16x2_v));
+  const float ra = a - __uint_as_float(hi << 16);
+  const float rb = b - __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{ra, rb}, bf16x2_v));
 }
 
 // Chunk swizzle of the V tile in LDS: 16-byte chunk c of row t is stored at
@@ -224,13 +231,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
         l[hb] += p[j];
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t h0b = bf16_bits(p[2 * j]), h1b = bf16_bits(p[2 * j + 1]);
-        const float r0 = p[2 * j] - __uint_as_float(h0b << 16);
-        const float r1 = p[2 * j + 1] - __uint_as_float(h1b << 16);
-        phi[hb][j] = h0b | (h1b << 16);
-        plo[hb][j] = bf16_bits(r0) | (bf16_bits(r1) << 16);
-      }
+      for (int j = 0; j < 4; ++j) split_bf16(p[2 * j], p[2 * j + 1], phi[hb][j], plo[hb][j]);
     }
 
     // O^T += V^T . P^T over the 32 tokens of the tile

@@ -67,9 +67,17 @@ ATTN_DEV int swz(int t) { return 2 * ((t >> 1) & 3) + ((t >> 3) & 1); }
 
 ATTN_DEV bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-ATTN_DEV uint32_t bf16_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+
+// (a, b) -> packed bf16 high parts (round to nearest even, v_cvt_pk_bf16_f32)
+// and packed bf16 remainders a - hi(a), b - hi(b): hi + lo carries about 16
+// significant bits of each weight.
+ATTN_DEV void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{a, b}, bf16x2_v));
+  const float ra = a - __uint_as_float(hi << 16);
+  const float rb = b - __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{ra, rb}, bf16x2_v));
 }
 
 // Work-group barrier that is also a compiler memory barrier, without the
@@ -179,21 +187,29 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
         abase[tb][e] = tile + t * kRowBytes + 16 * ((4 * e + lg) ^ swz(t));
     }
     f32x4_t sc[2][2] = {};
+    // operand reads run one k-step ahead of the MFMAs that use them
+    uint4 af[2][2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) af[0][tb] = *(const uint4*)(abase[tb][0]);
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      uint4 af[2];
+      const int cur = ks & 1;
+      if (ks + 1 < kKS) {
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-        af[tb] = *(const uint4*)(abase[tb][ks & 1] + 128 * (ks >> 1));
+        for (int tb = 0; tb < 2; ++tb)
+          af[cur ^ 1][tb] =
+              *(const uint4*)(abase[tb][(ks + 1) & 1] + 128 * ((ks + 1) >> 1));
+      }
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
           sc[tb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(af[tb]), as_bf16x8(qf[hb][ks]), sc[tb][hb], 0, 0, 0);
+              as_bf16x8(af[cur][tb]), as_bf16x8(qf[hb][ks]), sc[tb][hb], 0, 0, 0);
     }
 
     // online softmax per head (lazy maximum); weights split into bf16 hi+lo
+    const bool full = base + kTT <= p1;  // uniform: no masked row in the tile
     uint32_t phi[2][4], plo[2][4];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -201,10 +217,12 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          x[4 * tb + r] = (base + 16 * tb + 4 * lg + r < p1)
-                              ? sc[tb][hb][r] * a.scale_log2
-                              : neg_inf();
+        for (int r = 0; r < 4; ++r) x[4 * tb + r] = sc[tb][hb][r] * a.scale_log2;
+      if (!full) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (base + 16 * (j >> 2) + 4 * lg + (j & 3) >= p1) x[j] = neg_inf();
+      }
       float mt = x[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
@@ -225,16 +243,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
       float p[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        p[j] = (x[j] == neg_inf()) ? 0.f : fast_exp2(x[j] - m[hb]);
+        // m is finite once any row of this head was visible; masked rows
+        // (only in a partial tile) get weight 0
+        p[j] = (!full && x[j] == neg_inf()) ? 0.f : fast_exp2(x[j] - m[hb]);
         l[hb] += p[j];
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t h0b = bf16_bits(p[2 * j]), h1b = bf16_bits(p[2 * j + 1]);
-        phi[hb][j] = h0b | (h1b << 16);
-        plo[hb][j] = bf16_bits(p[2 * j] - __uint_as_float(h0b << 16)) |
-                     (bf16_bits(p[2 * j + 1] - __uint_as_float(h1b << 16)) << 16);
-      }
+      for (int j = 0; j < 4; ++j) split_bf16(p[2 * j], p[2 * j + 1], phi[hb][j], plo[hb][j]);
     }
 
     // values: transposed 4x16 reads of rows 4*lg + li/4 (and +16), columns
@@ -251,27 +266,33 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
         vbase[r][e] = tile + t * kRowBytes + 16 * ((2 * e + ((li & 3) >> 1)) ^ swz(t)) + half;
     }
     typedef s16x4_t __attribute__((address_space(3))) * lds_s16x4;
-#pragma unroll
-    for (int db = 0; db < kDB; ++db) {
+    auto read_v = [&](int db) {
       const int imm = 128 * (db >> 2);
       const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4)(__attribute__((address_space(3))) unsigned char*)(vbase[0][db & 3] + imm));
       const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4)(__attribute__((address_space(3))) unsigned char*)(vbase[1][db & 3] + imm));
-      const uint4 vu = make_uint4(
-          (uint32_t)(uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16),
-          (uint32_t)(uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16),
-          (uint32_t)(uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16),
-          (uint32_t)(uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16));
-      const bf16x8_t av = as_bf16x8(vu);
+      return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    typedef short s16x8_t __attribute__((ext_vector_type(8)));
+    const bf16x8_t bh[2] = {
+        as_bf16x8(make_uint4(phi[0][0], phi[0][1], phi[0][2], phi[0][3])),
+        as_bf16x8(make_uint4(phi[1][0], phi[1][1], phi[1][2], phi[1][3]))};
+    const bf16x8_t bl[2] = {
+        as_bf16x8(make_uint4(plo[0][0], plo[0][1], plo[0][2], plo[0][3])),
+        as_bf16x8(make_uint4(plo[1][0], plo[1][1], plo[1][2], plo[1][3]))};
+    // transposed value reads run one block ahead of their MFMAs
+    s16x8_t vf[2];
+    vf[0] = read_v(0);
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+      const int cur = db & 1;
+      if (db + 1 < kDB) vf[cur ^ 1] = read_v(db + 1);
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, vf[cur]);
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            av, as_bf16x8(make_uint4(phi[hb][0], phi[hb][1], phi[hb][2], phi[hb][3])),
-            o[db][hb], 0, 0, 0);
-        o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            av, as_bf16x8(make_uint4(plo[hb][0], plo[hb][1], plo[hb][2], plo[hb][3])),
-            o[db][hb], 0, 0, 0);
+        o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh[hb], o[db][hb], 0, 0, 0);
+        o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl[hb], o[db][hb], 0, 0, 0);
       }
     }
   };
