@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--probe", action="store_true",
+                    help="only run the HBM read probe and a 1 GiB plain copy")
     return ap.parse_args()
 
 
@@ -128,6 +130,48 @@ def cpu_baseline(w, inp, seconds):
                       f"({len(units)} per step) in {dt:.1f} s, float64 numpy"}
 
 
+def probe_read_gbs(dev, nbytes=4 << 30, reps=10):
+    """Best streaming-read rate of this GPU (attn_probe_read over a buffer far
+    larger than the caches), in GB/s."""
+    import torch
+
+    import decode_attention_kv_attn_amd as L
+    x = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    x.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    best = 0.0
+    for blocks in (256 * 8, 256 * 32):
+        for _ in range(2):
+            L.attn_probe_read(x, sink, blocks)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            L.attn_probe_read(x, sink, blocks)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del x
+    return best
+
+
+def run_probe(dev):
+    """Read probe plus a plain 1 GiB copy (the known-size kernel that scales
+    the FETCH_SIZE / WRITE_SIZE counters)."""
+    import torch
+
+    import decode_attention_kv_attn_amd as L
+    read = probe_read_gbs(dev)
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        L.attn_probe_copy(dst, src)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe_read_GBps": round(read, 1), "copy_bytes": n,
+                      "copy_launches": 3}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -142,6 +186,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.probe:
+        return run_probe(dev)
     w = synth.workload(args.workload)
     if w["kind"] == "mla":
         return bench_mla(args, w, dev)

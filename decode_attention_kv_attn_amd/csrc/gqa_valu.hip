@@ -37,6 +37,9 @@
 #ifndef ATTN_VALU_E_SMALL  // elements per lane per row when N <= 4
 #define ATTN_VALU_E_SMALL 16
 #endif
+#ifndef ATTN_VALU_WAVES  // waves per work group (upper bound)
+#define ATTN_VALU_WAVES 8
+#endif
 #ifndef ATTN_VALU_NONTEMPORAL  // K/V are read once: stream past the caches
 #define ATTN_VALU_NONTEMPORAL 1
 #endif
@@ -114,7 +117,8 @@ struct Cfg {
   static constexpr int TR = TR0 > RPI ? TR0 : RPI;  // rows per tile
   static constexpr int RPL = TR / RPI;              // rows per lane per tile
   static constexpr int NW0 = 15360 / (N * D);       // LDS cap for the merge
-  static constexpr int NW = NW0 >= 8 ? 8 : (NW0 >= 4 ? 4 : 2);
+  static constexpr int NWL = NW0 >= 16 ? 16 : (NW0 >= 8 ? 8 : (NW0 >= 4 ? 4 : 2));
+  static constexpr int NW = NWL < ATTN_VALU_WAVES ? NWL : ATTN_VALU_WAVES;
   static_assert(E % EPC == 0 && D % E == 0, "lane split");
   static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "lanes per row");
   static_assert(TR % RPI == 0, "tile rows");

@@ -109,7 +109,8 @@ struct MlaArgs {
 
 __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // uniform across the wave: keep wave-derived offsets in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15;
   const int lg = lane >> 4;
 
@@ -150,28 +151,46 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
 
   // Direct-to-LDS loads of tile `it` into stage I: this wave's 9 KiB.  LDS
   // chunk p of the tile holds row p / 72, logical chunk (p % 72) ^ swz(row).
-  auto issue_tile = [&](auto stage_tag, int it) {
+  // Per-lane byte offsets inside a full tile of this wave's direct-to-LDS
+  // loads: LDS chunk p = blk*64 + lane holds row p/72, logical chunk
+  // (p%72) ^ swz(row).  Offsets are < 2^16, two per register.
+  uint32_t dma_off[(kDmaPerWave + 1) / 2];
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j) {
+    const int p = (wave * kDmaPerWave + j) * 64 + lane;
+    const int t = p / kCPR;
+    const uint32_t off = t * kRowBytes + 16 * ((p - t * kCPR) ^ swz(t));
+    if (j & 1) dma_off[j >> 1] |= off << 16;
+    else dma_off[j >> 1] = off;
+  }
+
+  // Direct-to-LDS load j (of kDmaPerWave) of tile `it` into stage I.
+  auto issue_piece = [&](auto stage_tag, int it, int j) {
     constexpr int I = decltype(stage_tag)::value;
     const int base = p0 + it * kTT;
     const int nvalid = p1 - base;  // rows of this tile inside the split
     const unsigned char* tbase = lat_b + (size_t)base * kRowBytes;
-    int lv = lane;
-    asm volatile("" : "+v"(lv));  // recompute the offsets here, do not keep them live
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) {
-      const int blk = wave * kDmaPerWave + j;
-      const int p = blk * 64 + lv;
+    const int blk = wave * kDmaPerWave + j;
+    uint32_t off = (dma_off[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+    if (nvalid < kTT) {  // uniform: the split's last, partial tile
+      const int p = blk * 64 + lane;
       const int t = p / kCPR;
-      // a row past the split re-reads the same chunk of the tile's first row
-      const int off = t < nvalid ? ((16 * p) ^ (swz(t) << 4)) : 16 * (p - t * kCPR);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(tbase + off),
-          (__attribute__((address_space(3))) void*)(stage<I>() + blk * 1024), 16, 0,
-          0);
+      // a row past the split reads the same chunk of the tile's first row
+      if (t >= nvalid) off = 16 * (p - t * kCPR);
     }
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(tbase + off),
+        (__attribute__((address_space(3))) void*)(stage<I>() + blk * 1024), 16, 0, 0);
+  };
+  auto issue_tile = [&](auto stage_tag, int it) {
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) issue_piece(stage_tag, it, j);
   };
 
-  auto compute_tile = [&](auto stage_tag, int it) {
+  // Computes tile `it` from stage I; when `pf` is set, the loads of tile
+  // it+2 (into stage (I+2)%3) are issued piece by piece between the score
+  // MFMAs, so their issue stalls overlap matrix work.
+  auto compute_tile = [&](auto stage_tag, int it, bool pf) {
     constexpr int I = decltype(stage_tag)::value;
     const unsigned char* tile = stage<I>();
     const int base = p0 + it * kTT;
@@ -193,6 +212,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
     for (int tb = 0; tb < 2; ++tb) af[0][tb] = *(const uint4*)(abase[tb][0]);
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
+      if (pf && (ks & 1) == 0 && (ks >> 1) < kDmaPerWave)
+        issue_piece(std::integral_constant<int, (I + 2) % 3>{}, it + 2, ks >> 1);
       const int cur = ks & 1;
       if (ks + 1 < kKS) {
 #pragma unroll
@@ -213,11 +234,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
     uint32_t phi[2][4], plo[2][4];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
+      // raw scores; the scale (> 0) is applied once to the maximum and fused
+      // into the exponent below
       float x[8];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[4 * tb + r] = sc[tb][hb][r] * a.scale_log2;
+        for (int r = 0; r < 4; ++r) x[4 * tb + r] = sc[tb][hb][r];
       if (!full) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
@@ -228,6 +251,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
       for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
       mt = fmaxf(mt, xor16(mt));
       mt = fmaxf(mt, xor32(mt));
+      mt *= a.scale_log2;
       if (mt > m[hb] + 8.f) {
         const float al = fast_exp2(m[hb] - mt);
         l[hb] *= al;
@@ -245,7 +269,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
       for (int j = 0; j < 8; ++j) {
         // m is finite once any row of this head was visible; masked rows
         // (only in a partial tile) get weight 0
-        p[j] = (!full && x[j] == neg_inf()) ? 0.f : fast_exp2(x[j] - m[hb]);
+        p[j] = (!full && x[j] == neg_inf()) ? 0.f
+                                             : fast_exp2(fmaf(x[j], a.scale_log2, -m[hb]));
         l[hb] += p[j];
       }
 #pragma unroll
@@ -305,9 +330,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
     if (it + 1 < ntiles) wait_vmcnt<kDmaPerWave>();
     else wait_vmcnt<0>();
     lds_barrier();
-    if (it + 2 < ntiles)
-      issue_tile(std::integral_constant<int, (I + 2) % 3>{}, it + 2);
-    compute_tile(stage_tag, it);
+    compute_tile(stage_tag, it, it + 2 < ntiles);
   };
 
   if (ntiles > 0) issue_tile(std::integral_constant<int, 0>{}, 0);
