@@ -19,6 +19,9 @@ __all__ = [
     "attn_decode_gqa_splits", "attn_decode_gqa_workspace_bytes",
     "attn_decode_mla_splits", "attn_decode_mla_workspace_bytes",
     "attn_decode_workspace_bytes", "attn_status_string",
+    "attn_kv_append", "attn_kv_append_ring",
+    "attn_decode_gqa_global", "attn_decode_gqa_global_splits",
+    "attn_decode_gqa_global_workspace_bytes",
 ]
 
 ATTN_F32 = 0
@@ -32,6 +35,11 @@ _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_
 _SIGS = {
     "attn_decode_gqa": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                              _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "attn_decode_gqa_global": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
+                                    _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz,
+                                    _vp]),
+    "attn_decode_gqa_global_splits": (_i, [_i] * 9),
+    "attn_decode_gqa_global_workspace_bytes": (_sz, [_i] * 9),
     "attn_decode_gqa_splits": (_i, [_i] * 9),
     "attn_decode_gqa_workspace_bytes": (_sz, [_i] * 9),
     "attn_decode_mla": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
@@ -41,6 +49,8 @@ _SIGS = {
     "attn_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "attn_decode_workspace_bytes": (_sz, [_i] * 4),
     "attn_status_string": (ctypes.c_char_p, [_i]),
+    "attn_kv_append": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "attn_kv_append_ring": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "attn_probe_read": (_i, [_vp, _sz, _vp, _i, _vp]),
     "attn_probe_copy": (_i, [_vp, _vp, _sz, _vp]),
 }
@@ -164,6 +174,50 @@ def attn_decode_gqa(q, k, v, seq_lens=None, ring_head=None, window=0,
     return out, lse
 
 
+def attn_decode_gqa_global_splits(B, H_q, H_kv, T_cap, d, dtype, window,
+                                  n_global, num_splits=0):
+    return library().attn_decode_gqa_global_splits(
+        B, H_q, H_kv, T_cap, d, dtype, window, n_global, num_splits)
+
+
+def attn_decode_gqa_global_workspace_bytes(B, H_q, H_kv, T_cap, d, dtype,
+                                           window, n_global, num_splits=0):
+    return library().attn_decode_gqa_global_workspace_bytes(
+        B, H_q, H_kv, T_cap, d, dtype, window, n_global, num_splits)
+
+
+def attn_decode_gqa_global(q, k, v, global_pos, window, seq_lens=None,
+                           scale=None, num_splits=0, out=None, lse=None,
+                           workspace=None, want_lse=True, stream=None):
+    """Sliding window plus global positions over a linear cache.
+
+    ``global_pos``: sorted int32 [n_global] device tensor (or None for none);
+    other arguments as for :func:`attn_decode_gqa` without ``ring_head``.
+    """
+    _need_dev(q, k, v, seq_lens, global_pos, out, lse)
+    B, H_q, d = q.shape
+    _, H_kv, T_cap, _ = k.shape
+    dt = _dtype_code(q)
+    n_global = 0 if global_pos is None else global_pos.numel()
+    if out is None:
+        out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    nbytes = attn_decode_gqa_global_workspace_bytes(
+        B, H_q, H_kv, T_cap, d, dt, window, n_global, num_splits)
+    if nbytes == 2**64 - 1:
+        nbytes = 0
+    workspace = _workspace(nbytes, q.device, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = library().attn_decode_gqa_global(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seq_lens),
+        _ptr(global_pos), n_global, B, H_q, H_kv, T_cap, d, dt, window,
+        0.0 if scale is None else float(scale), num_splits, _ptr(workspace),
+        ws_bytes, _stream(stream, q.device))
+    _check("attn_decode_gqa_global", st)
+    return out, lse
+
+
 def attn_decode_mla_splits(B, H, T_cap, d_c, d_rope, num_splits=0):
     return library().attn_decode_mla_splits(B, H, T_cap, d_c, d_rope, num_splits)
 
@@ -213,6 +267,39 @@ def attn_combine(o_part, lse_part, out=None, lse=None, want_lse=True,
                                 _stream(stream, o_part.device))
     _check("attn_combine", st)
     return out, lse
+
+
+def _cache_dims(cache):
+    if cache.dim() == 4:
+        B, H, T_cap, d = cache.shape
+    elif cache.dim() == 3:  # latent cache [B, T_cap, width]
+        (B, T_cap, d), H = cache.shape, 1
+    else:
+        raise ValueError("cache must be [B, H, T, d] or [B, T, d]")
+    return B, H, T_cap, d
+
+
+def attn_kv_append(k_cache, k_new, positions, v_cache=None, v_new=None,
+                   stream=None):
+    """Write k_new (and v_new) [B, H, d] at row positions[b] of the cache."""
+    _need_dev(k_cache, k_new, positions, v_cache, v_new)
+    B, H, T_cap, d = _cache_dims(k_cache)
+    st = library().attn_kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(k_new),
+                                  _ptr(v_new), _ptr(positions), B, H, T_cap, d,
+                                  _dtype_code(k_cache), _stream(stream, k_cache.device))
+    _check("attn_kv_append", st)
+
+
+def attn_kv_append_ring(k_cache, k_new, ring_head, v_cache=None, v_new=None,
+                        stream=None):
+    """Advance ring_head[b] (in place) and write the rows at the new slot."""
+    _need_dev(k_cache, k_new, ring_head, v_cache, v_new)
+    B, H, T_cap, d = _cache_dims(k_cache)
+    st = library().attn_kv_append_ring(_ptr(k_cache), _ptr(v_cache), _ptr(k_new),
+                                       _ptr(v_new), _ptr(ring_head), B, H, T_cap, d,
+                                       _dtype_code(k_cache),
+                                       _stream(stream, k_cache.device))
+    _check("attn_kv_append_ring", st)
 
 
 def attn_probe_read(src, sink, blocks=0, stream=None):

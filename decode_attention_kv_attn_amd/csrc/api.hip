@@ -38,10 +38,13 @@ struct GqaPlan {
   size_t ws_bytes;  // workspace needed
 };
 
-// Largest number of positions any sequence can have visible.
-int max_visible(int T_cap, int window, int ring) {
+// Largest number of positions a non-global query can have visible (a query
+// that is itself a global position sees more; the last split takes the rest).
+int max_visible(int T_cap, int window, int ring, int n_global) {
   if (ring) return window > 0 ? window : T_cap;
-  return window > 0 ? (window < T_cap ? window : T_cap) : T_cap;
+  if (window <= 0) return T_cap;
+  const long long v = (long long)window + n_global;
+  return v < T_cap ? (int)v : T_cap;
 }
 
 int check_gqa_shape(int B, int H_q, int H_kv, int T_cap, int d, int dtype,
@@ -58,9 +61,11 @@ int check_gqa_shape(int B, int H_q, int H_kv, int T_cap, int d, int dtype,
 }
 
 int plan_gqa(int B, int H_q, int H_kv, int T_cap, int d, int dtype, int window,
-             int ring, int num_splits, GqaPlan* p) {
+             int ring, int n_global, int num_splits, GqaPlan* p) {
   int st = check_gqa_shape(B, H_q, H_kv, T_cap, d, dtype, window, ring);
   if (st != ATTN_OK) return st;
+  if (n_global < 0 || n_global > ATTN_MAX_GLOBAL || (ring && n_global > 0))
+    return ATTN_ERR_ARG;
   if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_ARG;
   const int n = H_q / H_kv;
   ValuGeometry geo;
@@ -76,7 +81,7 @@ int plan_gqa(int B, int H_q, int H_kv, int T_cap, int d, int dtype, int window,
   p->N = geo.heads_per_item;
   p->head_chunks = (n + geo.heads_per_item - 1) / geo.heads_per_item;
   p->waves = geo.waves;
-  const int mv = max_visible(T_cap, window, ring);
+  const int mv = max_visible(T_cap, window, ring, n_global);
   long long S;
   if (num_splits > 0) {
     S = num_splits;
@@ -114,7 +119,16 @@ size_t attn_decode_workspace_bytes(int B, int H, int d_v, int num_splits) {
 int attn_decode_gqa_splits(int B, int H_q, int H_kv, int T_cap, int d,
                            int dtype, int window, int ring, int num_splits) {
   GqaPlan p;
-  const int st = plan_gqa(B, H_q, H_kv, T_cap, d, dtype, window, ring,
+  const int st = plan_gqa(B, H_q, H_kv, T_cap, d, dtype, window, ring, 0,
+                          num_splits, &p);
+  return st == ATTN_OK ? p.S : st;
+}
+
+int attn_decode_gqa_global_splits(int B, int H_q, int H_kv, int T_cap, int d,
+                                  int dtype, int window, int n_global,
+                                  int num_splits) {
+  GqaPlan p;
+  const int st = plan_gqa(B, H_q, H_kv, T_cap, d, dtype, window, 0, n_global,
                           num_splits, &p);
   return st == ATTN_OK ? p.S : st;
 }
@@ -123,23 +137,42 @@ size_t attn_decode_gqa_workspace_bytes(int B, int H_q, int H_kv, int T_cap,
                                        int d, int dtype, int window, int ring,
                                        int num_splits) {
   GqaPlan p;
-  const int st = plan_gqa(B, H_q, H_kv, T_cap, d, dtype, window, ring,
+  const int st = plan_gqa(B, H_q, H_kv, T_cap, d, dtype, window, ring, 0,
                           num_splits, &p);
   return st == ATTN_OK ? p.ws_bytes : (size_t)-1;
 }
 
-int attn_decode_gqa(const void* q, const void* k, const void* v, float* out,
-                    float* lse_out, const int32_t* seq_lens,
-                    const int32_t* ring_head, int B, int H_q, int H_kv,
-                    int T_cap, int d, int dtype, int window, float scale,
-                    int num_splits, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+size_t attn_decode_gqa_global_workspace_bytes(int B, int H_q, int H_kv,
+                                              int T_cap, int d, int dtype,
+                                              int window, int n_global,
+                                              int num_splits) {
+  GqaPlan p;
+  const int st = plan_gqa(B, H_q, H_kv, T_cap, d, dtype, window, 0, n_global,
+                          num_splits, &p);
+  return st == ATTN_OK ? p.ws_bytes : (size_t)-1;
+}
+
+}  // extern "C"
+
+namespace attn {
+namespace {
+
+// Shared body of the two GQA entry points.
+int decode_gqa(const void* q, const void* k, const void* v, float* out,
+               float* lse_out, const int32_t* seq_lens, const int32_t* ring_head,
+               const int32_t* gpos, int n_global, int B, int H_q, int H_kv,
+               int T_cap, int d, int dtype, int window, float scale,
+               int num_splits, void* workspace, size_t workspace_bytes,
+               void* stream) {
   const int ring = ring_head != nullptr;
   GqaPlan p;
-  int st = plan_gqa(B, H_q, H_kv, T_cap, d, dtype, window, ring, num_splits, &p);
+  int st = plan_gqa(B, H_q, H_kv, T_cap, d, dtype, window, ring, n_global,
+                    num_splits, &p);
   if (st != ATTN_OK) return st;
   if (B == 0) return ATTN_OK;  // empty batch: nothing to read or write
   if (!q || !k || !v || !out) return ATTN_ERR_NULL;
+  if (n_global > 0 && !gpos) return ATTN_ERR_NULL;
+  if (gpos && !aligned(gpos, 4)) return ATTN_ERR_ALIGN;
   if (isinf(scale)) return ATTN_ERR_ARG;
   if (!(scale > 0.f)) scale = 1.0f / sqrtf((float)d);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 4) ||
@@ -159,6 +192,8 @@ int attn_decode_gqa(const void* q, const void* k, const void* v, float* out,
   a.lse = lse_out;
   a.seq_lens = seq_lens;
   a.ring_head = ring_head;
+  a.gpos = n_global > 0 ? gpos : nullptr;
+  a.n_global = n_global;
   a.B = B;
   a.H_q = H_q;
   a.H_kv = H_kv;
@@ -189,6 +224,34 @@ int attn_decode_gqa(const void* q, const void* k, const void* v, float* out,
       return ATTN_ERR_HIP;
   }
   return ATTN_OK;
+}
+
+}  // namespace
+}  // namespace attn
+
+extern "C" {
+
+int attn_decode_gqa(const void* q, const void* k, const void* v, float* out,
+                    float* lse_out, const int32_t* seq_lens,
+                    const int32_t* ring_head, int B, int H_q, int H_kv,
+                    int T_cap, int d, int dtype, int window, float scale,
+                    int num_splits, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return decode_gqa(q, k, v, out, lse_out, seq_lens, ring_head, nullptr, 0, B,
+                    H_q, H_kv, T_cap, d, dtype, window, scale, num_splits,
+                    workspace, workspace_bytes, stream);
+}
+
+int attn_decode_gqa_global(const void* q, const void* k, const void* v,
+                           float* out, float* lse_out, const int32_t* seq_lens,
+                           const int32_t* global_pos, int n_global, int B,
+                           int H_q, int H_kv, int T_cap, int d, int dtype,
+                           int window, float scale, int num_splits,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return decode_gqa(q, k, v, out, lse_out, seq_lens, nullptr, global_pos,
+                    n_global, B, H_q, H_kv, T_cap, d, dtype, window, scale,
+                    num_splits, workspace, workspace_bytes, stream);
 }
 
 int attn_combine(const float* o_part, const float* lse_part, float* out,

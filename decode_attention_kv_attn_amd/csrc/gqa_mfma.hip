@@ -108,11 +108,11 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   const int g = bid % a.H_kv;
   const int b = bid / a.H_kv;
 
-  const VisibleRange vr =
-      visible_range(a.seq_lens, a.ring_head, b, a.T_cap, a.window);
+  const VisibleRange vr = visible_range(a.seq_lens, a.ring_head, b, a.T_cap,
+                                        a.window, a.gpos, a.n_global);
   const bool ring = a.ring_head != nullptr;
-  int p0, p1;
-  split_range(vr, s, a.chunk, p0, p1);
+  int p0, p1;  // this split's virtual rows
+  split_range(vr, s, a.S, a.chunk, p0, p1);
   const int h0 = g * a.n + hc * NH;
   const int nh = min(NH, a.n - hc * NH);
 
@@ -148,9 +148,9 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   const int span = p1 - p0;
   const int ntiles = span > 0 ? (span + kTT - 1) / kTT : 0;
 
-  auto row_slot = [&](int base, int t) {
-    const int pos = base + t;
-    return slot_of(vr, ring, pos < p1 ? pos : base, a.T_cap);
+  auto tile_row = [&](int base, int t) {
+    const int vi = base + t;
+    return row_slot(vr, ring, base >= vr.n_extra, vi < p1 ? vi : base, a.T_cap);
   };
 
   // K fragments (token 16*tb + li, elements 32*ks + 8*lg..) and this lane's
@@ -159,14 +159,14 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
     const int base = p0 + it * kTT;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const uint16_t* kp = Kbg + (size_t)row_slot(base, 16 * tb + li) * D + 8 * lg;
+      const uint16_t* kp = Kbg + (size_t)tile_row(base, 16 * tb + li) * D + 8 * lg;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kf[tb][ks] = nt_load16(kp + 32 * ks);
     }
 #pragma unroll
     for (int i = 0; i < VLD; ++i) {
       const int t = RPI * i + lane / CPR;
-      const uint16_t* vp = Vbg + (size_t)row_slot(base, t) * D + 8 * (lane % CPR);
+      const uint16_t* vp = Vbg + (size_t)tile_row(base, t) * D + 8 * (lane % CPR);
       vr_[i] = nt_load16(vp);
     }
   };

@@ -177,11 +177,11 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
   const int g = bid % a.H_kv;
   const int b = bid / a.H_kv;
 
-  const VisibleRange vr =
-      visible_range(a.seq_lens, a.ring_head, b, a.T_cap, a.window);
+  const VisibleRange vr = visible_range(a.seq_lens, a.ring_head, b, a.T_cap,
+                                        a.window, a.gpos, a.n_global);
   const bool ring = a.ring_head != nullptr;
-  int p0, p1;
-  split_range(vr, s, a.chunk, p0, p1);
+  int p0, p1;  // this split's virtual rows
+  split_range(vr, s, a.S, a.chunk, p0, p1);
   const int h0 = g * a.n + hc * N;       // first query head served
   const int nh = min(N, a.n - hc * N);   // heads actually present
 
@@ -217,18 +217,19 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
   // re-read the tile's first row; they get weight 0 below).
   auto load_tile = [&](int it, uint4 (&kr)[RPL][CPL], uint4 (&vv)[RPL][CPL]) {
     const int base = p0 + it * TR;
+    const bool fast = base >= vr.n_extra;  // uniform: no global rows in the tile
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-      const int pos = base + rg + i * RPI;
-      const int slot = slot_of(vr, ring, pos < p1 ? pos : base, a.T_cap);
+      const int vi = base + rg + i * RPI;
+      const int slot = row_slot(vr, ring, fast, vi < p1 ? vi : base, a.T_cap);
       const T* kp = Kbg + (size_t)slot * D + cl * EPC;
 #pragma unroll
       for (int k = 0; k < CPL; ++k) kr[i][k] = load16(kp + k * LPR * EPC);
     }
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-      const int pos = base + rg + i * RPI;
-      const int slot = slot_of(vr, ring, pos < p1 ? pos : base, a.T_cap);
+      const int vi = base + rg + i * RPI;
+      const int slot = row_slot(vr, ring, fast, vi < p1 ? vi : base, a.T_cap);
       const T* vp = Vbg + (size_t)slot * D + cl * EPC;
 #pragma unroll
       for (int k = 0; k < CPL; ++k) vv[i][k] = load16(vp + k * LPR * EPC);

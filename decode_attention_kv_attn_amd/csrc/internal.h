@@ -21,6 +21,8 @@ struct GqaArgs {
   float* lse_part;   // [B, H_q, S]    when S > 1
   const int32_t* seq_lens;   // nullable
   const int32_t* ring_head;  // nullable: linear addressing
+  const int32_t* gpos;       // global positions (linear cache only), nullable
+  int n_global;
   int B, H_q, H_kv, T_cap, window;
   int n;            // query heads per KV head
   int head_chunks;  // work items per KV head along the query heads

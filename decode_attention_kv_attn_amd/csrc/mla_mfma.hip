@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
 
   const VisibleRange vr = visible_range(a.seq_lens, nullptr, b, a.T_cap, 0);
   int p0, p1;
-  split_range(vr, s, a.chunk, p0, p1);
+  split_range(vr, s, a.S, a.chunk, p0, p1);  // no window: rows = positions
   const int hw0 = hc * kHG + wave * kHW;  // first head of this wave
   const int span = p1 - p0;
   const int ntiles = span > 0 ? (span + kTT - 1) / kTT : 0;

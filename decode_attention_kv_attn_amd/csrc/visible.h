@@ -1,16 +1,22 @@
-// Visible range and slot addressing of a decode query (the tile skipper).
+// Visible set and row addressing of a decode query (the tile skipper).
 //
-// The query of sequence b sits at logical position t = T_b - 1.  It sees a
-// contiguous position range [lo, hi):
-//   hi = T_b;
-//   lo = T_b - w          when a window of width w > 0 is set (positions
-//                          t-w+1 .. t; xuesongtap "attention-head" note,
-//                          section 3, worked example w=3: row 8 sees 6, 7, 8);
-//   lo = T_b - S_cap      at least, in ring mode, where only the newest S_cap
-//                          positions are resident (same section: a pure
-//                          sliding-window layer may reuse slots as a ring);
-//   lo = 0                otherwise.
-// A work item owns a sub-range of [lo, hi) and loads only rows inside it, so
+// The query of sequence b sits at logical position t = T_b - 1 and sees
+//   * the contiguous range [lo, T_b), where
+//       lo = T_b - w          with a window of width w > 0 (positions
+//                              t-w+1 .. t; xuesongtap "attention-head" note,
+//                              section 3, worked example w=3: row 8 sees
+//                              6, 7, 8),
+//       lo >= T_b - S_cap     in ring mode, where only the newest S_cap
+//                              positions are resident (same section: a pure
+//                              sliding-window layer may reuse slots as a ring),
+//       lo = 0                otherwise;
+//   * plus, in a linear cache with global positions G (sorted, unique), every
+//     g in G with g < lo; a query that is itself in G sees all of [0, T_b)
+//     (same section, the window-plus-global pattern with G = {0, 5}).
+//
+// Kernels walk a dense virtual index vi in [0, n): vi < n_extra are the
+// global positions before the window (G[vi]), the rest is lo + (vi - n_extra).
+// A work item owns a sub-range of [0, n) and loads only rows inside it, so
 // masked rows -- beyond a ragged end, outside the window, overwritten in the
 // ring -- are never read.
 //
@@ -23,16 +29,30 @@
 
 namespace attn {
 
+// Entries of the ascending list g[0..n) that are below x (binary search).
+ATTN_DEV int count_below(const int32_t* g, int n, int x) {
+  int a = 0, b = n;
+  while (a < b) {
+    const int mid = (a + b) >> 1;
+    if (g[mid] < x) a = mid + 1; else b = mid;
+  }
+  return a;
+}
+
 struct VisibleRange {
-  int lo;    // first visible position
-  int hi;    // one past the last visible position (== T_b)
-  int t;     // query position
-  int head;  // ring: slot of position t; linear: unused
+  int lo;       // first windowed position
+  int hi;       // one past the last visible position (== T_b)
+  int t;        // query position
+  int head;     // ring: slot of position t; linear: unused
+  int n_extra;  // global positions before lo (virtual rows 0 .. n_extra-1)
+  int n;        // visible rows
+  const int32_t* gpos;  // global positions (valid when n_extra > 0)
 };
 
 ATTN_DEV VisibleRange visible_range(const int32_t* seq_lens,
                                     const int32_t* ring_head, int b, int T_cap,
-                                    int window) {
+                                    int window, const int32_t* gpos = nullptr,
+                                    int n_global = 0) {
   int T_b = seq_lens ? seq_lens[b] : T_cap;
   const bool ring = ring_head != nullptr;
   if (T_b < 0) T_b = 0;
@@ -40,11 +60,24 @@ ATTN_DEV VisibleRange visible_range(const int32_t* seq_lens,
   int lo = 0;
   if (window > 0) lo = max(lo, T_b - window);
   if (ring) lo = max(lo, T_b - T_cap);
+  int n_extra = 0;
+  if (n_global > 0 && T_b > 0 && lo > 0) {
+    // G is sorted: n_extra = #{g < lo}; the query is global iff t is in G.
+    n_extra = count_below(gpos, n_global, lo);
+    const int k = count_below(gpos, n_global, T_b - 1);
+    if (k < n_global && gpos[k] == T_b - 1) {
+      lo = 0;
+      n_extra = 0;
+    }
+  }
   VisibleRange r;
   r.lo = lo;
   r.hi = T_b;
   r.t = T_b - 1;
   r.head = 0;
+  r.n_extra = n_extra;
+  r.n = n_extra + (T_b - lo);
+  r.gpos = gpos;
   if (ring) {
     int h = ring_head[b] % T_cap;
     r.head = h < 0 ? h + T_cap : h;
@@ -52,22 +85,41 @@ ATTN_DEV VisibleRange visible_range(const int32_t* seq_lens,
   return r;
 }
 
-// Cache row of visible position `pos` (lo <= pos < hi).  `ring` is uniform
-// across the work item.
+// Logical position of virtual row vi (0 <= vi < n).  Global positions are
+// clamped into the cache so a malformed list cannot address outside it.
+ATTN_DEV int row_position(const VisibleRange& r, int vi, int T_cap) {
+  if (vi < r.n_extra) {
+    const int g = r.gpos[vi];
+    return g < 0 ? 0 : (g >= T_cap ? T_cap - 1 : g);
+  }
+  return r.lo + (vi - r.n_extra);
+}
+
+// Cache row of a visible position.  `ring` is uniform across the work item.
 ATTN_DEV int slot_of(const VisibleRange& r, bool ring, int pos, int T_cap) {
   if (!ring) return pos;
   const int s = r.head - (r.t - pos);
   return s < 0 ? s + T_cap : s;
 }
 
-// Sub-range of split `s` when the visible range is cut into pieces of
-// `chunk` positions starting at lo.  Empty when s*chunk >= hi-lo.
-ATTN_DEV void split_range(const VisibleRange& r, int s, int chunk, int& p0,
-                          int& p1) {
-  const long long a = (long long)r.lo + (long long)s * chunk;
-  p0 = a < r.hi ? (int)a : r.hi;
-  const long long e = a + chunk;
-  p1 = e < r.hi ? (int)e : r.hi;
+// Cache row of virtual row vi.  When the whole tile [base, base + rows) lies
+// past the global rows (the common case; `tile_fast`, uniform), the position
+// is a plain offset.
+ATTN_DEV int row_slot(const VisibleRange& r, bool ring, bool tile_fast, int vi,
+                      int T_cap) {
+  const int pos = tile_fast ? r.lo + (vi - r.n_extra) : row_position(r, vi, T_cap);
+  return slot_of(r, ring, pos, T_cap);
+}
+
+// Virtual sub-range of split s when [0, n) is cut into pieces of `chunk`
+// rows.  The last split also takes any rows past S*chunk (a query that is
+// itself global sees more rows than the planner's bound).
+ATTN_DEV void split_range(const VisibleRange& r, int s, int S, int chunk,
+                          int& p0, int& p1) {
+  const long long a = (long long)s * chunk;
+  p0 = a < r.n ? (int)a : r.n;
+  const long long e = (s == S - 1) ? (long long)r.n : a + chunk;
+  p1 = e < r.n ? (int)e : r.n;
 }
 
 }  // namespace attn

@@ -126,6 +126,47 @@ size_t attn_decode_gqa_workspace_bytes(int B, int H_q, int H_kv, int T_cap,
                                        int d, int dtype, int window, int ring,
                                        int num_splits);
 
+/* Largest accepted n_global. */
+#define ATTN_MAX_GLOBAL 65536
+
+/*
+ * attn_decode_gqa_global -- attn_decode_gqa over a linear cache with a
+ * sliding window plus global positions (attention-head section 3, the
+ * window-plus-global pattern, example G = {0, 5}).
+ *
+ *   global_pos [n_global] int32 device array: the global positions G,
+ *             sorted ascending, no repeats, each in [0, T_cap).  Shared by
+ *             the whole batch.
+ *   n_global  0..ATTN_MAX_GLOBAL; 0 (global_pos may then be NULL) gives
+ *             exactly attn_decode_gqa without ring.
+ *   The query at t = T_b - 1 sees its window t-w+1 .. t plus every g in G
+ *   with g < t-w+1; a query that is itself in G (t in G) sees all of 0..t.
+ *   window == 0 means no window (G then changes nothing).
+ *   Every other argument, and the split / workspace rules, as for
+ *   attn_decode_gqa with ring_head == NULL; size the workspace with
+ *   attn_decode_gqa_global_workspace_bytes.
+ *   Values of global_pos are not checked on the host.  An unsorted list or
+ *   one with repeats gives an unspecified result; entries outside
+ *   [0, T_cap) are clamped to a cache row, so no access leaves the cache.
+ */
+int attn_decode_gqa_global(const void* q, const void* k, const void* v,
+                           float* out, float* lse_out, const int32_t* seq_lens,
+                           const int32_t* global_pos, int n_global, int B,
+                           int H_q, int H_kv, int T_cap, int d, int dtype,
+                           int window, float scale, int num_splits,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Split count and workspace bytes of attn_decode_gqa_global, with the same
+ * return conventions as attn_decode_gqa_splits / _workspace_bytes. */
+int attn_decode_gqa_global_splits(int B, int H_q, int H_kv, int T_cap, int d,
+                                  int dtype, int window, int n_global,
+                                  int num_splits);
+size_t attn_decode_gqa_global_workspace_bytes(int B, int H_q, int H_kv,
+                                              int T_cap, int d, int dtype,
+                                              int window, int n_global,
+                                              int num_splits);
+
 /*
  * attn_decode_mla -- one decode step of absorbed multi-head latent attention.
  *
@@ -180,6 +221,36 @@ size_t attn_decode_mla_workspace_bytes(int B, int H, int T_cap, int d_c,
  */
 int attn_combine(const float* o_part, const float* lse_part, float* out,
                  float* lse_out, int B, int H, int S, int d_v, void* stream);
+
+/*
+ * attn_kv_append -- write the current token's rows into a linear cache (the
+ * step before a decode call: the pages' modules concatenate the new key and
+ * value onto the cached ones along the sequence axis -- toolsku MHA / GQA /
+ * MLA modules).  For every sequence b and head g:
+ *     k_cache[b, g, positions[b], :] = k_new[b, g, :]   (and v likewise)
+ *   k_cache, v_cache [B, H, T_cap, d]; k_new, v_new [B, H, d]; dtype as for
+ *   attn_decode_gqa.  v_cache and v_new may both be NULL (one tensor only,
+ *   e.g. an MLA latent cache [B, T_cap, d_c + d_rope] with H = 1).
+ *   positions [B] int32: usually the length before the append (T_b - 1
+ *   after it).  Positions outside [0, T_cap) are skipped.
+ *   Rows must be a multiple of 16 bytes; pointers 16-byte aligned.
+ */
+int attn_kv_append(void* k_cache, void* v_cache, const void* k_new,
+                   const void* v_new, const int32_t* positions, int B, int H,
+                   int T_cap, int d, int dtype, void* stream);
+
+/*
+ * attn_kv_append_ring -- the ring-buffer form (attention-head section 3:
+ * slots of positions that left the window are reused).  For every b the row
+ * goes to slot (ring_head[b] + 1) mod T_cap, which then becomes the newest
+ * slot: ring_head[b] is updated in place (device memory), ready for
+ * attn_decode_gqa's ring mode.  An empty ring starts with ring_head =
+ * T_cap - 1 so the first row lands in slot 0.  Other arguments as
+ * attn_kv_append.
+ */
+int attn_kv_append_ring(void* k_cache, void* v_cache, const void* k_new,
+                        const void* v_new, int32_t* ring_head, int B, int H,
+                        int T_cap, int d, int dtype, void* stream);
 
 /* Bytes of the split buffers for S splits: o_part [B,H,S,d_v] and lse_part
  * [B,H,S], float32, each 256-byte aligned inside the workspace (0 if S<=1). */

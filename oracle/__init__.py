@@ -37,4 +37,6 @@ from .attention import (  # noqa: F401
     mla_explicit_ref,
     combine_ref,
     partial_ref,
+    kv_append_ref,
+    kv_append_ring_ref,
 )

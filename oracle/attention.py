@@ -49,6 +49,8 @@ __all__ = [
     "mla_explicit_ref",
     "combine_ref",
     "partial_ref",
+    "kv_append_ref",
+    "kv_append_ring_ref",
 ]
 
 
@@ -106,12 +108,18 @@ def _window_low(t, window):
     return 0
 
 
-def visible_positions(T_b, window=0, ring_capacity=None):
+def visible_positions(T_b, window=0, ring_capacity=None, global_pos=None):
     """Logical positions visible to the decode query of a length-``T_b`` sequence.
 
     With ``ring_capacity`` set, only the last ``ring_capacity`` positions are
     still resident in the ring buffer [attention-head section 3, ring-buffer
     reuse of out-of-window slots].
+
+    ``global_pos`` (linear cache only) lists global token positions: every
+    query also sees the global positions at or before it, and a query that is
+    itself global sees its whole history [attention-head section 3, the
+    window-plus-global pattern with G = {0, 5}: row 8 reaches 0 and 5 as well
+    as 6, 7, 8; row 5 reaches 0..5].
     """
     if T_b <= 0:
         return np.zeros(0, dtype=np.int64)
@@ -119,6 +127,13 @@ def visible_positions(T_b, window=0, ring_capacity=None):
     lo = _window_low(t, window)
     if ring_capacity is not None:
         lo = max(lo, T_b - ring_capacity)
+    if global_pos is not None and len(global_pos):
+        g = {int(x) for x in np.asarray(global_pos).reshape(-1)}
+        if t in g:
+            return np.arange(0, t + 1, dtype=np.int64)
+        extra = sorted(x for x in g if 0 <= x < lo)
+        return np.concatenate([np.array(extra, dtype=np.int64),
+                               np.arange(lo, t + 1, dtype=np.int64)])
     return np.arange(lo, t + 1, dtype=np.int64)
 
 
@@ -172,14 +187,16 @@ def _as_int(x, B, default):
 
 
 def gqa_decode_ref(q, k, v, seq_lens=None, ring_head=None, window=0,
-                   scale=None, batches=None, kv_heads=None):
+                   scale=None, batches=None, kv_heads=None, global_pos=None):
     """One decode step of MHA / GQA / MQA attention.
 
     q [B, H_q, d], k [B, H_kv, T_cap, d], v [B, H_kv, T_cap, d_v].
     ``seq_lens[b]`` is the logical length T_b (default T_cap); ``ring_head``
     switches the cache to ring-buffer addressing with T_cap slots;
     ``window`` is the sliding-window width (0 = full causal, and in ring mode
-    0 = the whole resident set).  Returns ``(out [B, H_q, d_v], lse [B, H_q])``
+    0 = the whole resident set); ``global_pos`` adds global positions to a
+    linear cache's window (see ``visible_positions``).
+    Returns ``(out [B, H_q, d_v], lse [B, H_q])``
     in float64.  ``batches`` / ``kv_heads`` restrict the work to a subset
     (other entries stay 0 / -inf), for sampled checks on large inputs.
 
@@ -199,6 +216,13 @@ def gqa_decode_ref(q, k, v, seq_lens=None, ring_head=None, window=0,
         raise ValueError("window must be >= 0")
     if ring_head is not None and window > T_cap:
         raise ValueError("window larger than the ring")
+    if ring_head is not None and global_pos is not None:
+        raise ValueError("global positions need a linear cache")
+    gp = None
+    if global_pos is not None:
+        if hasattr(global_pos, "detach"):
+            global_pos = global_pos.detach().cpu().numpy()
+        gp = [int(x) for x in np.asarray(global_pos).reshape(-1)]
     n = H_q // H_kv
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -213,7 +237,7 @@ def gqa_decode_ref(q, k, v, seq_lens=None, ring_head=None, window=0,
         if heads is None:
             if T_b > T_cap:
                 raise ValueError("seq_len exceeds the cache capacity")
-            pos = visible_positions(T_b, window)
+            pos = visible_positions(T_b, window, global_pos=gp)
             slots = pos
         else:
             pos = visible_positions(T_b, window, ring_capacity=T_cap)
@@ -329,3 +353,45 @@ def combine_ref(o_part, lse_part):
     out = np.where(empty, 0.0, out)
     lse = np.where(empty[..., 0], -np.inf, (Ls + np.log(safe))[..., 0])
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# Cache append (the step before a decode call)
+# --------------------------------------------------------------------------
+def kv_append_ref(cache, new_rows, positions):
+    """Linear cache: write each sequence's new row at its position.
+
+    cache [B, H, T_cap, d] (or [B, T_cap, d] for a latent cache), new_rows
+    [B, H, d] (or [B, d]), positions [B].  Returns a new array.  Appending
+    the current token's key and value to the cached ones along the sequence
+    axis is what the toolsku MHA / GQA / MLA modules do with ``past_kv``
+    (``torch.cat`` on dim 2); here the cache is preallocated, so the append
+    is a write at index T_b.  Positions outside [0, T_cap) are not written.
+    """
+    out = np.array(_as_f64(cache), copy=True)
+    new_rows = _as_f64(new_rows)
+    B = out.shape[0]
+    T_cap = out.shape[-2]
+    pos = _as_int(positions, B, 0)
+    for b in range(B):
+        if 0 <= pos[b] < T_cap:
+            out[b, ..., pos[b], :] = new_rows[b]
+    return out
+
+
+def kv_append_ring_ref(cache, new_rows, ring_head):
+    """Ring cache: advance each sequence's head one slot (mod T_cap) and write
+    the new row there, overwriting the oldest position once the ring is full
+    [attention-head section 3: a sliding-window layer may reuse the slots of
+    positions that left the window].  Returns (new cache, new heads)."""
+    out = np.array(_as_f64(cache), copy=True)
+    new_rows = _as_f64(new_rows)
+    B = out.shape[0]
+    T_cap = out.shape[-2]
+    heads = _as_int(ring_head, B, 0)
+    new_heads = []
+    for b in range(B):
+        h = (heads[b] % T_cap + 1) % T_cap
+        out[b, ..., h, :] = new_rows[b]
+        new_heads.append(h)
+    return out, np.array(new_heads, dtype=np.int64)

@@ -28,12 +28,14 @@ def _slot_position(slot, t, ring_head, capacity):
     return t - age
 
 
-def visible_slots_brute(T_b, T_cap, window=0, ring_head=None):
+def visible_slots_brute(T_b, T_cap, window=0, ring_head=None, global_pos=None):
     """List of (slot, position) pairs the decode query reads, by testing each
-    slot of the cache one at a time."""
+    slot of the cache one at a time.  ``global_pos``: positions every query
+    may also see; a global query sees everything before it (linear cache)."""
     if T_b <= 0:
         return []
     t = T_b - 1
+    gset = set() if global_pos is None else {int(x) for x in global_pos}
     out = []
     for slot in range(T_cap):
         if ring_head is None:
@@ -45,7 +47,8 @@ def visible_slots_brute(T_b, T_cap, window=0, ring_head=None):
             if pos < 0:          # the ring has not wrapped this far yet
                 continue
         if window > 0 and t - pos >= window:   # older than the window
-            continue
+            if pos not in gset and t not in gset:
+                continue
         out.append((slot, pos))
     out.sort(key=lambda sp: sp[1])
     return out
@@ -62,7 +65,7 @@ def _softmax_weighted(scores, values):
 
 
 def gqa_decode_brute(q, k, v, seq_lens=None, ring_head=None, window=0,
-                     scale=None):
+                     scale=None, global_pos=None):
     """Scalar-loop decode attention; same contract as
     ``oracle.attention.gqa_decode_ref``, returns nested lists."""
     q, k, v = _lst(q), _lst(k), _lst(v)
@@ -75,7 +78,7 @@ def gqa_decode_brute(q, k, v, seq_lens=None, ring_head=None, window=0,
     out, lse = [], []
     for b in range(B):
         sl = visible_slots_brute(lens[b], T_cap, window,
-                                 None if heads is None else heads[b])
+                                 None if heads is None else heads[b], global_pos)
         ob, lb = [], []
         for h in range(H_q):
             g = h * H_kv // H_q

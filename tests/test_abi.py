@@ -123,3 +123,44 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "library_path", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         L.library()
+
+
+def test_append_host_errors(lib):
+    ap = lib.attn_kv_append
+    assert ap(None, None, P16, None, P16, 1, 2, 8, 64, 1, None) == -1
+    assert ap(P16, P16, P16, None, P16, 1, 2, 8, 64, 1, None) == -1   # v pair mismatch
+    assert ap(P16, None, P16, None, P16, 1, 0, 8, 64, 1, None) == -2
+    assert ap(P16, None, P16, None, P16, 1, 2, 8, 64, 5, None) == -3
+    assert ap(P16, None, P16, None, P16, 1, 2, 8, 3, 1, None) == -7    # 6-byte rows
+    assert ap(ctypes.c_void_p(4100), None, P16, None, P16, 1, 2, 8, 64, 1, None) == -7
+    assert ap(None, None, None, None, None, 0, 2, 8, 64, 1, None) == 0
+    ar = lib.attn_kv_append_ring
+    assert ar(P16, None, P16, None, None, 1, 2, 8, 64, 1, None) == -1
+    assert ar(P16, None, P16, None, P16, 1, 2, 0, 64, 1, None) == -2
+
+
+def test_global_host_errors(lib):
+    def gg(gp=P16, n=2, q=P16, window=64, B=1, T=512, S=0, ws=None, wsb=0):
+        return lib.attn_decode_gqa_global(q, P16, P16, P16, None, None, gp, n, B,
+                                          8, 2, T, 64, 1, window, 0.0, S, ws,
+                                          wsb, None)
+    assert gg(gp=None) == -1                 # n_global > 0 needs the list
+    assert gg(n=-1) == -9
+    assert gg(n=65537) == -9
+    assert gg(gp=ctypes.c_void_p(4098)) == -7
+    assert gg(q=None) == -1
+    assert gg(window=-1) == -5
+    assert gg(B=0, gp=None, q=None) == 0
+    # the planner's bound grows with the global count, and splits never exceed it
+    for window, n in [(64, 0), (64, 2), (4096, 100), (0, 5)]:
+        S = lib.attn_decode_gqa_global_splits(16, 32, 8, 32768, 128, 1, window, n, 0)
+        mv = min(window + n, 32768) if window else 32768
+        assert 1 <= S <= 1024
+        chunk = -(-mv // S)
+        assert (S - 1) * chunk < mv
+        ws = lib.attn_decode_gqa_global_workspace_bytes(16, 32, 8, 32768, 128, 1,
+                                                        window, n, 0)
+        assert ws == (0 if S == 1 else lib.attn_decode_workspace_bytes(16, 32, 128, S))
+    # without global positions the plan is attn_decode_gqa's
+    assert (lib.attn_decode_gqa_global_splits(8, 32, 8, 4096, 128, 1, 512, 0, 0)
+            == lib.attn_decode_gqa_splits(8, 32, 8, 4096, 128, 1, 512, 0, 0))

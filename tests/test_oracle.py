@@ -562,3 +562,110 @@ def test_planted_mla_value_columns_are_caught(monkeypatch):
     monkeypatch.setattr(A, "mla_decode_ref", wrong)
     monkeypatch.setattr(oracle, "mla_decode_ref", wrong)
     assert _caught()
+
+
+# ------------------------------------------------------------- cache append
+def check_append_then_decode_equals_concat(seed=14):
+    """Appending the new token's K/V and decoding equals decoding over the
+    past cache concatenated with the new row (toolsku modules: torch.cat of
+    past_kv and the new k, v along the sequence axis)."""
+    rng = _rng(seed)
+    B, H_q, H_kv, T_cap, d = 2, 4, 2, 12, 4
+    past = np.array([5, 9])
+    k = rng.standard_normal((B, H_kv, T_cap, d))
+    v = rng.standard_normal((B, H_kv, T_cap, d))
+    kn = rng.standard_normal((B, H_kv, d))
+    vn = rng.standard_normal((B, H_kv, d))
+    q = rng.standard_normal((B, H_q, d))
+    k2 = oracle.kv_append_ref(k, kn, past)
+    v2 = oracle.kv_append_ref(v, vn, past)
+    o, l = oracle.gqa_decode_ref(q, k2, v2, past + 1)
+    for b in range(B):
+        kc = np.concatenate([k[b, :, :past[b]], kn[b][:, None]], axis=1)[None]
+        vc = np.concatenate([v[b, :, :past[b]], vn[b][:, None]], axis=1)[None]
+        ob, lb = oracle.gqa_decode_ref(q[b:b + 1], kc, vc)
+        assert np.allclose(o[b], ob[0], atol=1e-13) and np.allclose(l[b], lb[0], atol=1e-13)
+    # out-of-range positions are not written
+    assert np.array_equal(oracle.kv_append_ref(k, kn, np.array([T_cap, -1])), k)
+
+
+def test_append_then_decode_equals_concat():
+    check_append_then_decode_equals_concat()
+
+
+def check_ring_append_sequence(seed=15):
+    """A long run of ring appends + windowed decode equals decoding the full
+    linear history with the same window, at every step."""
+    rng = _rng(seed)
+    cap, d, steps, w = 5, 3, 13, 4
+    hist_k = rng.standard_normal((steps, d))
+    hist_v = rng.standard_normal((steps, d))
+    q = rng.standard_normal((1, 2, d))
+    ring_k = np.zeros((1, 1, cap, d))
+    ring_v = np.zeros((1, 1, cap, d))
+    head = np.array([cap - 1])        # empty ring: the first append lands in slot 0
+    for t in range(steps):
+        ring_k, _ = oracle.kv_append_ring_ref(ring_k, hist_k[t][None, None], head)
+        ring_v, head = oracle.kv_append_ring_ref(ring_v, hist_v[t][None, None], head)
+        o, l = oracle.gqa_decode_ref(q, ring_k, ring_v, np.array([t + 1]), head, w)
+        lin_k = hist_k[None, None, :t + 1]
+        lin_v = hist_v[None, None, :t + 1]
+        o2, l2 = oracle.gqa_decode_ref(q, lin_k, lin_v, np.array([t + 1]), window=w)
+        assert np.allclose(o, o2, atol=1e-13) and np.allclose(l, l2, atol=1e-13), t
+
+
+def test_ring_append_sequence():
+    check_ring_append_sequence()
+
+
+ALL_CHECKS += [check_append_then_decode_equals_concat, check_ring_append_sequence]
+
+
+def test_planted_append_off_by_one_is_caught(monkeypatch):
+    orig = oracle.kv_append_ref
+
+    def shifted(cache, new_rows, positions):
+        return orig(cache, new_rows, np.asarray(positions) + 1)
+
+    monkeypatch.setattr(oracle, "kv_append_ref", shifted)
+    assert _caught()
+
+
+# ------------------------------------------------------------ global tokens
+def check_global_golden():
+    g = json.load(open(os.path.join(GOLD, "window_example.json")))
+    for e in g["global_cases"]:
+        got = oracle.visible_positions(e["T_b"], e["window"],
+                                       global_pos=e["globals"]).tolist()
+        assert got == e["visible"], (e["cite"], got)
+        bf = [p for _, p in BF.visible_slots_brute(e["T_b"], e["T_b"] + 3, e["window"],
+                                                    global_pos=e["globals"])]
+        assert bf == e["visible"], (e["cite"], bf)
+
+
+def test_global_golden():
+    check_global_golden()
+
+
+def check_global_brute_force(seed=16):
+    rng = _rng(seed)
+    for c in range(30):
+        T_cap = int(rng.integers(1, 30))
+        G = sorted(set(rng.integers(0, T_cap + 3, size=int(rng.integers(0, 6))).tolist()))
+        window = int(rng.choice([1, 2, 3, 5]))
+        q, k, v, lens, _ = _tiny_case(rng, 2, 4, 2, T_cap, 4)
+        o, l = oracle.gqa_decode_ref(q, k, v, lens, window=window, scale=0.7,
+                                     global_pos=G)
+        ob, lb = BF.gqa_decode_brute(q, k, v, lens, window=window, scale=0.7,
+                                     global_pos=G)
+        assert np.allclose(o, np.array(ob), atol=1e-12), c
+        lb = np.array(lb)
+        fin = np.isfinite(l)
+        assert np.array_equal(fin, np.isfinite(lb)) and np.allclose(l[fin], lb[fin], atol=1e-12)
+
+
+def test_global_brute_force():
+    check_global_brute_force()
+
+
+ALL_CHECKS += [check_global_golden, check_global_brute_force]
