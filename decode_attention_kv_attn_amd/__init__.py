@@ -22,6 +22,7 @@ __all__ = [
     "attn_kv_append", "attn_kv_append_ring",
     "attn_decode_gqa_global", "attn_decode_gqa_global_splits",
     "attn_decode_gqa_global_workspace_bytes",
+    "attn_decode_gqa_paged", "attn_decode_mla_paged", "attn_kv_append_paged",
 ]
 
 ATTN_F32 = 0
@@ -40,6 +41,12 @@ _SIGS = {
                                     _vp]),
     "attn_decode_gqa_global_splits": (_i, [_i] * 9),
     "attn_decode_gqa_global_workspace_bytes": (_sz, [_i] * 9),
+    "attn_decode_gqa_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                                   _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "attn_decode_mla_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                                   _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "attn_kv_append_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                                  _i, _i, _i, _vp]),
     "attn_decode_gqa_splits": (_i, [_i] * 9),
     "attn_decode_gqa_workspace_bytes": (_sz, [_i] * 9),
     "attn_decode_mla": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
@@ -300,6 +307,84 @@ def attn_kv_append_ring(k_cache, k_new, ring_head, v_cache=None, v_new=None,
                                        _dtype_code(k_cache),
                                        _stream(stream, k_cache.device))
     _check("attn_kv_append_ring", st)
+
+
+def attn_decode_gqa_paged(q, k_pages, v_pages, block_table, seq_lens=None,
+                          window=0, scale=None, num_splits=0, out=None, lse=None,
+                          workspace=None, want_lse=True, stream=None):
+    """Decode over a paged K/V pool: k_pages / v_pages [num_pages, H_kv, P,
+    d], block_table int32 [B, max_pages].  Returns ``(out, lse)`` as
+    :func:`attn_decode_gqa`."""
+    _need_dev(q, k_pages, v_pages, block_table, seq_lens, out, lse)
+    B, H_q, d = q.shape
+    num_pages, H_kv, P, _ = k_pages.shape
+    max_pages = block_table.shape[1]
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    nbytes = attn_decode_gqa_workspace_bytes(B, H_q, H_kv, max_pages * P, d, dt,
+                                             window, False, num_splits)
+    if nbytes == 2**64 - 1:
+        nbytes = 0
+    workspace = _workspace(nbytes, q.device, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = library().attn_decode_gqa_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(out), _ptr(lse),
+        _ptr(seq_lens), _ptr(block_table), max_pages, B, H_q, H_kv, num_pages, P,
+        d, dt, window, 0.0 if scale is None else float(scale), num_splits,
+        _ptr(workspace), ws_bytes, _stream(stream, q.device))
+    _check("attn_decode_gqa_paged", st)
+    return out, lse
+
+
+def attn_decode_mla_paged(q, latent_pages, block_table, d_c, scale,
+                          seq_lens=None, num_splits=0, out=None, lse=None,
+                          workspace=None, want_lse=True, stream=None):
+    """Absorbed MLA over a paged latent pool [num_pages, P, d_c+d_rope]
+    (bfloat16) with block_table int32 [B, max_pages]."""
+    _need_dev(q, latent_pages, block_table, seq_lens, out, lse)
+    B, H, dk = q.shape
+    num_pages, P, _ = latent_pages.shape
+    max_pages = block_table.shape[1]
+    d_rope = dk - d_c
+    if out is None:
+        out = torch.empty((B, H, d_c), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    nbytes = attn_decode_mla_workspace_bytes(B, H, max_pages * P, d_c, d_rope,
+                                             num_splits)
+    if nbytes == 2**64 - 1:
+        nbytes = 0
+    workspace = _workspace(nbytes, q.device, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = library().attn_decode_mla_paged(
+        _ptr(q), _ptr(latent_pages), _ptr(out), _ptr(lse), _ptr(seq_lens),
+        _ptr(block_table), max_pages, B, H, num_pages, P, d_c, d_rope,
+        float(scale), num_splits, _ptr(workspace), ws_bytes,
+        _stream(stream, q.device))
+    _check("attn_decode_mla_paged", st)
+    return out, lse
+
+
+def attn_kv_append_paged(k_pages, k_new, positions, block_table, v_pages=None,
+                         v_new=None, stream=None):
+    """Write k_new (and v_new) [B, H, d] at position positions[b] of each
+    sequence's pages ([num_pages, H, P, d]; a latent pool [num_pages, P, d]
+    with [B, d] rows is taken as H = 1)."""
+    _need_dev(k_pages, k_new, positions, block_table, v_pages, v_new)
+    if k_pages.dim() == 3:
+        num_pages, P, d = k_pages.shape
+        H = 1
+    else:
+        num_pages, H, P, d = k_pages.shape
+    B = positions.shape[0]
+    st = library().attn_kv_append_paged(
+        _ptr(k_pages), _ptr(v_pages), _ptr(k_new), _ptr(v_new), _ptr(positions),
+        _ptr(block_table), block_table.shape[1], B, H, num_pages, P, d,
+        _dtype_code(k_pages), _stream(stream, k_pages.device))
+    _check("attn_kv_append_paged", st)
 
 
 def attn_probe_read(src, sink, blocks=0, stream=None):

@@ -60,6 +60,29 @@ int check_gqa_shape(int B, int H_q, int H_kv, int T_cap, int d, int dtype,
   return ATTN_OK;
 }
 
+}  // namespace
+}  // namespace attn
+
+// Page geometry shared by the paged entry points: page_size a power of two
+// in [16, 2^16], at least one page, every logical length and every row of
+// the pool addressable with 32-bit indices.
+int attn_check_pages(int max_pages, int num_pages, int page_size, int rows_per_pos,
+                     int* shift) {
+  if (max_pages <= 0 || num_pages <= 0 || rows_per_pos <= 0) return ATTN_ERR_SHAPE;
+  if (page_size < 16 || page_size > (1 << 16) || (page_size & (page_size - 1)))
+    return ATTN_ERR_UNSUPPORTED;
+  if ((long long)max_pages * page_size > (1LL << 30)) return ATTN_ERR_SHAPE;
+  if ((long long)num_pages * rows_per_pos * page_size > 0x7fffffffLL)
+    return ATTN_ERR_SHAPE;
+  int s = 0;
+  while ((1 << s) < page_size) ++s;
+  *shift = s;
+  return ATTN_OK;
+}
+
+namespace attn {
+namespace {
+
 int plan_gqa(int B, int H_q, int H_kv, int T_cap, int d, int dtype, int window,
              int ring, int n_global, int num_splits, GqaPlan* p) {
   int st = check_gqa_shape(B, H_q, H_kv, T_cap, d, dtype, window, ring);
@@ -157,11 +180,18 @@ size_t attn_decode_gqa_global_workspace_bytes(int B, int H_q, int H_kv,
 namespace attn {
 namespace {
 
-// Shared body of the two GQA entry points.
+// Paged caches: (block_table, max_pages, page_shift, num_pages), with
+// T_cap = max_pages << page_shift; block_table == nullptr otherwise.
+struct PagedArgs {
+  const int32_t* block_table;
+  int max_pages, page_shift, num_pages;
+};
+
+// Shared body of the GQA entry points.
 int decode_gqa(const void* q, const void* k, const void* v, float* out,
                float* lse_out, const int32_t* seq_lens, const int32_t* ring_head,
-               const int32_t* gpos, int n_global, int B, int H_q, int H_kv,
-               int T_cap, int d, int dtype, int window, float scale,
+               const int32_t* gpos, int n_global, PagedArgs pg, int B, int H_q,
+               int H_kv, int T_cap, int d, int dtype, int window, float scale,
                int num_splits, void* workspace, size_t workspace_bytes,
                void* stream) {
   const int ring = ring_head != nullptr;
@@ -194,6 +224,10 @@ int decode_gqa(const void* q, const void* k, const void* v, float* out,
   a.ring_head = ring_head;
   a.gpos = n_global > 0 ? gpos : nullptr;
   a.n_global = n_global;
+  a.block_table = pg.block_table;
+  a.max_pages = pg.max_pages;
+  a.page_shift = pg.page_shift;
+  a.num_pages = pg.num_pages;
   a.B = B;
   a.H_q = H_q;
   a.H_kv = H_kv;
@@ -237,9 +271,9 @@ int attn_decode_gqa(const void* q, const void* k, const void* v, float* out,
                     int T_cap, int d, int dtype, int window, float scale,
                     int num_splits, void* workspace, size_t workspace_bytes,
                     void* stream) {
-  return decode_gqa(q, k, v, out, lse_out, seq_lens, ring_head, nullptr, 0, B,
-                    H_q, H_kv, T_cap, d, dtype, window, scale, num_splits,
-                    workspace, workspace_bytes, stream);
+  return decode_gqa(q, k, v, out, lse_out, seq_lens, ring_head, nullptr, 0,
+                    PagedArgs{nullptr, 0, 0, 0}, B, H_q, H_kv, T_cap, d, dtype,
+                    window, scale, num_splits, workspace, workspace_bytes, stream);
 }
 
 int attn_decode_gqa_global(const void* q, const void* k, const void* v,
@@ -250,7 +284,26 @@ int attn_decode_gqa_global(const void* q, const void* k, const void* v,
                            void* workspace, size_t workspace_bytes,
                            void* stream) {
   return decode_gqa(q, k, v, out, lse_out, seq_lens, nullptr, global_pos,
-                    n_global, B, H_q, H_kv, T_cap, d, dtype, window, scale,
+                    n_global, PagedArgs{nullptr, 0, 0, 0}, B, H_q, H_kv, T_cap, d,
+                    dtype, window, scale, num_splits, workspace, workspace_bytes,
+                    stream);
+}
+
+int attn_decode_gqa_paged(const void* q, const void* k_pages,
+                          const void* v_pages, float* out, float* lse_out,
+                          const int32_t* seq_lens, const int32_t* block_table,
+                          int max_pages, int B, int H_q, int H_kv, int num_pages,
+                          int page_size, int d, int dtype, int window,
+                          float scale, int num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int shift = 0;
+  const int st = attn_check_pages(max_pages, num_pages, page_size, H_kv, &shift);
+  if (st != ATTN_OK) return st;
+  if (B > 0 && !block_table) return ATTN_ERR_NULL;
+  if (block_table && !aligned(block_table, 4)) return ATTN_ERR_ALIGN;
+  return decode_gqa(q, k_pages, v_pages, out, lse_out, seq_lens, nullptr, nullptr,
+                    0, PagedArgs{block_table, max_pages, shift, num_pages}, B, H_q,
+                    H_kv, max_pages * page_size, d, dtype, window, scale,
                     num_splits, workspace, workspace_bytes, stream);
 }
 

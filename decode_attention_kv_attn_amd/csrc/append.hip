@@ -5,7 +5,9 @@
 // xuesongtap "attention-head" note, section 3).
 //
 // One work group per (sequence, head): each lane moves 16-byte chunks of the
-// row.  The work is a few KiB per call, so the kernel is launch-bound.
+// row.  The work is a few KiB per call, so the kernel is launch-bound.  A
+// paged pool is addressed through the block table (baidu article, section
+// 四.3: KV-cache paging).
 
 #include "../../include/attn_decode.h"
 #include "device_common.h"
@@ -38,6 +40,29 @@ __global__ __launch_bounds__(64) void append_rows(
   for (int c = threadIdx.x * 16; c < row_bytes; c += 64 * 16) {
     *(uint4*)(k_cache + dst + c) = *(const uint4*)(k_new + src + c);
     if (v_cache) *(uint4*)(v_cache + dst + c) = *(const uint4*)(v_new + src + c);
+  }
+}
+
+// Paged: position positions[b] of sequence b goes to page
+// table[b][pos >> shift], row pos & (P - 1), of every head (skipped unless
+// 0 <= pos < max_pages * P; page ids are clamped to the pool).
+__global__ __launch_bounds__(64) void append_rows_paged(
+    unsigned char* __restrict__ k_pages, unsigned char* __restrict__ v_pages,
+    const unsigned char* __restrict__ k_new, const unsigned char* __restrict__ v_new,
+    const int32_t* __restrict__ positions, const int32_t* __restrict__ table,
+    int max_pages, int shift, int num_pages, int H, int row_bytes) {
+  const int b = blockIdx.x / H;
+  const int h = blockIdx.x - b * H;
+  const int pos = positions[b];
+  if (pos < 0 || (pos >> shift) >= max_pages) return;
+  int page = table[(size_t)b * max_pages + (pos >> shift)];
+  page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+  const size_t src = (size_t)blockIdx.x * row_bytes;
+  const size_t dst =
+      ((((size_t)page * H + h) << shift) + (pos & ((1 << shift) - 1))) * row_bytes;
+  for (int c = threadIdx.x * 16; c < row_bytes; c += 64 * 16) {
+    *(uint4*)(k_pages + dst + c) = *(const uint4*)(k_new + src + c);
+    if (v_pages) *(uint4*)(v_pages + dst + c) = *(const uint4*)(v_new + src + c);
   }
 }
 
@@ -104,6 +129,31 @@ int attn_kv_append_ring(void* k_cache, void* v_cache, const void* k_new,
   if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   hipLaunchKernelGGL(advance_ring, dim3((unsigned)((B + 63) / 64)), dim3(64), 0, s,
                      ring_head, B, T_cap);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_kv_append_paged(void* k_pages, void* v_pages, const void* k_new,
+                         const void* v_new, const int32_t* positions,
+                         const int32_t* block_table, int max_pages, int B, int H,
+                         int num_pages, int page_size, int d, int dtype,
+                         void* stream) {
+  int shift = 0;
+  int st = attn_check_pages(max_pages, num_pages, page_size, H, &shift);
+  if (st != ATTN_OK) return st;
+  st = check(k_pages, k_new, B, H, page_size, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (B == 0) return ATTN_OK;
+  if (!k_pages || !k_new || !positions || !block_table || (!v_pages != !v_new))
+    return ATTN_ERR_NULL;
+  if (((uintptr_t)k_pages | (uintptr_t)k_new | (uintptr_t)v_pages | (uintptr_t)v_new) % 16 ||
+      (uintptr_t)positions % 4 || (uintptr_t)block_table % 4)
+    return ATTN_ERR_ALIGN;
+  const int row_bytes = d * (dtype == ATTN_F32 ? 4 : 2);
+  hipLaunchKernelGGL(append_rows_paged, dim3((unsigned)(B * H)), dim3(64), 0,
+                     (hipStream_t)stream, (unsigned char*)k_pages,
+                     (unsigned char*)v_pages, (const unsigned char*)k_new,
+                     (const unsigned char*)v_new, positions, block_table,
+                     max_pages, shift, num_pages, H, row_bytes);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

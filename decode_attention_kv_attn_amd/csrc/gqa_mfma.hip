@@ -25,6 +25,10 @@
 // four waves take the split's 32-token tiles in turn and are merged by the
 // log-sum-exp rule through LDS.  Softmax state is per head and lives in the
 // lanes that own that head (lane % 16), so rescaling O^T is lane-local.
+//
+// The addressing mode (dense linear/ring, global positions, paged) is a
+// template parameter; on a paged cache each wave fetches the page ids of
+// its next tile with one vector load a tile ahead of the row loads.
 
 #include "device_common.h"
 #include "internal.h"
@@ -84,7 +88,7 @@ struct MfmaCfg {
   static constexpr int SMEM = MERGE_BYTES > LOOP_BYTES ? MERGE_BYTES : LOOP_BYTES;
 };
 
-template <int D, int NH>
+template <int D, int NH, int MODE>
 __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   using C = MfmaCfg<D, NH>;
   constexpr int KS = C::KS, HB = C::HB, DB = C::DB, CPR = C::CPR;
@@ -92,7 +96,8 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // uniform across the wave: tile bases and page ids stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15;   // column inside a 16-wide block
   const int lg = lane >> 4;   // 16-lane group
 
@@ -108,15 +113,25 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   const int g = bid % a.H_kv;
   const int b = bid / a.H_kv;
 
-  const VisibleRange vr = visible_range(a.seq_lens, a.ring_head, b, a.T_cap,
-                                        a.window, a.gpos, a.n_global);
-  const bool ring = a.ring_head != nullptr;
+  const VisibleRange vr =
+      MODE == kAddrGlobal
+          ? visible_range(a.seq_lens, nullptr, b, a.T_cap, a.window, a.gpos, a.n_global)
+          : visible_range(a.seq_lens, MODE == kAddrDense ? a.ring_head : nullptr, b,
+                          a.T_cap, a.window);
+  const bool ring = MODE == kAddrDense && a.ring_head != nullptr;
   int p0, p1;  // this split's virtual rows
   split_range(vr, s, a.S, a.chunk, p0, p1);
   const int h0 = g * a.n + hc * NH;
   const int nh = min(NH, a.n - hc * NH);
 
-  const size_t kv_off = (size_t)(b * a.H_kv + g) * (size_t)a.T_cap * D;
+  Pages pg{};
+  if constexpr (MODE == kAddrPaged)
+    pg = page_view(a.block_table, a.max_pages, b, vr.hi, a.page_shift, a.num_pages,
+                   a.H_kv);
+  // K/V base: the (sequence, head) slab, or the head's rows in page 0
+  const size_t kv_off = MODE == kAddrPaged
+                            ? ((size_t)g << a.page_shift) * D
+                            : (size_t)(b * a.H_kv + g) * (size_t)a.T_cap * D;
   const uint16_t* __restrict__ Kbg = (const uint16_t*)a.k + kv_off;
   const uint16_t* __restrict__ Vbg = (const uint16_t*)a.v + kv_off;
 
@@ -148,26 +163,47 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   const int span = p1 - p0;
   const int ntiles = span > 0 ? (span + kTT - 1) / kTT : 0;
 
-  auto tile_row = [&](int base, int t) {
-    const int vi = base + t;
-    return row_slot(vr, ring, base >= vr.n_extra, vi < p1 ? vi : base, a.T_cap);
+  // Cache row (from the K/V base) of row t of the tile at virtual row
+  // `base`; rows past the split re-read the tile's first row.
+  auto tile_row = [&](int base, int t, const int (&pid)[3]) -> int {
+    int vi = base + t;
+    vi = vi < p1 ? vi : base;
+    if constexpr (MODE == kAddrDense) return slot_of(vr, ring, vr.lo + vi, a.T_cap);
+    else if constexpr (MODE == kAddrGlobal)
+      return row_slot(vr, false, base >= vr.n_extra, vi, a.T_cap);
+    else return paged_row(pg, pid, vr.lo + base, vr.lo + vi);
+  };
+  // Page ids of tile `it` (paged caches only): one vector load, lane k
+  // holding id k; read with readlane when the tile's loads are issued.
+  auto fetch_pages = [&](int it) -> int {
+    if constexpr (MODE == kAddrPaged) return tile_pages_lanes(pg, vr.lo + p0 + it * kTT, lane);
+    else return 0;
+  };
+  auto page_ids = [&](int pv, int (&id)[3]) {
+    if constexpr (MODE == kAddrPaged) page_ids_from_lanes(pg, pv, id);
   };
 
   // K fragments (token 16*tb + li, elements 32*ks + 8*lg..) and this lane's
   // share of the V tile (rows RPI*i + lane/CPR, chunk lane%CPR).
-  auto load_tile = [&](int it, uint4 (&kf)[2][KS], uint4 (&vr_)[VLD]) {
+  // A tile index past the split (uniform) reads row 0 of the K/V base
+  // instead: in bounds, shared by the work group's waves, never used.
+  auto load_tile = [&](int it, int pv, uint4 (&kf)[2][KS], uint4 (&vr_)[VLD]) {
     const int base = p0 + it * kTT;
+    const bool dummy = it >= ntiles;
+    int pid[3];
+    page_ids(pv, pid);
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const uint16_t* kp = Kbg + (size_t)tile_row(base, 16 * tb + li) * D + 8 * lg;
+      const int row = dummy ? 0 : tile_row(base, 16 * tb + li, pid);
+      const uint16_t* kp = Kbg + (size_t)row * D + 8 * lg;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kf[tb][ks] = nt_load16(kp + 32 * ks);
     }
 #pragma unroll
     for (int i = 0; i < VLD; ++i) {
       const int t = RPI * i + lane / CPR;
-      const uint16_t* vp = Vbg + (size_t)tile_row(base, t) * D + 8 * (lane % CPR);
-      vr_[i] = nt_load16(vp);
+      const int row = dummy ? 0 : tile_row(base, t, pid);
+      vr_[i] = nt_load16(Vbg + (size_t)row * D + 8 * (lane % CPR));
     }
   };
 
@@ -267,20 +303,32 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
     }
   };
 
+  // two register stages; page ids run a tile ahead, loaded before the
+  // current tile's rows so that waiting for them never waits for row data
   uint4 kA[2][KS], vA[VLD], kB[2][KS], vB[VLD];
-  int it = wave;
-  if (it < ntiles) load_tile(it, kA, vA);
-  while (it < ntiles) {
-    int nx = it + kNW;
-    if (nx < ntiles) load_tile(nx, kB, vB);
-    compute_tile(it, kA, vA);
-    it = nx;
-    if (it >= ntiles) break;
-    nx = it + kNW;
-    if (nx < ntiles) load_tile(nx, kA, vA);
-    compute_tile(it, kB, vB);
-    it = nx;
+  // The loop body is one pair of tiles with both loads unconditional (a
+  // load behind a condition, or a break between the halves, makes the
+  // compiler's wait for the current tile also cover the next tile's loads);
+  // the tile after the wave's last re-reads row 0 of the K/V base instead
+  // (never used).  Page ids (pA / pB, alternating like the stages) are loaded
+  // a tile ahead of the rows.
+  const int nt = wave < ntiles ? (ntiles - wave + kNW - 1) / kNW : 0;  // this wave's tiles
+  int pA = 0, pB = 0;
+  if (nt > 0) {
+    const int pcur = fetch_pages(wave);
+    pA = fetch_pages(wave + kNW);
+    load_tile(wave, pcur, kA, vA);
   }
+  for (int j = 0; j + 1 < nt; j += 2) {
+    const int it = wave + j * kNW;
+    pB = fetch_pages(it + 2 * kNW);
+    load_tile(it + kNW, pA, kB, vB);
+    compute_tile(it, kA, vA);
+    pA = fetch_pages(it + 3 * kNW);
+    load_tile(it + 2 * kNW, pB, kA, vA);
+    compute_tile(it + kNW, kB, vB);
+  }
+  if (nt & 1) compute_tile(wave + (nt - 1) * kNW, kA, vA);
 
   // per-head partial sums of the four lane groups
 #pragma unroll
@@ -336,10 +384,23 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   }
 }
 
-template <int D, int NH>
+template <int D, int NH, int MODE>
 hipError_t launch_one(const GqaArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((gqa_decode_mfma<D, NH>), dim3(grid), dim3(kNW * 64), 0, st, a);
+  hipLaunchKernelGGL((gqa_decode_mfma<D, NH, MODE>), dim3(grid), dim3(kNW * 64), 0,
+                     st, a);
   return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(const GqaArgs& a, int d, int heads_per_item, int grid,
+                       hipStream_t st) {
+  switch (d * 1000 + heads_per_item) {
+    case 64016: return launch_one<64, 16, MODE>(a, grid, st);
+    case 64032: return launch_one<64, 32, MODE>(a, grid, st);
+    case 128016: return launch_one<128, 16, MODE>(a, grid, st);
+    case 128032: return launch_one<128, 32, MODE>(a, grid, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -359,13 +420,9 @@ int mfma_waves() { return kNW; }
 
 hipError_t launch_gqa_mfma(const GqaArgs& a, int d, int heads_per_item, int grid,
                            hipStream_t st) {
-  switch (d * 1000 + heads_per_item) {
-    case 64016: return launch_one<64, 16>(a, grid, st);
-    case 64032: return launch_one<64, 32>(a, grid, st);
-    case 128016: return launch_one<128, 16>(a, grid, st);
-    case 128032: return launch_one<128, 32>(a, grid, st);
-  }
-  return hipErrorInvalidValue;
+  if (a.block_table) return launch_mode<kAddrPaged>(a, d, heads_per_item, grid, st);
+  if (a.n_global > 0) return launch_mode<kAddrGlobal>(a, d, heads_per_item, grid, st);
+  return launch_mode<kAddrDense>(a, d, heads_per_item, grid, st);
 }
 
 }  // namespace attn

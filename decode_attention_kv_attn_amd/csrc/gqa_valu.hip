@@ -25,6 +25,12 @@
 // Rows of a tile past the end of the split are not loaded from their own
 // address: they re-read the tile's first row (always visible) and get weight
 // 0, so no masked cache row is ever read (attention-head section 3).
+//
+// The addressing mode (dense linear/ring, global positions, paged) is a
+// template parameter; this file is compiled once per mode (ATTN_VALU_MODE),
+// so each translation unit holds one mode's instantiations.  On a paged
+// cache the page ids of a wave's next tile are fetched with one vector load
+// a tile ahead, so the row addresses never wait on the block table.
 
 #include "device_common.h"
 #include "internal.h"
@@ -42,6 +48,9 @@
 #endif
 #ifndef ATTN_VALU_NONTEMPORAL  // K/V are read once: stream past the caches
 #define ATTN_VALU_NONTEMPORAL 1
+#endif
+#ifndef ATTN_VALU_MODE  // addressing mode of this translation unit
+#define ATTN_VALU_MODE 0
 #endif
 
 namespace attn {
@@ -122,6 +131,7 @@ struct Cfg {
   static_assert(E % EPC == 0 && D % E == 0, "lane split");
   static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "lanes per row");
   static_assert(TR % RPI == 0, "tile rows");
+  static_assert(TR <= 33, "a tile must fit in three pages of >= 16 rows");
 };
 
 // Fold the state held RPI_STEP row groups away into this lane's state.
@@ -147,7 +157,7 @@ ATTN_DEV void merge_fn(float (&m)[N], float (&l)[N], float (&acc)[N][E], F mv) {
   }
 }
 
-template <typename T, int D, int N>
+template <typename T, int D, int N, int MODE>
 __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
     GqaArgs a) {
   using C = Cfg<T, D, N>;
@@ -160,7 +170,8 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
   __shared__ float sm_l[NW][N];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // uniform across the wave: tile bases and page ids stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rg = lane / LPR;  // row group
   const int cl = lane % LPR;  // lane inside the row
 
@@ -177,15 +188,26 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
   const int g = bid % a.H_kv;
   const int b = bid / a.H_kv;
 
-  const VisibleRange vr = visible_range(a.seq_lens, a.ring_head, b, a.T_cap,
-                                        a.window, a.gpos, a.n_global);
-  const bool ring = a.ring_head != nullptr;
+  const VisibleRange vr =
+      MODE == kAddrGlobal
+          ? visible_range(a.seq_lens, nullptr, b, a.T_cap, a.window, a.gpos, a.n_global)
+          : visible_range(a.seq_lens, MODE == kAddrDense ? a.ring_head : nullptr, b,
+                          a.T_cap, a.window);
+  const bool ring = MODE == kAddrDense && a.ring_head != nullptr;
   int p0, p1;  // this split's virtual rows
   split_range(vr, s, a.S, a.chunk, p0, p1);
   const int h0 = g * a.n + hc * N;       // first query head served
   const int nh = min(N, a.n - hc * N);   // heads actually present
 
-  const size_t kv_off = (size_t)(b * a.H_kv + g) * (size_t)a.T_cap * D;
+  Pages pg{};
+  if constexpr (MODE == kAddrPaged)
+    pg = page_view(a.block_table, a.max_pages, b, vr.hi, a.page_shift, a.num_pages,
+                   a.H_kv);
+  // K/V base of this (sequence, KV head): a [T_cap, D] slab, or the head's
+  // rows inside page 0 of the pool
+  const size_t kv_off = MODE == kAddrPaged
+                            ? ((size_t)g << a.page_shift) * D
+                            : (size_t)(b * a.H_kv + g) * (size_t)a.T_cap * D;
   const T* __restrict__ Kbg = (const T*)a.k + kv_off;
   const T* __restrict__ Vbg = (const T*)a.v + kv_off;
 
@@ -213,15 +235,38 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
   const int span = p1 - p0;
   const int ntiles = span > 0 ? (span + TR - 1) / TR : 0;
 
+  // Cache row (from the K/V base) of virtual row vi of the tile at `base`;
+  // `pid` holds that tile's page ids on a paged cache.
+  auto row_of = [&](int base, int vi, const int (&pid)[3]) -> int {
+    if constexpr (MODE == kAddrDense) return slot_of(vr, ring, vr.lo + vi, a.T_cap);
+    else if constexpr (MODE == kAddrGlobal)
+      return row_slot(vr, false, base >= vr.n_extra, vi, a.T_cap);
+    else return paged_row(pg, pid, vr.lo + base, vr.lo + vi);
+  };
+  // Page ids of tile `it` (paged caches only): one vector load, lane k
+  // holding id k; read with readlane when the tile's loads are issued.
+  auto fetch_pages = [&](int it) -> int {
+    if constexpr (MODE == kAddrPaged) return tile_pages_lanes(pg, vr.lo + p0 + it * TR, lane);
+    else return 0;
+  };
+  auto page_ids = [&](int pv, int (&id)[3]) {
+    if constexpr (MODE == kAddrPaged) page_ids_from_lanes(pg, pv, id);
+  };
+
   // Issue the 16-byte K and V loads of tile `it` (rows past the split's end
   // re-read the tile's first row; they get weight 0 below).
-  auto load_tile = [&](int it, uint4 (&kr)[RPL][CPL], uint4 (&vv)[RPL][CPL]) {
+  // A tile index past the split (uniform) reads row 0 of the K/V base
+  // instead: in bounds, shared by the work group's waves, never used.
+  auto load_tile = [&](int it, int pv, uint4 (&kr)[RPL][CPL],
+                       uint4 (&vv)[RPL][CPL]) {
     const int base = p0 + it * TR;
-    const bool fast = base >= vr.n_extra;  // uniform: no global rows in the tile
+    const bool dummy = it >= ntiles;
+    int pid[3];
+    page_ids(pv, pid);
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
       const int vi = base + rg + i * RPI;
-      const int slot = row_slot(vr, ring, fast, vi < p1 ? vi : base, a.T_cap);
+      const int slot = dummy ? 0 : row_of(base, vi < p1 ? vi : base, pid);
       const T* kp = Kbg + (size_t)slot * D + cl * EPC;
 #pragma unroll
       for (int k = 0; k < CPL; ++k) kr[i][k] = load16(kp + k * LPR * EPC);
@@ -229,7 +274,7 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
       const int vi = base + rg + i * RPI;
-      const int slot = row_slot(vr, ring, fast, vi < p1 ? vi : base, a.T_cap);
+      const int slot = dummy ? 0 : row_of(base, vi < p1 ? vi : base, pid);
       const T* vp = Vbg + (size_t)slot * D + cl * EPC;
 #pragma unroll
       for (int k = 0; k < CPL; ++k) vv[i][k] = load16(vp + k * LPR * EPC);
@@ -298,21 +343,30 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
   };
 
   // Two register stages: the loads of a wave's next tile are in flight
-  // while it computes on the current one.
+  // while it computes on the current one.  The loop body is one pair of
+  // tiles with both loads unconditional (a load behind a condition, or a
+  // break between the halves, makes the compiler's wait for the current
+  // tile also cover the next tile's loads); the tile after the wave's last
+  // re-reads row 0 of the K/V base instead (never used).  Page ids (pA /
+  // pB, alternating like the stages) run a tile ahead of the rows.
   uint4 kA[RPL][CPL], vA[RPL][CPL], kB[RPL][CPL], vB[RPL][CPL];
-  int it = wave;
-  if (it < ntiles) load_tile(it, kA, vA);
-  while (it < ntiles) {
-    int nx = it + NW;
-    if (nx < ntiles) load_tile(nx, kB, vB);
-    compute_tile(it, kA, vA);
-    it = nx;
-    if (it >= ntiles) break;
-    nx = it + NW;
-    if (nx < ntiles) load_tile(nx, kA, vA);
-    compute_tile(it, kB, vB);
-    it = nx;
+  const int nt = wave < ntiles ? (ntiles - wave + NW - 1) / NW : 0;  // this wave's tiles
+  int pA = 0, pB = 0;
+  if (nt > 0) {
+    const int pcur = fetch_pages(wave);
+    pA = fetch_pages(wave + NW);
+    load_tile(wave, pcur, kA, vA);
   }
+  for (int j = 0; j + 1 < nt; j += 2) {
+    const int it = wave + j * NW;
+    pB = fetch_pages(it + 2 * NW);
+    load_tile(it + NW, pA, kB, vB);
+    compute_tile(it, kA, vA);
+    pA = fetch_pages(it + 3 * NW);
+    load_tile(it + 2 * NW, pB, kA, vA);
+    compute_tile(it + NW, kB, vB);
+  }
+  if (nt & 1) compute_tile(wave + (nt - 1) * NW, kA, vA);
 
   // ---- merge the row groups of this wave ----------------------------------
   // Partners are RPI_k = LPR * 2^k lanes away; rotations inside a 16-lane row
@@ -375,16 +429,9 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
 
 template <typename T, int D, int N>
 hipError_t launch_one(const GqaArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((gqa_decode_valu<T, D, N>), dim3(grid),
+  hipLaunchKernelGGL((gqa_decode_valu<T, D, N, ATTN_VALU_MODE>), dim3(grid),
                      dim3(Cfg<T, D, N>::NW * 64), 0, st, a);
   return hipGetLastError();
-}
-
-template <typename T, int D, int N>
-void geometry_one(ValuGeometry* g) {
-  g->heads_per_item = N;
-  g->tile_rows = Cfg<T, D, N>::TR;
-  g->waves = Cfg<T, D, N>::NW;
 }
 
 template <typename T, int D>
@@ -402,6 +449,28 @@ hipError_t launch_d(const GqaArgs& a, int N, int grid, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_mode(const GqaArgs& a, int dtype, int d, int grid, hipStream_t st) {
+  const int N = a.n <= 8 ? a.n : 8;
+  if (dtype == 0) {
+    if (d == 64) return launch_d<float, 64>(a, N, grid, st);
+    if (d == 128) return launch_d<float, 128>(a, N, grid, st);
+    if (d == 256) return launch_d<float, 256>(a, N, grid, st);
+  } else if (dtype == 1) {
+    if (d == 64) return launch_d<uint16_t, 64>(a, N, grid, st);
+    if (d == 128) return launch_d<uint16_t, 128>(a, N, grid, st);
+    if (d == 256) return launch_d<uint16_t, 256>(a, N, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+#if ATTN_VALU_MODE == 0
+template <typename T, int D, int N>
+void geometry_one(ValuGeometry* g) {
+  g->heads_per_item = N;
+  g->tile_rows = Cfg<T, D, N>::TR;
+  g->waves = Cfg<T, D, N>::NW;
+}
+
 template <typename T, int D>
 void geometry_d(int N, ValuGeometry* g) {
   switch (N) {
@@ -415,9 +484,11 @@ void geometry_d(int N, ValuGeometry* g) {
     default: geometry_one<T, D, 8>(g); break;
   }
 }
+#endif
 
 }  // namespace
 
+#if ATTN_VALU_MODE == 0
 // Heads per work item: the whole group when it has <= 8 heads, else chunks
 // of 8 (each chunk re-reads the group's K/V rows).
 bool valu_geometry(int dtype, int d, int n, ValuGeometry* g) {
@@ -441,17 +512,27 @@ bool valu_geometry(int dtype, int d, int n, ValuGeometry* g) {
 
 hipError_t launch_gqa_valu(const GqaArgs& a, int dtype, int d, int grid,
                            hipStream_t st) {
-  const int N = a.n <= 8 ? a.n : 8;
-  if (dtype == 0) {
-    if (d == 64) return launch_d<float, 64>(a, N, grid, st);
-    if (d == 128) return launch_d<float, 128>(a, N, grid, st);
-    if (d == 256) return launch_d<float, 256>(a, N, grid, st);
-  } else if (dtype == 1) {
-    if (d == 64) return launch_d<uint16_t, 64>(a, N, grid, st);
-    if (d == 128) return launch_d<uint16_t, 128>(a, N, grid, st);
-    if (d == 256) return launch_d<uint16_t, 256>(a, N, grid, st);
-  }
-  return hipErrorInvalidValue;
+  if (a.block_table) return launch_gqa_valu_paged(a, dtype, d, grid, st);
+  if (a.n_global > 0) return launch_gqa_valu_global(a, dtype, d, grid, st);
+  return launch_gqa_valu_dense(a, dtype, d, grid, st);
 }
+
+hipError_t launch_gqa_valu_dense(const GqaArgs& a, int dtype, int d, int grid,
+                                 hipStream_t st) {
+  return launch_mode(a, dtype, d, grid, st);
+}
+#elif ATTN_VALU_MODE == 1
+hipError_t launch_gqa_valu_global(const GqaArgs& a, int dtype, int d, int grid,
+                                  hipStream_t st) {
+  return launch_mode(a, dtype, d, grid, st);
+}
+#elif ATTN_VALU_MODE == 2
+hipError_t launch_gqa_valu_paged(const GqaArgs& a, int dtype, int d, int grid,
+                                 hipStream_t st) {
+  return launch_mode(a, dtype, d, grid, st);
+}
+#else
+#error "ATTN_VALU_MODE must be 0 (dense), 1 (global positions) or 2 (paged)"
+#endif
 
 }  // namespace attn

@@ -23,7 +23,9 @@ struct GqaArgs {
   const int32_t* ring_head;  // nullable: linear addressing
   const int32_t* gpos;       // global positions (linear cache only), nullable
   int n_global;
-  int B, H_q, H_kv, T_cap, window;
+  const int32_t* block_table;  // paged cache: [B, max_pages], else nullptr
+  int max_pages, page_shift, num_pages;
+  int B, H_q, H_kv, T_cap, window;  // paged: T_cap = max_pages << page_shift
   int n;            // query heads per KV head
   int head_chunks;  // work items per KV head along the query heads
   int S;            // splits of the visible range
@@ -41,8 +43,16 @@ struct ValuGeometry {
 
 // dtype: 0 = float32, 1 = bf16.  Returns false if no instantiation exists.
 bool valu_geometry(int dtype, int d, int n, ValuGeometry* g);
+// Picks the addressing mode from `a` (paged, global positions, or dense);
+// each mode's instantiations live in a translation unit of their own.
 hipError_t launch_gqa_valu(const GqaArgs& a, int dtype, int d, int grid,
                            hipStream_t stream);
+hipError_t launch_gqa_valu_dense(const GqaArgs& a, int dtype, int d, int grid,
+                                 hipStream_t stream);
+hipError_t launch_gqa_valu_global(const GqaArgs& a, int dtype, int d, int grid,
+                                  hipStream_t stream);
+hipError_t launch_gqa_valu_paged(const GqaArgs& a, int dtype, int d, int grid,
+                                 hipStream_t stream);
 
 // Matrix-core path for large groups (bf16).
 int mfma_heads_per_item(int dtype, int d, int n);
@@ -54,11 +64,24 @@ hipError_t launch_gqa_mfma(const GqaArgs& a, int d, int heads_per_item, int grid
 // Absorbed MLA on the matrix cores (bf16, d_c = 512, d_rope = 64).
 int mla_heads_per_group();
 int mla_tile_rows();
+// block_table == nullptr: dense latent [B, T_cap, 576]; else a page pool
+// [num_pages, 2^page_shift, 576] with T_cap = max_pages << page_shift, and
+// `chunk` a multiple of the tile rows.
 hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
                            float* lse, float* o_part, float* lse_part,
-                           const int32_t* seq_lens, int B, int H, int T_cap,
-                           int S, int chunk, int head_chunks, float scale_log2,
-                           hipStream_t stream);
+                           const int32_t* seq_lens, const int32_t* block_table,
+                           int max_pages, int page_shift, int num_pages, int B,
+                           int H, int T_cap, int S, int chunk, int head_chunks,
+                           float scale_log2, hipStream_t stream);
+
+}  // namespace attn
+
+// Page-geometry check shared by the paged entry points (api.hip); returns an
+// ATTN_* status and log2(page_size) in *shift.
+int attn_check_pages(int max_pages, int num_pages, int page_size, int rows_per_pos,
+                     int* shift);
+
+namespace attn {
 
 hipError_t launch_combine(const float* o_part, const float* lse_part,
                           float* out, float* lse, int B, int H, int S, int d_v,

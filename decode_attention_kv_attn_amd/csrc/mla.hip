@@ -41,7 +41,11 @@ int plan_mla(int B, int H, int T_cap, int d_c, int d_rope, int num_splits,
   }
   if (S < 1) S = 1;
   if (S > T_cap) S = T_cap;
+  // splits start at multiples of the tile rows (a paged cache needs each
+  // 16-row half of a tile inside one page)
+  const int tr = attn::mla_tile_rows();
   p->chunk = (int)((T_cap + S - 1) / S);
+  p->chunk = (p->chunk + tr - 1) / tr * tr;
   p->S = (T_cap + p->chunk - 1) / p->chunk;
   p->ws_bytes = attn_decode_workspace_bytes(B, H, d_c, p->S);
   return ATTN_OK;
@@ -67,11 +71,15 @@ size_t attn_decode_mla_workspace_bytes(int B, int H, int T_cap, int d_c,
   return st == ATTN_OK ? p.ws_bytes : (size_t)-1;
 }
 
-int attn_decode_mla(const void* q, const void* latent, float* out,
-                    float* lse_out, const int32_t* seq_lens, int B, int H,
-                    int T_cap, int d_c, int d_rope, float scale,
-                    int num_splits, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_mla(const void* q, const void* latent, float* out, float* lse_out,
+               const int32_t* seq_lens, const int32_t* block_table,
+               int max_pages, int page_shift, int num_pages, int B, int H,
+               int T_cap, int d_c, int d_rope, float scale, int num_splits,
+               void* workspace, size_t workspace_bytes, void* stream) {
   MlaPlan p;
   int st = plan_mla(B, H, T_cap, d_c, d_rope, num_splits, &p);
   if (st != ATTN_OK) return st;
@@ -92,14 +100,46 @@ int attn_decode_mla(const void* q, const void* latent, float* out,
   }
   if ((long long)B * p.S * p.head_chunks > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
-  if (attn::launch_mla_mfma(q, latent, out, lse_out, o_part, lse_part, seq_lens, B,
-                            H, T_cap, p.S, p.chunk, p.head_chunks,
+  if (attn::launch_mla_mfma(q, latent, out, lse_out, o_part, lse_part, seq_lens,
+                            block_table, max_pages, page_shift, num_pages, B, H,
+                            T_cap, p.S, p.chunk, p.head_chunks,
                             scale * 1.4426950408889634f, s) != hipSuccess)
     return ATTN_ERR_HIP;
   if (p.S > 1 && attn::launch_combine(o_part, lse_part, out, lse_out, B, H, p.S,
                                       d_c, s) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_mla(const void* q, const void* latent, float* out,
+                    float* lse_out, const int32_t* seq_lens, int B, int H,
+                    int T_cap, int d_c, int d_rope, float scale,
+                    int num_splits, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return decode_mla(q, latent, out, lse_out, seq_lens, nullptr, 0, 0, 0, B, H,
+                    T_cap, d_c, d_rope, scale, num_splits, workspace,
+                    workspace_bytes, stream);
+}
+
+int attn_decode_mla_paged(const void* q, const void* latent_pages, float* out,
+                          float* lse_out, const int32_t* seq_lens,
+                          const int32_t* block_table, int max_pages, int B,
+                          int H, int num_pages, int page_size, int d_c,
+                          int d_rope, float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  int shift = 0;
+  const int st = attn_check_pages(max_pages, num_pages, page_size, 1, &shift);
+  if (st != ATTN_OK) return st;
+  if (B > 0 && !block_table) return ATTN_ERR_NULL;
+  if (block_table && !aligned(block_table, 4)) return ATTN_ERR_ALIGN;
+  return decode_mla(q, latent_pages, out, lse_out, seq_lens, block_table,
+                    max_pages, shift, num_pages, B, H, max_pages * page_size, d_c,
+                    d_rope, scale, num_splits, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -20,6 +20,13 @@
 //
 // The weights keep ~16 significant bits as P_hi + P_lo in bf16 (two MFMAs
 // per value block); the value columns stay exactly bf16.
+//
+// Paged latent caches ([num_pages, P, 576], P a power of two >= 16; the
+// paging the baidu article, section 四.3, names for MLA): splits and tiles
+// start at multiples of 32 positions, so each 16-row half of a tile lies in
+// one page and a tile needs two page ids.  They are fetched a tile ahead
+// with one vector load, issued before the direct-to-LDS loads of the tile
+// two ahead, so the pipeline's own vmcnt wait already covers it.
 
 #include <type_traits>
 
@@ -97,7 +104,9 @@ ATTN_DEV void wait_vmcnt() {
 
 struct MlaArgs {
   const uint16_t* q;       // [B, H, 576]
-  const uint16_t* latent;  // [B, T_cap, 576]
+  const uint16_t* latent;  // [B, T_cap, 576], or the page pool [num_pages, P, 576]
+  const int32_t* block_table;  // [B, max_pages] (paged only)
+  int max_pages, page_shift, num_pages;
   float* out;              // [B, H, 512] when S == 1
   float* lse;              // [B, H] (nullable) when S == 1
   float* o_part;           // [B, H, S, 512]
@@ -107,6 +116,7 @@ struct MlaArgs {
   float scale_log2;
 };
 
+template <int MODE>
 __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
   const int lane = threadIdx.x & 63;
   // uniform across the wave: keep wave-derived offsets in scalar registers
@@ -126,7 +136,12 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
   const int hw0 = hc * kHG + wave * kHW;  // first head of this wave
   const int span = p1 - p0;
   const int ntiles = span > 0 ? (span + kTT - 1) / kTT : 0;
-  const unsigned char* lat_b = (const unsigned char*)(a.latent + (size_t)b * a.T_cap * kDK);
+  const unsigned char* lat_b =
+      (const unsigned char*)(MODE == kAddrPaged ? a.latent
+                                                : a.latent + (size_t)b * a.T_cap * kDK);
+  Pages pg{};
+  if constexpr (MODE == kAddrPaged)
+    pg = page_view(a.block_table, a.max_pages, b, vr.hi, a.page_shift, a.num_pages, 1);
 
   // Q^T fragments: head hw0 + 16*hb + li, elements 32*ks + 8*lg .. +7
   uint4 qf[2][kKS];
@@ -155,6 +170,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
   // loads: LDS chunk p = blk*64 + lane holds row p/72, logical chunk
   // (p%72) ^ swz(row).  Offsets are < 2^16, two per register.
   uint32_t dma_off[(kDmaPerWave + 1) / 2];
+  uint32_t hi_rows = 0;  // bit j: load j of this lane is in the tile's rows 16..31
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j) {
     const int p = (wave * kDmaPerWave + j) * 64 + lane;
@@ -162,24 +178,49 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
     const uint32_t off = t * kRowBytes + 16 * ((p - t * kCPR) ^ swz(t));
     if (j & 1) dma_off[j >> 1] |= off << 16;
     else dma_off[j >> 1] = off;
+    hi_rows |= (t >= 16 ? 1u : 0u) << j;
   }
+
+  // Page ids of the tile in each stage (paged caches only): lane k holds
+  // id k of the tile's pages.
+  int pidv[3] = {0, 0, 0};
+  auto fetch_pages = [&](auto stage_tag, int it) {
+    constexpr int I = decltype(stage_tag)::value;
+    if constexpr (MODE == kAddrPaged) pidv[I] = tile_pages_lanes(pg, p0 + it * kTT, lane);
+  };
 
   // Direct-to-LDS load j (of kDmaPerWave) of tile `it` into stage I.
   auto issue_piece = [&](auto stage_tag, int it, int j) {
     constexpr int I = decltype(stage_tag)::value;
     const int base = p0 + it * kTT;
     const int nvalid = p1 - base;  // rows of this tile inside the split
-    const unsigned char* tbase = lat_b + (size_t)base * kRowBytes;
     const int blk = wave * kDmaPerWave + j;
     uint32_t off = (dma_off[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+    bool hi = (hi_rows >> j) & 1;
     if (nvalid < kTT) {  // uniform: the split's last, partial tile
       const int p = blk * 64 + lane;
       const int t = p / kCPR;
       // a row past the split reads the same chunk of the tile's first row
-      if (t >= nvalid) off = 16 * (p - t * kCPR);
+      if (t >= nvalid) {
+        off = 16 * (p - t * kCPR);
+        hi = false;
+      }
+    }
+    const unsigned char* src;
+    if constexpr (MODE == kAddrPaged) {
+      // rows 0..15 sit in one page, rows 16..31 in one page; `off` counts
+      // rows from the tile's start, so the upper half's base is shifted back
+      // by 16 rows (the sum stays inside the pool)
+      int id[3];
+      page_ids_from_lanes(pg, pidv[I], id);
+      const int rlo = paged_row(pg, id, base, base);
+      const int rhi = paged_row(pg, id, base, base + 16) - 16;
+      src = lat_b + ((long long)(hi ? rhi : rlo) * kRowBytes + off);
+    } else {
+      src = lat_b + (size_t)base * kRowBytes + off;
     }
     __builtin_amdgcn_global_load_lds(
-        (const void*)(tbase + off),
+        (const void*)src,
         (__attribute__((address_space(3))) void*)(stage<I>() + blk * 1024), 16, 0, 0);
   };
   auto issue_tile = [&](auto stage_tag, int it) {
@@ -194,6 +235,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
     constexpr int I = decltype(stage_tag)::value;
     const unsigned char* tile = stage<I>();
     const int base = p0 + it * kTT;
+    // page ids of tile it+3 (its stage is this one), ahead of the loads of
+    // tile it+2 below
+    fetch_pages(stage_tag, it + 3);
 
     // scores.  Chunk (4*ks + lg) ^ swz(t) = 8*(ks/2) + ((4*(ks&1) + lg) ^ swz(t)):
     // two base addresses per row block, the rest is an immediate offset.
@@ -333,6 +377,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
     compute_tile(stage_tag, it, it + 2 < ntiles);
   };
 
+  fetch_pages(std::integral_constant<int, 0>{}, 0);
+  fetch_pages(std::integral_constant<int, 1>{}, 1);
+  fetch_pages(std::integral_constant<int, 2>{}, 2);
   if (ntiles > 0) issue_tile(std::integral_constant<int, 0>{}, 0);
   if (ntiles > 1) issue_tile(std::integral_constant<int, 1>{}, 1);
   for (int it = 0; it < ntiles; it += 3) {
@@ -376,12 +423,17 @@ int mla_tile_rows() { return kTT; }
 
 hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
                            float* lse, float* o_part, float* lse_part,
-                           const int32_t* seq_lens, int B, int H, int T_cap,
-                           int S, int chunk, int head_chunks, float scale_log2,
-                           hipStream_t stream) {
+                           const int32_t* seq_lens, const int32_t* block_table,
+                           int max_pages, int page_shift, int num_pages, int B,
+                           int H, int T_cap, int S, int chunk, int head_chunks,
+                           float scale_log2, hipStream_t stream) {
   MlaArgs a;
   a.q = (const uint16_t*)q;
   a.latent = (const uint16_t*)latent;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.page_shift = page_shift;
+  a.num_pages = num_pages;
   a.out = out;
   a.lse = lse;
   a.o_part = o_part;
@@ -394,8 +446,12 @@ hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
   a.head_chunks = head_chunks;
   a.scale_log2 = scale_log2;
   const long long grid = (long long)B * S * head_chunks;
-  hipLaunchKernelGGL(mla_decode_mfma, dim3((unsigned)grid), dim3(kNW * 64), 0,
-                     stream, a);
+  if (block_table)
+    hipLaunchKernelGGL(mla_decode_mfma<kAddrPaged>, dim3((unsigned)grid),
+                       dim3(kNW * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(mla_decode_mfma<kAddrDense>, dim3((unsigned)grid),
+                       dim3(kNW * 64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -23,6 +23,12 @@
 // Ring addressing: position j lives in slot (head - (t - j)) mod S_cap, where
 // head is the slot of the newest position.  For a resident j, 0 <= t-j <
 // S_cap, so one conditional add replaces the modulo.
+//
+// Paged addressing (the KV-cache paging the baidu article, section 四.3,
+// names as the system side of GQA and MLA): the cache is a pool of pages of
+// P = 2^shift positions, [num_pages, H_kv, P, d] (one page holds every KV
+// head's rows of its positions, each head's P rows contiguous); position j
+// of sequence b lives in page table[b][j >> shift], row j & (P - 1).
 #pragma once
 
 #include "device_common.h"
@@ -120,6 +126,72 @@ ATTN_DEV void split_range(const VisibleRange& r, int s, int S, int chunk,
   p0 = a < r.n ? (int)a : r.n;
   const long long e = (s == S - 1) ? (long long)r.n : a + chunk;
   p1 = e < r.n ? (int)e : r.n;
+}
+
+// Addressing modes, fixed per kernel instantiation so that the common case
+// carries no per-row branches: a dense [B, H_kv, T_cap, d] cache (linear or
+// ring), a linear cache with global positions, or a paged cache.
+enum AddrMode : int { kAddrDense = 0, kAddrGlobal = 1, kAddrPaged = 2 };
+
+// One sequence's view of a paged cache.
+struct Pages {
+  const int32_t* table;  // this sequence's block-table row
+  int shift;             // log2 of the page size
+  int last;              // last table entry the sequence uses (>= 0)
+  int num_pages;         // pool size: page ids are clamped to [0, num_pages)
+  int stride;            // rows from one page to the next for one head
+};
+
+ATTN_DEV Pages page_view(const int32_t* block_table, int max_pages, int b,
+                         int T_b, int shift, int num_pages, int H_kv) {
+  Pages p;
+  p.table = block_table + (size_t)b * max_pages;
+  p.shift = shift;
+  const int last = T_b > 0 ? (T_b - 1) >> shift : 0;
+  p.last = last < max_pages ? last : max_pages - 1;
+  p.num_pages = num_pages;
+  p.stride = H_kv << shift;
+  return p;
+}
+
+// Ids of the three pages starting with the one that holds position pos0:
+// every tile of at most 2P + 1 rows starting at pos0 lies inside them.
+// Entries past the sequence's last page repeat that page; ids outside the
+// pool are clamped, so a corrupt table cannot address outside it.
+ATTN_DEV void tile_pages(const Pages& p, int pos0, int (&id)[3]) {
+  const int j0 = pos0 >> p.shift;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int j = min(j0 + k, p.last);
+    const int v = p.table[j];
+    id[k] = v < 0 ? 0 : (v >= p.num_pages ? p.num_pages - 1 : v);
+  }
+}
+
+// The same three table entries with one vector load: lane k < 3 gets entry
+// k (the others repeat entry 2), unclamped.  The caller reads them with
+// page_ids_from_lanes only when it issues the tile's loads, so the wait for
+// this load lands there and not next to the load.
+ATTN_DEV int tile_pages_lanes(const Pages& p, int pos0, int lane) {
+  const int j = min((pos0 >> p.shift) + min(lane, 2), p.last);
+  return p.table[j];
+}
+
+// Ids (clamped to the pool) from the lanes filled by tile_pages_lanes.
+ATTN_DEV void page_ids_from_lanes(const Pages& p, int pv, int (&id)[3]) {
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int v = __builtin_amdgcn_readlane(pv, k);
+    id[k] = v < 0 ? 0 : (v >= p.num_pages ? p.num_pages - 1 : v);
+  }
+}
+
+// Row (in units of one head's rows, from the head's base) of position pos
+// of a tile that starts at pos0 <= pos.
+ATTN_DEV int paged_row(const Pages& p, const int (&id)[3], int pos0, int pos) {
+  const int k = (pos >> p.shift) - (pos0 >> p.shift);
+  const int page = k == 0 ? id[0] : (k == 1 ? id[1] : id[2]);
+  return page * p.stride + (pos & ((1 << p.shift) - 1));
 }
 
 }  // namespace attn

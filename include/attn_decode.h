@@ -157,6 +157,39 @@ int attn_decode_gqa_global(const void* q, const void* k, const void* v,
                            void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/*
+ * attn_decode_gqa_paged -- attn_decode_gqa over a paged KV cache (the KV
+ * cache paging that the baidu article, section 四.3, names as the serving
+ * side of MQA / GQA and MLA; the pages fix no layout, this one is the
+ * library's).
+ *
+ *   k_pages, v_pages [num_pages, H_kv, page_size, d] dtype: a pool of
+ *             pages; page p holds page_size consecutive positions of one
+ *             sequence for every KV head, each head's rows contiguous.
+ *   block_table [B, max_pages] int32: position j of sequence b lives in
+ *             page block_table[b][j / page_size], row j % page_size.
+ *             Only entries 0 .. (T_b - 1) / page_size of a row are read.
+ *   seq_lens  [B] int32, may be NULL (all max_pages * page_size); clamped
+ *             to [0, max_pages * page_size].
+ *   page_size a power of two, 16 .. 65536 (else ATTN_ERR_UNSUPPORTED).
+ *   num_pages >= 1, max_pages >= 1; max_pages * page_size <= 2^30 and
+ *             num_pages * H_kv * page_size < 2^31 (else ATTN_ERR_SHAPE).
+ *   window    as for attn_decode_gqa (no ring mode on a paged cache).
+ *   Everything else as for attn_decode_gqa.  Split count and workspace are
+ *   those of attn_decode_gqa_splits / _workspace_bytes with
+ *   T_cap = max_pages * page_size and ring = 0.
+ *   Table entries are not checked on the host: ids outside [0, num_pages)
+ *   are clamped to the pool, so no access leaves it (the result is then
+ *   unspecified).
+ */
+int attn_decode_gqa_paged(const void* q, const void* k_pages,
+                          const void* v_pages, float* out, float* lse_out,
+                          const int32_t* seq_lens, const int32_t* block_table,
+                          int max_pages, int B, int H_q, int H_kv, int num_pages,
+                          int page_size, int d, int dtype, int window,
+                          float scale, int num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /* Split count and workspace bytes of attn_decode_gqa_global, with the same
  * return conventions as attn_decode_gqa_splits / _workspace_bytes. */
 int attn_decode_gqa_global_splits(int B, int H_q, int H_kv, int T_cap, int d,
@@ -208,6 +241,33 @@ size_t attn_decode_mla_workspace_bytes(int B, int H, int T_cap, int d_c,
                                        int d_rope, int num_splits);
 
 /*
+ * attn_decode_mla_paged -- attn_decode_mla over a paged latent cache (the
+ * paging strategy the baidu article, section 四.3, says an MLA stack must
+ * adapt; the layout is the library's).
+ *
+ *   latent_pages [num_pages, page_size, d_c + d_rope] bf16: a pool of
+ *             pages of page_size consecutive latent rows [c_j | k^R_j].
+ *   block_table [B, max_pages] int32: position j of sequence b lives in
+ *             page block_table[b][j / page_size], row j % page_size; only
+ *             entries 0 .. (T_b - 1) / page_size are read.
+ *   seq_lens  [B] int32, may be NULL (all max_pages * page_size); clamped
+ *             to [0, max_pages * page_size].
+ *   page_size, num_pages, max_pages: as for attn_decode_gqa_paged (with
+ *             H_kv = 1 in the pool-size bound).
+ *   Everything else as for attn_decode_mla; split count and workspace are
+ *   those of attn_decode_mla_splits / _workspace_bytes with
+ *   T_cap = max_pages * page_size.  Table ids outside [0, num_pages) are
+ *   clamped to the pool.
+ */
+int attn_decode_mla_paged(const void* q, const void* latent_pages, float* out,
+                          float* lse_out, const int32_t* seq_lens,
+                          const int32_t* block_table, int max_pages, int B,
+                          int H, int num_pages, int page_size, int d_c,
+                          int d_rope, float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
  * attn_combine -- merge results computed over S disjoint parts of each key
  * set.  With L = max_s lse_part[s] and w_s = exp(lse_part[s] - L):
  *     out = sum_s w_s o_part[s] / sum_s w_s,   lse = L + ln(sum_s w_s).
@@ -251,6 +311,24 @@ int attn_kv_append(void* k_cache, void* v_cache, const void* k_new,
 int attn_kv_append_ring(void* k_cache, void* v_cache, const void* k_new,
                         const void* v_new, int32_t* ring_head, int B, int H,
                         int T_cap, int d, int dtype, void* stream);
+
+/*
+ * attn_kv_append_paged -- attn_kv_append into a paged pool (the layout of
+ * attn_decode_gqa_paged; a latent pool [num_pages, page_size, d_c + d_rope]
+ * is the case H = 1).  For every sequence b with
+ * 0 <= positions[b] < max_pages * page_size and every head h:
+ *     k_pages[block_table[b][pos / page_size], h, pos % page_size, :] = k_new[b, h, :]
+ *   k_pages, v_pages [num_pages, H, page_size, d]; k_new, v_new [B, H, d];
+ *   v_pages / v_new may both be NULL.  positions and block_table are device
+ *   int32 arrays ([B] and [B, max_pages]); page ids outside [0, num_pages)
+ *   are clamped to the pool.  Page geometry is checked as for
+ *   attn_decode_gqa_paged; rows must be a multiple of 16 bytes.
+ */
+int attn_kv_append_paged(void* k_pages, void* v_pages, const void* k_new,
+                         const void* v_new, const int32_t* positions,
+                         const int32_t* block_table, int max_pages, int B, int H,
+                         int num_pages, int page_size, int d, int dtype,
+                         void* stream);
 
 /* Bytes of the split buffers for S splits: o_part [B,H,S,d_v] and lse_part
  * [B,H,S], float32, each 256-byte aligned inside the workspace (0 if S<=1). */

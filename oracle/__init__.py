@@ -21,7 +21,8 @@ against the pages by eye.  Short names used for the pages in the citations:
 * ``llmdeepdive``  - "MQA, GQA e MLA" (llmdeepdive.com lesson 7.6),
   section "Conceito": per-token cache accounting.
 * ``baidu``  - "大模型注意力机制对比：MLA与MQA该怎么选" (cloud.baidu.com),
-  section 二: cache shapes of MHA, MQA and MLA.
+  section 二: cache shapes of MHA, MQA and MLA; section 四.3: KV-cache
+  paging as the serving side of both.
 * ``astro-blog``  - "MHA vs MQA vs GQA vs MLA：四种 Attention 机制显存与性能全对比":
   the ``calc_kv_cache_memory`` helper.
 """
@@ -39,4 +40,8 @@ from .attention import (  # noqa: F401
     partial_ref,
     kv_append_ref,
     kv_append_ring_ref,
+    paged_positions,
+    gqa_decode_paged_ref,
+    mla_decode_paged_ref,
+    kv_append_paged_ref,
 )

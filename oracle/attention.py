@@ -51,6 +51,10 @@ __all__ = [
     "partial_ref",
     "kv_append_ref",
     "kv_append_ring_ref",
+    "paged_positions",
+    "gqa_decode_paged_ref",
+    "mla_decode_paged_ref",
+    "kv_append_paged_ref",
 ]
 
 
@@ -395,3 +399,100 @@ def kv_append_ring_ref(cache, new_rows, ring_head):
         out[b, ..., h, :] = new_rows[b]
         new_heads.append(h)
     return out, np.array(new_heads, dtype=np.int64)
+
+
+# --------------------------------------------------------------------------
+# Paged caches
+# --------------------------------------------------------------------------
+# The baidu article (section 四.3) names KV-cache paging as the memory
+# management a serving stack puts around GQA and MLA, without fixing a
+# layout.  The reading taken here: a pool of pages of P consecutive
+# positions; sequence b's position j lives in page block_table[b][j // P]
+# at row j % P; a GQA page holds every KV head, [num_pages, H_kv, P, d], an
+# MLA page the latent rows, [num_pages, P, d_c + d_rope].
+
+
+def paged_positions(positions, block_table_row, page_size):
+    """(page, row) of each logical position of one sequence."""
+    positions = np.asarray(positions, dtype=np.int64)
+    table = np.asarray(block_table_row, dtype=np.int64)
+    return table[positions // page_size], positions % page_size
+
+
+def gqa_decode_paged_ref(q, k_pages, v_pages, block_table, seq_lens=None,
+                         window=0, scale=None):
+    """Decode attention over a paged K/V pool: gather each sequence's rows
+    through its block table into the linear layout, then apply the plain
+    definition (``gqa_decode_ref``) to it.
+
+    k_pages / v_pages [num_pages, H_kv, P, d]; block_table [B, max_pages];
+    seq_lens [B] (default max_pages * P).
+    """
+    q64 = _as_f64(q)
+    kp, vp = _as_f64(k_pages), _as_f64(v_pages)
+    if hasattr(block_table, "detach"):
+        block_table = block_table.detach().cpu().numpy()
+    table = np.asarray(block_table, dtype=np.int64)
+    B = q64.shape[0]
+    _, H_kv, P, d = kp.shape
+    T_cap = table.shape[1] * P
+    lens = _as_int(seq_lens, B, T_cap)
+    k_lin = np.zeros((B, H_kv, T_cap, d))
+    v_lin = np.zeros((B, H_kv, T_cap, vp.shape[3]))
+    for b in range(B):
+        if lens[b] > T_cap:
+            raise ValueError("seq_len exceeds the block table")
+        pos = np.arange(lens[b])
+        page, row = paged_positions(pos, table[b], P)
+        k_lin[b][:, pos] = kp[page, :, row].transpose(1, 0, 2)
+        v_lin[b][:, pos] = vp[page, :, row].transpose(1, 0, 2)
+    return gqa_decode_ref(q64, k_lin, v_lin, lens, None, window, scale)
+
+
+def mla_decode_paged_ref(q, latent_pages, block_table, d_c, scale,
+                         seq_lens=None):
+    """Absorbed MLA over a paged latent pool [num_pages, P, d_c + d_rope]:
+    gather each sequence's rows through its block table, then apply
+    ``mla_decode_ref``."""
+    q64 = _as_f64(q)
+    lp = _as_f64(latent_pages)
+    if hasattr(block_table, "detach"):
+        block_table = block_table.detach().cpu().numpy()
+    table = np.asarray(block_table, dtype=np.int64)
+    B = q64.shape[0]
+    _, P, dk = lp.shape
+    T_cap = table.shape[1] * P
+    lens = _as_int(seq_lens, B, T_cap)
+    lat = np.zeros((B, T_cap, dk))
+    for b in range(B):
+        if lens[b] > T_cap:
+            raise ValueError("seq_len exceeds the block table")
+        pos = np.arange(lens[b])
+        page, row = paged_positions(pos, table[b], P)
+        lat[b, pos] = lp[page, row]
+    return mla_decode_ref(q64, lat, d_c, scale, lens)
+
+
+def kv_append_paged_ref(pages, new_rows, positions, block_table):
+    """Write each sequence's new row at its position of a paged pool.
+
+    pages [num_pages, H, P, d] (or [num_pages, P, d] for a latent pool),
+    new_rows [B, H, d] (or [B, d]), positions [B]; positions outside the
+    block table are not written.  Returns a new array."""
+    out = np.array(_as_f64(pages), copy=True)
+    new_rows = _as_f64(new_rows)
+    if hasattr(block_table, "detach"):
+        block_table = block_table.detach().cpu().numpy()
+    table = np.asarray(block_table, dtype=np.int64)
+    latent = out.ndim == 3
+    P = out.shape[1] if latent else out.shape[2]
+    B = table.shape[0]
+    pos = _as_int(positions, B, 0)
+    for b in range(B):
+        if 0 <= pos[b] < table.shape[1] * P:
+            page, row = paged_positions([pos[b]], table[b], P)
+            if latent:
+                out[page[0], row[0]] = new_rows[b]
+            else:
+                out[page[0], :, row[0]] = new_rows[b]
+    return out

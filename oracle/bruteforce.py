@@ -151,3 +151,78 @@ def combine_brute(o_part, lse_part):
         res_o.append(ro)
         res_l.append(rl)
     return res_o, res_l
+
+
+def gqa_decode_paged_brute(q, k_pages, v_pages, block_table, seq_lens,
+                           window=0, scale=None):
+    """Scalar-loop decode over a paged pool: walk every block-table entry and
+    every row of its page, derive the row's logical position from where it
+    sits (entry index * P + row), and keep it if it is visible."""
+    q, kp, vp = _lst(q), _lst(k_pages), _lst(v_pages)
+    table = [[int(x) for x in row] for row in _lst(block_table)]
+    B, H_q, d = len(q), len(q[0]), len(q[0][0])
+    H_kv, P = len(kp[0]), len(kp[0][0])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lens = [int(x) for x in _lst(seq_lens)]
+    out, lse = [], []
+    for b in range(B):
+        t = lens[b] - 1
+        rows = []  # (position, page, row)
+        for j, page in enumerate(table[b]):
+            for r in range(P):
+                pos = j * P + r
+                if pos > t:
+                    continue
+                if window > 0 and t - pos >= window:
+                    continue
+                rows.append((pos, page, r))
+        ob, lb = [], []
+        for h in range(H_q):
+            g = h * H_kv // H_q
+            if not rows:
+                ob.append([0.0] * len(vp[0][0][0]))
+                lb.append(-math.inf)
+                continue
+            scores = [scale * math.fsum(q[b][h][i] * kp[page][g][r][i]
+                                        for i in range(d)) for _, page, r in rows]
+            vals = [vp[page][g][r] for _, page, r in rows]
+            o, l = _softmax_weighted(scores, vals)
+            ob.append(o)
+            lb.append(l)
+        out.append(ob)
+        lse.append(lb)
+    return out, lse
+
+
+def mla_decode_paged_brute(q, latent_pages, block_table, d_c, scale, seq_lens):
+    """Scalar-loop absorbed MLA over a paged latent pool (same walk as
+    ``gqa_decode_paged_brute``; content and RoPE sums kept apart)."""
+    q, lp = _lst(q), _lst(latent_pages)
+    table = [[int(x) for x in row] for row in _lst(block_table)]
+    B, H, dk = len(q), len(q[0]), len(q[0][0])
+    P = len(lp[0])
+    lens = [int(x) for x in _lst(seq_lens)]
+    out, lse = [], []
+    for b in range(B):
+        rows = [(j * P + r, page, r) for j, page in enumerate(table[b])
+                for r in range(P) if j * P + r < lens[b]]
+        ob, lb = [], []
+        for h in range(H):
+            if not rows:
+                ob.append([0.0] * d_c)
+                lb.append(-math.inf)
+                continue
+            scores = []
+            for _, page, r in rows:
+                row = lp[page][r]
+                content = math.fsum(q[b][h][i] * row[i] for i in range(d_c))
+                rope = math.fsum(q[b][h][i] * row[i] for i in range(d_c, dk))
+                scores.append(scale * (content + rope))
+            vals = [lp[page][r][:d_c] for _, page, r in rows]
+            o, l = _softmax_weighted(scores, vals)
+            ob.append(o)
+            lb.append(l)
+        out.append(ob)
+        lse.append(lb)
+    return out, lse

@@ -164,3 +164,30 @@ def test_global_host_errors(lib):
     # without global positions the plan is attn_decode_gqa's
     assert (lib.attn_decode_gqa_global_splits(8, 32, 8, 4096, 128, 1, 512, 0, 0)
             == lib.attn_decode_gqa_splits(8, 32, 8, 4096, 128, 1, 512, 0, 0))
+
+
+def test_paged_host_errors(lib):
+    def gp(bt=P16, max_pages=8, num_pages=64, P=16, B=1, H_kv=2, q=P16):
+        return lib.attn_decode_gqa_paged(q, P16, P16, P16, None, None, bt, max_pages,
+                                         B, 8, H_kv, num_pages, P, 64, 1, 0, 0.0, 0,
+                                         None, 0, None)
+    assert gp(bt=None) == -1
+    assert gp(P=24) == -4            # not a power of two
+    assert gp(P=8) == -4             # below the smallest page
+    assert gp(max_pages=0) == -2
+    assert gp(num_pages=0) == -2
+    assert gp(num_pages=1 << 26, P=64) == -2   # pool rows overflow 32 bits
+    assert gp(bt=ctypes.c_void_p(4098)) == -7
+    assert gp(q=None) == -1
+    assert gp(B=0, bt=None, q=None) == 0
+
+    def mp(bt=P16, P=64, d_c=512):
+        return lib.attn_decode_mla_paged(P16, P16, P16, None, None, bt, 4, 1, 16, 8,
+                                         P, d_c, 64, 0.07, 0, None, 0, None)
+    assert mp(bt=None) == -1
+    assert mp(P=48) == -4
+    assert mp(d_c=256) == -4
+    ap = lib.attn_kv_append_paged
+    assert ap(P16, None, P16, None, P16, None, 4, 1, 2, 8, 16, 64, 1, None) == -1
+    assert ap(P16, None, P16, None, P16, P16, 4, 1, 2, 8, 12, 64, 1, None) == -4
+    assert ap(None, None, None, None, None, None, 4, 0, 2, 8, 16, 64, 1, None) == 0

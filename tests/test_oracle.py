@@ -669,3 +669,154 @@ def test_global_brute_force():
 
 
 ALL_CHECKS += [check_global_golden, check_global_brute_force]
+
+
+# -------------------------------------------------------------- paged caches
+def _paged_pool(rng, lens, P, H, d, spare=3):
+    """A shuffled pool holding each sequence's positions 0..len-1 in pages of
+    P rows, plus a few unused pages; returns (pool, table)."""
+    need = [max(1, -(-int(n) // P)) for n in lens]
+    max_pages = max(need)
+    n_pages = sum(need) + spare
+    perm = rng.permutation(n_pages)
+    pool = rng.standard_normal((n_pages, H, P, d))
+    table = np.full((len(lens), max_pages), int(n_pages - 1), dtype=np.int64)
+    k = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[k:k + n]
+        k += n
+    return pool, table
+
+
+def check_paged_brute_force(seed=17):
+    """Vectorised paged reference == scalar page walk, over shuffled pools,
+    page sizes 1..4, windows, ragged and empty sequences."""
+    rng = _rng(seed)
+    for c in range(25):
+        P = int(rng.integers(1, 5))
+        lens = rng.integers(0, 14, size=2)
+        H_q, H_kv, d = 4, 2, 3
+        kp, table = _paged_pool(rng, lens, P, H_kv, d)
+        vp = rng.standard_normal(kp.shape)
+        q = rng.standard_normal((2, H_q, d))
+        w = int(rng.choice([0, 1, 2, 5]))
+        o, l = oracle.gqa_decode_paged_ref(q, kp, vp, table, lens, w, 0.8)
+        ob, lb = BF.gqa_decode_paged_brute(q, kp, vp, table, lens, w, 0.8)
+        assert np.allclose(o, np.array(ob), atol=1e-12), c
+        lb = np.array(lb)
+        fin = np.isfinite(l)
+        assert np.array_equal(fin, np.isfinite(lb)) and np.allclose(l[fin], lb[fin], atol=1e-12)
+
+
+def test_paged_brute_force():
+    check_paged_brute_force()
+
+
+def check_paged_contiguous_reduction(seed=18):
+    """A contiguous cache cut into pages with the identity block table is the
+    linear cache: results equal the (pinned) linear reference exactly."""
+    rng = _rng(seed)
+    B, H_q, H_kv, T, d, P = 3, 6, 3, 24, 5, 4
+    k = rng.standard_normal((B, H_kv, T, d))
+    v = rng.standard_normal((B, H_kv, T, d))
+    q = rng.standard_normal((B, H_q, d))
+    lens = np.array([24, 13, 1])
+    npb = T // P
+    kp = k.reshape(B, H_kv, npb, P, d).transpose(0, 2, 1, 3, 4).reshape(B * npb, H_kv, P, d)
+    vp = v.reshape(B, H_kv, npb, P, d).transpose(0, 2, 1, 3, 4).reshape(B * npb, H_kv, P, d)
+    table = np.arange(B * npb).reshape(B, npb)
+    for w in (0, 3):
+        o, l = oracle.gqa_decode_paged_ref(q, kp, vp, table, lens, w)
+        o2, l2 = oracle.gqa_decode_ref(q, k, v, lens, window=w)
+        assert np.array_equal(o, o2) and np.array_equal(l, l2)
+
+
+def test_paged_contiguous_reduction():
+    check_paged_contiguous_reduction()
+
+
+def check_paged_permutation_invariance(seed=19):
+    """Moving pages inside the pool and rewriting the table to match changes
+    nothing."""
+    rng = _rng(seed)
+    lens = np.array([11, 7])
+    kp, table = _paged_pool(rng, lens, 2, 2, 3)
+    vp = rng.standard_normal(kp.shape)
+    q = rng.standard_normal((2, 4, 3))
+    perm = rng.permutation(kp.shape[0])
+    inv = np.argsort(perm)
+    o, l = oracle.gqa_decode_paged_ref(q, kp, vp, table, lens)
+    o2, l2 = oracle.gqa_decode_paged_ref(q, kp[perm], vp[perm], inv[table], lens)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+
+
+def test_paged_permutation_invariance():
+    check_paged_permutation_invariance()
+
+
+def check_mla_paged(seed=20):
+    """Paged MLA == scalar page walk, and == the linear MLA reference on a
+    contiguous cache cut into pages."""
+    rng = _rng(seed)
+    d_c, dk, P = 4, 6, 2
+    lens = np.array([7, 0, 4])
+    pool = rng.standard_normal((9, P, dk))
+    table = np.array([[3, 0, 7, 5], [1, 1, 1, 1], [8, 2, 4, 4]])
+    q = rng.standard_normal((3, 3, dk))
+    z, l = oracle.mla_decode_paged_ref(q, pool, table, d_c, 0.5, lens)
+    zb, lb = BF.mla_decode_paged_brute(q, pool, table, d_c, 0.5, lens)
+    assert np.allclose(z, np.array(zb), atol=1e-12)
+    fin = np.isfinite(l)
+    assert np.array_equal(fin, np.isfinite(np.array(lb)))
+    assert np.allclose(l[fin], np.array(lb)[fin], atol=1e-12)
+    lat = rng.standard_normal((2, 8, dk))
+    pages = lat.reshape(2 * 4, P, dk)
+    t2 = np.arange(8).reshape(2, 4)
+    z1, l1 = oracle.mla_decode_paged_ref(q[:2], pages, t2, d_c, 0.5, [8, 5])
+    z2, l2 = oracle.mla_decode_ref(q[:2], lat, d_c, 0.5, [8, 5])
+    assert np.array_equal(z1, z2) and np.array_equal(l1, l2)
+
+
+def test_mla_paged():
+    check_mla_paged()
+
+
+def check_paged_append(seed=21):
+    """Appending into a paged pool and decoding equals appending into the
+    linear cache and decoding."""
+    rng = _rng(seed)
+    B, H_kv, T, d, P = 2, 2, 8, 3, 4
+    k = rng.standard_normal((B, H_kv, T, d))
+    kn = rng.standard_normal((B, H_kv, d))
+    pos = np.array([5, 0])
+    kp = k.reshape(B, H_kv, 2, P, d).transpose(0, 2, 1, 3, 4).reshape(B * 2, H_kv, P, d)
+    kp = kp[[0, 2, 1, 3]]  # pool order: seq0 page0, seq1 page0, seq0 page1, seq1 page1
+    table = np.array([[0, 2], [1, 3]])
+    got = oracle.kv_append_paged_ref(kp, kn, pos, table)
+    lin = oracle.kv_append_ref(k, kn, pos)
+    q = rng.standard_normal((B, 4, d))
+    o1, l1 = oracle.gqa_decode_paged_ref(q, got, got, table, pos + 1)
+    o2, l2 = oracle.gqa_decode_ref(q, lin, lin, pos + 1)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # positions past the table are not written
+    assert np.array_equal(oracle.kv_append_paged_ref(kp, kn, [8, -1], table), kp)
+
+
+def test_paged_append():
+    check_paged_append()
+
+
+ALL_CHECKS += [check_paged_brute_force, check_paged_contiguous_reduction,
+               check_paged_permutation_invariance, check_mla_paged,
+               check_paged_append]
+
+
+@pytest.mark.parametrize("mutant", [
+    lambda pos, row, P: (np.asarray(row)[np.asarray(pos) % P], np.asarray(pos) // P),
+    lambda pos, row, P: (np.asarray(row)[np.asarray(pos) // P], (np.asarray(pos) + 1) % P),
+    lambda pos, row, P: (np.asarray(row)[np.minimum(np.asarray(pos) // P + 1, len(row) - 1)],
+                         np.asarray(pos) % P),
+], ids=["page_row_swapped", "row_off_by_one", "next_page"])
+def test_planted_paging_mistakes_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(A, "paged_positions", mutant)
+    assert _caught()
