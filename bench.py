@@ -32,6 +32,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 METRIC = "decode-attention KV-read GB/s (% of HBM peak) and µs/step per layer"
 DEFAULT_WORKLOAD = "llama3_8b_gqa_t4096"
+SETTLE_S = 0.3  # seconds of untimed calls before the warmup (clock ramp-up)
 KERNEL_SOURCES = {"gqa": ["gqa_valu.hip", "gqa_mfma.hip", "visible.h", "device_common.h"],
                   "mla": ["mla_mfma.hip", "visible.h", "device_common.h"]}
 
@@ -47,6 +48,12 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--record-traffic", metavar="PMC_DIR",
+                    help="write profiles/traffic_<workload>.json from rocprofv3 "
+                         "--pmc FETCH_SIZE / WRITE_SIZE runs of this workload "
+                         "(PMC_DIR/{FETCH_SIZE,WRITE_SIZE}/run_counter_collection.csv) "
+                         "and of the --probe copy (--copy-dir)")
+    ap.add_argument("--copy-dir", default="gpurun_out/pmc/copy")
     ap.add_argument("--probe", action="store_true",
                     help="only run the HBM read probe and a 1 GiB plain copy")
     return ap.parse_args()
@@ -172,8 +179,130 @@ def run_probe(dev):
                       "copy_launches": 3}), flush=True)
 
 
+def _counter_kib_per_dispatch(csv_path, kernel_substr):
+    """Mean over dispatches of a kernel (name containing kernel_substr) of the
+    counter in a rocprofv3 counter_collection.csv, summed per dispatch."""
+    import csv
+    per = {}
+    name = None
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if kernel_substr in row["Kernel_Name"]:
+                per[row["Dispatch_Id"]] = per.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+                name = row["Counter_Name"]
+    if not per:
+        raise SystemExit(f"no dispatch of {kernel_substr} in {csv_path}")
+    return sum(per.values()) / len(per), name, len(per)
+
+
+def record_traffic(args):
+    """HBM bytes per launch of the workload's decode kernel from FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch), each scaled by what the same counter
+    reads for the 1 GiB plain copy of --probe, into
+    profiles/traffic_<workload>.json with a hash of the kernel sources."""
+    import synth
+    w = synth.workload(args.workload)
+    kind = "mla" if w["kind"] == "mla" else "gqa"
+    kern = "mla_decode_mfma" if kind == "mla" else "gqa_decode_"
+    d = args.record_traffic
+    fk, _, nf = _counter_kib_per_dispatch(os.path.join(d, "FETCH_SIZE", "run_counter_collection.csv"), kern)
+    wk, _, nw = _counter_kib_per_dispatch(os.path.join(d, "WRITE_SIZE", "run_counter_collection.csv"), kern)
+    cf, _, _ = _counter_kib_per_dispatch(os.path.join(args.copy_dir, "FETCH_SIZE", "run_counter_collection.csv"), "plain_copy")
+    cw, _, _ = _counter_kib_per_dispatch(os.path.join(args.copy_dir, "WRITE_SIZE", "run_counter_collection.csv"), "plain_copy")
+    copy_bytes = 1 << 30
+    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    if kind == "mla":
+        lens = workload_seq_lens(w)
+        Tsum = w["B"] * w["T_cap"] if lens is None else int(lens.clamp(0, w["T_cap"]).sum())
+        alg = Tsum * (w["d_c"] + w["d_rope"]) * 2
+    else:
+        s = 2 if w.get("dtype", "bf16") == "bf16" else 4
+        alg = int(2 * s * w["d"] * w["H_kv"] * int(visible_counts(w, workload_seq_lens(w)).sum()))
+    rec = {
+        "workload": w["name"], "kernel": kern + "*",
+        "kernel_source_hash": kernel_source_hash(kind),
+        "commands": [
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/FETCH_SIZE -o run -- "
+            f"python bench.py --workload {w['name']} --steps 3 --warmup 1 --no-cpu-baseline",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/WRITE_SIZE -o run -- "
+            f"python bench.py --workload {w['name']} --steps 3 --warmup 1 --no-cpu-baseline",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {args.copy_dir}/FETCH_SIZE -o run -- python bench.py --probe",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {args.copy_dir}/WRITE_SIZE -o run -- python bench.py --probe",
+        ],
+        "dispatches": [nf, nw],
+        "fetch_kib_per_dispatch_raw": round(fk, 1),
+        "write_kib_per_dispatch_raw": round(wk, 1),
+        "copy_calibration": {"bytes": copy_bytes, "fetch_kib_raw": round(cf, 1),
+                             "write_kib_raw": round(cw, 1), "fetch_scale": round(fs, 4),
+                             "write_scale": round(ws, 4)},
+        "read_bytes_per_launch": int(fk * 1024 * fs),
+        "write_bytes_per_launch": int(wk * 1024 * ws),
+        "bytes_per_launch": int(fk * 1024 * fs + wk * 1024 * ws),
+        "algorithmic_bytes_per_launch": alg,
+    }
+    path = os.path.join(ROOT, "profiles", f"traffic_{w['name']}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def workload_seq_lens(w):
+    """The workload's seq_lens on the CPU (None when every sequence is full),
+    drawn exactly as the input generator draws them."""
+    import torch
+
+    import synth
+    base = 1234 + 100 * w["index"]
+    if w.get("ragged"):
+        lo, hi = w["ragged"]
+        return synth.draw_ints(w["B"], lo, hi, base + 3)
+    if w.get("logical_len"):
+        return torch.full((w["B"],), w["logical_len"], dtype=torch.int32)
+    return None
+
+
+def run_timed(step, args, dev):
+    """Settle, warm up, then time exactly args.steps calls of step(i).
+
+    The settle phase runs the same step for at least SETTLE_S seconds before
+    the warmup, so the memory and core clocks have left their idle states
+    when the timed region starts.  Returns (ms per step over the whole timed
+    region, mean per-call ms from events around each call, settle steps)."""
+    import numpy as np
+    import torch
+
+    settle = 0
+    t_end = time.perf_counter() + SETTLE_S
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            step(settle)
+            settle += 1
+        torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    return ms, call_ms, settle
+
+
 def main():
     args = parse()
+    if args.record_traffic:
+        return record_traffic(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the path runs on a single GPU).", file=sys.stderr)
@@ -216,34 +345,16 @@ def main():
                           inp["ring_head"], inp["window"], inp["scale"],
                           args.num_splits, out=out, lse=lse, workspace=ws)
 
-    print(f"bench: {R} cache copies, {S} split(s); warmup {args.warmup}",
+    plan = L.attn_decode_gqa_plan(B, H_q, H_kv, T, d, dt_code, inp["window"], ring,
+                                  0, args.num_splits)
+    kernel = "gqa_decode_" + plan["kernel"]
+    print(f"bench: {R} cache copies, {S} split(s), {kernel}; warmup {args.warmup}",
           file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step(i)
-        ends[i].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    per_call = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
-    ms_per_step = total_ms / args.steps
-    call_ms = float(per_call.mean())
+    ms_per_step, call_ms, settle = run_timed(step, args, dev)
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (call_ms * 1e-3) / 1e9
-    print(f"bench: {ms_per_step * 1e3:.1f} us/step, call {call_ms * 1e3:.1f} us "
-          f"(median {np.median(per_call) * 1e3:.1f}), {value:.0f} GB/s",
-          file=sys.stderr, flush=True)
+    print(f"bench: {ms_per_step * 1e3:.1f} us/step, call {call_ms * 1e3:.1f} us, "
+          f"{value:.0f} GB/s (settled over {settle} steps)", file=sys.stderr, flush=True)
 
     res = {
         "metric": METRIC,
@@ -263,7 +374,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w["name"], "B": B, "H_q": H_q, "H_kv": H_kv,
                    "d": d, "T": T, "window": inp["window"], "ring": ring,
-                   "splits": S, "cache_copies": R,
+                   "splits": S, "cache_copies": R, "settle_steps": settle,
                    "kv_bytes_per_step": alg_bytes},
         "roofline": {
             "bound": "hbm",
@@ -272,7 +383,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_profile(w["name"]),
-            "kernel": "gqa_decode_valu" + ("" if S == 1 else " + lse_combine"),
+            "kernel": kernel + ("" if S == 1 else " + lse_combine"),
             "kernel_us": round(call_ms * 1e3, 2),
         },
     }
@@ -312,23 +423,7 @@ def bench_mla(args, w, dev):
                           inp["seq_lens"], args.num_splits, out=out, lse=lse,
                           workspace=ws)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step(i)
-        ends[i].record(stream)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
-    call_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    ms, call_ms, settle = run_timed(step, args, dev)
     value = alg_bytes / (ms * 1e-3) / 1e9
     tflops = flops / (call_ms * 1e-3) / 1e12
     res = {
@@ -340,6 +435,7 @@ def bench_mla(args, w, dev):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w["name"], "B": B, "H": H, "T": T, "d_c": w["d_c"],
                    "d_rope": w["d_rope"], "splits": S, "cache_copies": R,
+                   "settle_steps": settle,
                    "latent_bytes_per_step": alg_bytes, "flops_per_step": flops},
         "roofline": {"bound": "hbm", "achieved": round(alg_bytes / (call_ms * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",

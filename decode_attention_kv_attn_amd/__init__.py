@@ -23,6 +23,7 @@ __all__ = [
     "attn_decode_gqa_global", "attn_decode_gqa_global_splits",
     "attn_decode_gqa_global_workspace_bytes",
     "attn_decode_gqa_paged", "attn_decode_mla_paged", "attn_kv_append_paged",
+    "attn_decode_gqa_plan",
 ]
 
 ATTN_F32 = 0
@@ -47,6 +48,7 @@ _SIGS = {
                                    _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "attn_kv_append_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                                   _i, _i, _i, _vp]),
+    "attn_decode_gqa_plan": (_i, [_i] * 10 + [_vp]),
     "attn_decode_gqa_splits": (_i, [_i] * 9),
     "attn_decode_gqa_workspace_bytes": (_sz, [_i] * 9),
     "attn_decode_mla": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
@@ -130,6 +132,27 @@ def attn_decode_gqa_workspace_bytes(B, H_q, H_kv, T_cap, d, dtype, window=0,
                                     ring=False, num_splits=0):
     return library().attn_decode_gqa_workspace_bytes(
         B, H_q, H_kv, T_cap, d, dtype, window, int(bool(ring)), num_splits)
+
+
+class _GqaPlan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("splits", ctypes.c_int),
+                ("chunk", ctypes.c_int), ("heads_per_item", ctypes.c_int),
+                ("tile_rows", ctypes.c_int), ("waves", ctypes.c_int),
+                ("groups", ctypes.c_longlong)]
+
+
+def attn_decode_gqa_plan(B, H_q, H_kv, T_cap, d, dtype, window=0, ring=False,
+                         n_global=0, num_splits=0):
+    """How a GQA decode call would run: dict with kernel ("valu" / "mfma"),
+    splits, chunk, heads_per_item, tile_rows, waves, groups."""
+    p = _GqaPlan()
+    st = library().attn_decode_gqa_plan(B, H_q, H_kv, T_cap, d, dtype, window,
+                                        int(bool(ring)), n_global, num_splits,
+                                        ctypes.byref(p))
+    _check("attn_decode_gqa_plan", st)
+    return {"kernel": "mfma" if p.kernel else "valu", "splits": p.splits,
+            "chunk": p.chunk, "heads_per_item": p.heads_per_item,
+            "tile_rows": p.tile_rows, "waves": p.waves, "groups": p.groups}
 
 
 def attn_decode_workspace_bytes(B, H, d_v, num_splits):

@@ -35,6 +35,7 @@ struct GqaPlan {
   int S;            // splits
   int chunk;        // positions per split
   int waves;        // waves per work group
+  int tile_rows;    // positions per wave per tile
   size_t ws_bytes;  // workspace needed
 };
 
@@ -104,6 +105,7 @@ int plan_gqa(int B, int H_q, int H_kv, int T_cap, int d, int dtype, int window,
   p->N = geo.heads_per_item;
   p->head_chunks = (n + geo.heads_per_item - 1) / geo.heads_per_item;
   p->waves = geo.waves;
+  p->tile_rows = geo.tile_rows;
   const int mv = max_visible(T_cap, window, ring, n_global);
   long long S;
   if (num_splits > 0) {
@@ -145,6 +147,24 @@ int attn_decode_gqa_splits(int B, int H_q, int H_kv, int T_cap, int d,
   const int st = plan_gqa(B, H_q, H_kv, T_cap, d, dtype, window, ring, 0,
                           num_splits, &p);
   return st == ATTN_OK ? p.S : st;
+}
+
+int attn_decode_gqa_plan(int B, int H_q, int H_kv, int T_cap, int d, int dtype,
+                         int window, int ring, int n_global, int num_splits,
+                         attn_gqa_plan* plan) {
+  if (!plan) return ATTN_ERR_NULL;
+  GqaPlan p;
+  const int st = plan_gqa(B, H_q, H_kv, T_cap, d, dtype, window, ring ? 1 : 0,
+                          n_global, num_splits, &p);
+  if (st != ATTN_OK) return st;
+  plan->kernel = p.mfma;
+  plan->splits = p.S;
+  plan->chunk = p.chunk;
+  plan->heads_per_item = p.N;
+  plan->tile_rows = p.tile_rows;
+  plan->waves = p.waves;
+  plan->groups = (long long)B * H_kv * p.head_chunks * p.S;
+  return ATTN_OK;
 }
 
 int attn_decode_gqa_global_splits(int B, int H_q, int H_kv, int T_cap, int d,

@@ -1,11 +1,14 @@
-// Decode attention on the matrix cores for large head groups (MQA-like).
+// Decode attention on the matrix cores for head groups of 3 or more (GQA
+// through MQA).
 //
-// When many query heads share one KV head (H_q/H_kv >= 9; MQA at 32 heads is
-// the extreme: xuesongtap "attention-head" note, section 2.1), every K and V
-// row serves all of them, and the scores of a tile are a dense product
-// [tokens x d] . [d x heads].  The vector ALUs cannot keep up with HBM there
-// (32 flop/byte at 32 heads), so both products run on MFMA 16x16x32 (bf16 in,
-// fp32 accumulate):
+// When several query heads share one KV head (xuesongtap "attention-head"
+// note, sections 2.1-2.2; MQA at 32 heads is the extreme), every K and V row
+// serves all of them, and the scores of a tile are a dense product
+// [tokens x d] . [d x heads].  The vector ALUs fall behind HBM from about
+// six heads per row on (2n flop per K/V element), and even at four the
+// matrix cores free the vector units for the softmax, so both products run
+// on MFMA 16x16x32 (bf16 in, fp32 accumulate), with the head block padded
+// to 16 or 32 columns:
 //
 //   S^T[tokens, heads] = K_tile[tokens, d] . Q^T[d, heads]
 //       A = K rows straight from HBM (each lane's 8 elements are 16
@@ -29,6 +32,8 @@
 // The addressing mode (dense linear/ring, global positions, paged) is a
 // template parameter; on a paged cache each wave fetches the page ids of
 // its next tile with one vector load a tile ahead of the row loads.
+
+#include <stdlib.h>
 
 #include "device_common.h"
 #include "internal.h"
@@ -409,7 +414,14 @@ hipError_t launch_mode(const GqaArgs& a, int d, int heads_per_item, int grid,
 // does not apply (float32 data, d = 256, or groups small enough for the
 // vector kernel).
 int mfma_heads_per_item(int dtype, int d, int n) {
-  if (dtype != 1 || n < 9) return 0;
+  // smallest group sent to the matrix cores (overridable for tuning sweeps
+  // through ATTN_DECODE_MFMA_MIN_GROUP)
+  static const int min_group = [] {
+    const char* e = getenv("ATTN_DECODE_MFMA_MIN_GROUP");
+    const int x = e ? atoi(e) : 0;
+    return x > 0 ? x : 3;
+  }();
+  if (dtype != 1 || n < min_group) return 0;
   if (d != 64 && d != 128) return 0;
   const int r = (n + 15) / 16 * 16;
   return r < 32 ? r : 32;

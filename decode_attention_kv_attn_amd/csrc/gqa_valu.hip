@@ -40,6 +40,9 @@
 #ifndef ATTN_VALU_TILE_BYTES
 #define ATTN_VALU_TILE_BYTES 8192
 #endif
+#ifndef ATTN_VALU_TILE_BYTES_WIDE  // per-wave tile bytes when N >= 7
+#define ATTN_VALU_TILE_BYTES_WIDE 4096
+#endif
 #ifndef ATTN_VALU_E_SMALL  // elements per lane per row when N <= 4
 #define ATTN_VALU_E_SMALL 16
 #endif
@@ -121,7 +124,8 @@ struct Cfg {
   static constexpr int CPL = E / EPC;          // chunks per lane per row
   static constexpr int LPR = D / E;            // lanes per row
   static constexpr int RPI = 64 / LPR;         // rows per load instruction
-  static constexpr int TR_BYTES = ATTN_VALU_TILE_BYTES;  // K+V per wave per tile
+  static constexpr int TR_BYTES =  // K+V per wave per tile
+      N >= 7 ? ATTN_VALU_TILE_BYTES_WIDE : ATTN_VALU_TILE_BYTES;
   static constexpr int TR0 = TR_BYTES / (2 * D * (int)sizeof(T));
   static constexpr int TR = TR0 > RPI ? TR0 : RPI;  // rows per tile
   static constexpr int RPL = TR / RPI;              // rows per lane per tile

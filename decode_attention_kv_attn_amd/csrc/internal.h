@@ -54,7 +54,7 @@ hipError_t launch_gqa_valu_global(const GqaArgs& a, int dtype, int d, int grid,
 hipError_t launch_gqa_valu_paged(const GqaArgs& a, int dtype, int d, int grid,
                                  hipStream_t stream);
 
-// Matrix-core path for large groups (bf16).
+// Matrix-core path for bf16 groups of 3 or more heads, d in {64, 128}.
 int mfma_heads_per_item(int dtype, int d, int n);
 int mfma_tile_rows();
 int mfma_waves();

@@ -126,6 +126,26 @@ size_t attn_decode_gqa_workspace_bytes(int B, int H_q, int H_kv, int T_cap,
                                        int d, int dtype, int window, int ring,
                                        int num_splits);
 
+/* How attn_decode_gqa (and its _global / _paged forms) would run a call:
+ * which kernel, how the visible range is split, the launch shape. */
+typedef struct {
+  int kernel;          /* 0 = vector-ALU kernel, 1 = matrix-core kernel      */
+  int splits;          /* pieces of each visible range (1 = no combine pass) */
+  int chunk;           /* positions per piece                                */
+  int heads_per_item;  /* query heads one work group serves                  */
+  int tile_rows;       /* positions per wave per tile                        */
+  int waves;           /* waves per work group                               */
+  long long groups;    /* work groups of the decode kernel                   */
+} attn_gqa_plan;
+
+/* Fills *plan for these arguments (n_global as for attn_decode_gqa_global,
+ * 0 otherwise; a paged call plans as T_cap = max_pages * page_size, ring 0).
+ * Returns ATTN_OK or the status the decode call would return for the shape
+ * arguments; plan must not be NULL (ATTN_ERR_NULL). */
+int attn_decode_gqa_plan(int B, int H_q, int H_kv, int T_cap, int d, int dtype,
+                         int window, int ring, int n_global, int num_splits,
+                         attn_gqa_plan* plan);
+
 /* Largest accepted n_global. */
 #define ATTN_MAX_GLOBAL 65536
 
