@@ -23,7 +23,7 @@ __all__ = [
     "attn_decode_gqa_global", "attn_decode_gqa_global_splits",
     "attn_decode_gqa_global_workspace_bytes",
     "attn_decode_gqa_paged", "attn_decode_mla_paged", "attn_kv_append_paged",
-    "attn_decode_gqa_plan",
+    "attn_decode_gqa_plan", "attn_decode_gqa_multi", "attn_decode_mla_multi",
 ]
 
 ATTN_F32 = 0
@@ -43,12 +43,17 @@ _SIGS = {
     "attn_decode_gqa_global_splits": (_i, [_i] * 9),
     "attn_decode_gqa_global_workspace_bytes": (_sz, [_i] * 9),
     "attn_decode_gqa_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
-                                   _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+                                   _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz,
+                                   _vp]),
     "attn_decode_mla_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
-                                   _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+                                   _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "attn_decode_gqa_multi": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                                   _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "attn_decode_mla_multi": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                   _i, _f, _i, _vp, _sz, _vp]),
     "attn_kv_append_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                                   _i, _i, _i, _vp]),
-    "attn_decode_gqa_plan": (_i, [_i] * 10 + [_vp]),
+    "attn_decode_gqa_plan": (_i, [_i] * 11 + [_vp]),
     "attn_decode_gqa_splits": (_i, [_i] * 9),
     "attn_decode_gqa_workspace_bytes": (_sz, [_i] * 9),
     "attn_decode_mla": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
@@ -138,21 +143,22 @@ class _GqaPlan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("splits", ctypes.c_int),
                 ("chunk", ctypes.c_int), ("heads_per_item", ctypes.c_int),
                 ("tile_rows", ctypes.c_int), ("waves", ctypes.c_int),
-                ("groups", ctypes.c_longlong)]
+                ("groups", ctypes.c_longlong), ("workspace_bytes", ctypes.c_size_t)]
 
 
 def attn_decode_gqa_plan(B, H_q, H_kv, T_cap, d, dtype, window=0, ring=False,
-                         n_global=0, num_splits=0):
+                         n_global=0, num_splits=0, q_len=1):
     """How a GQA decode call would run: dict with kernel ("valu" / "mfma"),
-    splits, chunk, heads_per_item, tile_rows, waves, groups."""
+    splits, chunk, heads_per_item, tile_rows, waves, groups, workspace_bytes."""
     p = _GqaPlan()
-    st = library().attn_decode_gqa_plan(B, H_q, H_kv, T_cap, d, dtype, window,
-                                        int(bool(ring)), n_global, num_splits,
-                                        ctypes.byref(p))
+    st = library().attn_decode_gqa_plan(B, q_len, H_q, H_kv, T_cap, d, dtype,
+                                        window, int(bool(ring)), n_global,
+                                        num_splits, ctypes.byref(p))
     _check("attn_decode_gqa_plan", st)
     return {"kernel": "mfma" if p.kernel else "valu", "splits": p.splits,
             "chunk": p.chunk, "heads_per_item": p.heads_per_item,
-            "tile_rows": p.tile_rows, "waves": p.waves, "groups": p.groups}
+            "tile_rows": p.tile_rows, "waves": p.waves, "groups": p.groups,
+            "workspace_bytes": p.workspace_bytes}
 
 
 def attn_decode_workspace_bytes(B, H, d_v, num_splits):
@@ -332,33 +338,69 @@ def attn_kv_append_ring(k_cache, k_new, ring_head, v_cache=None, v_new=None,
     _check("attn_kv_append_ring", st)
 
 
+def _gqa_plan_bytes(B, L, H_q, H_kv, T_cap, d, dt, window, ring, num_splits):
+    try:
+        return attn_decode_gqa_plan(B, H_q, H_kv, T_cap, d, dt, window, ring, 0,
+                                    num_splits, L)["workspace_bytes"]
+    except AttnError:
+        return 0  # invalid arguments: the call itself reports the status
+
+
 def attn_decode_gqa_paged(q, k_pages, v_pages, block_table, seq_lens=None,
                           window=0, scale=None, num_splits=0, out=None, lse=None,
                           workspace=None, want_lse=True, stream=None):
     """Decode over a paged K/V pool: k_pages / v_pages [num_pages, H_kv, P,
-    d], block_table int32 [B, max_pages].  Returns ``(out, lse)`` as
-    :func:`attn_decode_gqa`."""
+    d], block_table int32 [B, max_pages]; q [B, H_q, d] (one token) or
+    [B, L, H_q, d] (L tokens per sequence).  Returns ``(out, lse)`` shaped
+    like q (float32) and q without its last dim."""
     _need_dev(q, k_pages, v_pages, block_table, seq_lens, out, lse)
-    B, H_q, d = q.shape
+    lead = q.shape[:-2]
+    B, L = (q.shape[0], 1) if q.dim() == 3 else (q.shape[0], q.shape[1])
+    H_q, d = q.shape[-2], q.shape[-1]
     num_pages, H_kv, P, _ = k_pages.shape
     max_pages = block_table.shape[1]
     dt = _dtype_code(q)
     if out is None:
-        out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
+        out = torch.empty((*lead, H_q, d), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
-        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
-    nbytes = attn_decode_gqa_workspace_bytes(B, H_q, H_kv, max_pages * P, d, dt,
-                                             window, False, num_splits)
-    if nbytes == 2**64 - 1:
-        nbytes = 0
+        lse = torch.empty((*lead, H_q), dtype=torch.float32, device=q.device)
+    nbytes = _gqa_plan_bytes(B, L, H_q, H_kv, max_pages * P, d, dt, window, False,
+                             num_splits)
     workspace = _workspace(nbytes, q.device, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = library().attn_decode_gqa_paged(
         _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(out), _ptr(lse),
-        _ptr(seq_lens), _ptr(block_table), max_pages, B, H_q, H_kv, num_pages, P,
-        d, dt, window, 0.0 if scale is None else float(scale), num_splits,
+        _ptr(seq_lens), _ptr(block_table), max_pages, B, L, H_q, H_kv, num_pages,
+        P, d, dt, window, 0.0 if scale is None else float(scale), num_splits,
         _ptr(workspace), ws_bytes, _stream(stream, q.device))
     _check("attn_decode_gqa_paged", st)
+    return out, lse
+
+
+def attn_decode_gqa_multi(q, k, v, seq_lens=None, ring_head=None, window=0,
+                          scale=None, num_splits=0, out=None, lse=None,
+                          workspace=None, want_lse=True, stream=None):
+    """L query tokens per sequence: q [B, L, H_q, d] (the last L positions of
+    each cache), k / v [B, H_kv, T_cap, d].  Returns ``(out [B, L, H_q, d],
+    lse [B, L, H_q])`` float32."""
+    _need_dev(q, k, v, seq_lens, ring_head, out, lse)
+    B, L, H_q, d = q.shape
+    _, H_kv, T_cap, _ = k.shape
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, L, H_q, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, L, H_q), dtype=torch.float32, device=q.device)
+    nbytes = _gqa_plan_bytes(B, L, H_q, H_kv, T_cap, d, dt, window,
+                             ring_head is not None, num_splits)
+    workspace = _workspace(nbytes, q.device, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = library().attn_decode_gqa_multi(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seq_lens),
+        _ptr(ring_head), B, L, H_q, H_kv, T_cap, d, dt, window,
+        0.0 if scale is None else float(scale), num_splits, _ptr(workspace),
+        ws_bytes, _stream(stream, q.device))
+    _check("attn_decode_gqa_multi", st)
     return out, lse
 
 
@@ -366,17 +408,20 @@ def attn_decode_mla_paged(q, latent_pages, block_table, d_c, scale,
                           seq_lens=None, num_splits=0, out=None, lse=None,
                           workspace=None, want_lse=True, stream=None):
     """Absorbed MLA over a paged latent pool [num_pages, P, d_c+d_rope]
-    (bfloat16) with block_table int32 [B, max_pages]."""
+    (bfloat16) with block_table int32 [B, max_pages]; q [B, H, d_c+d_rope]
+    or [B, L, H, d_c+d_rope] (L tokens per sequence)."""
     _need_dev(q, latent_pages, block_table, seq_lens, out, lse)
-    B, H, dk = q.shape
+    lead = q.shape[:-2]
+    B, L = (q.shape[0], 1) if q.dim() == 3 else (q.shape[0], q.shape[1])
+    H, dk = q.shape[-2], q.shape[-1]
     num_pages, P, _ = latent_pages.shape
     max_pages = block_table.shape[1]
     d_rope = dk - d_c
     if out is None:
-        out = torch.empty((B, H, d_c), dtype=torch.float32, device=q.device)
+        out = torch.empty((*lead, H, d_c), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    nbytes = attn_decode_mla_workspace_bytes(B, H, max_pages * P, d_c, d_rope,
+        lse = torch.empty((*lead, H), dtype=torch.float32, device=q.device)
+    nbytes = attn_decode_mla_workspace_bytes(B, H * L, max_pages * P, d_c, d_rope,
                                              num_splits)
     if nbytes == 2**64 - 1:
         nbytes = 0
@@ -384,10 +429,37 @@ def attn_decode_mla_paged(q, latent_pages, block_table, d_c, scale,
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = library().attn_decode_mla_paged(
         _ptr(q), _ptr(latent_pages), _ptr(out), _ptr(lse), _ptr(seq_lens),
-        _ptr(block_table), max_pages, B, H, num_pages, P, d_c, d_rope,
+        _ptr(block_table), max_pages, B, L, H, num_pages, P, d_c, d_rope,
         float(scale), num_splits, _ptr(workspace), ws_bytes,
         _stream(stream, q.device))
     _check("attn_decode_mla_paged", st)
+    return out, lse
+
+
+def attn_decode_mla_multi(q, latent, d_c, scale, seq_lens=None, num_splits=0,
+                          out=None, lse=None, workspace=None, want_lse=True,
+                          stream=None):
+    """Absorbed MLA with L query tokens per sequence: q [B, L, H,
+    d_c+d_rope], latent [B, T_cap, d_c+d_rope] (bfloat16).  Returns
+    ``(z [B, L, H, d_c], lse [B, L, H])`` float32."""
+    _need_dev(q, latent, seq_lens, out, lse)
+    B, L, H, dk = q.shape
+    _, T_cap, _ = latent.shape
+    d_rope = dk - d_c
+    if out is None:
+        out = torch.empty((B, L, H, d_c), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, L, H), dtype=torch.float32, device=q.device)
+    nbytes = attn_decode_mla_workspace_bytes(B, H * L, T_cap, d_c, d_rope, num_splits)
+    if nbytes == 2**64 - 1:
+        nbytes = 0
+    workspace = _workspace(nbytes, q.device, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = library().attn_decode_mla_multi(
+        _ptr(q), _ptr(latent), _ptr(out), _ptr(lse), _ptr(seq_lens), B, L, H,
+        T_cap, d_c, d_rope, float(scale), num_splits, _ptr(workspace), ws_bytes,
+        _stream(stream, q.device))
+    _check("attn_decode_mla_multi", st)
     return out, lse
 
 

@@ -149,12 +149,17 @@ int attn_decode_gqa_splits(int B, int H_q, int H_kv, int T_cap, int d,
   return st == ATTN_OK ? p.S : st;
 }
 
-int attn_decode_gqa_plan(int B, int H_q, int H_kv, int T_cap, int d, int dtype,
-                         int window, int ring, int n_global, int num_splits,
-                         attn_gqa_plan* plan) {
+int attn_decode_gqa_plan(int B, int q_len, int H_q, int H_kv, int T_cap, int d,
+                         int dtype, int window, int ring, int n_global,
+                         int num_splits, attn_gqa_plan* plan) {
   if (!plan) return ATTN_ERR_NULL;
+  if (q_len < 1 || q_len > ATTN_MAX_QLEN) return ATTN_ERR_ARG;
+  if (q_len > 1 && n_global > 0) return ATTN_ERR_UNSUPPORTED;
+  if (H_q > 0 && (long long)H_q * q_len > (1 << 30)) return ATTN_ERR_SHAPE;
+  if (window < 0) return ATTN_ERR_WINDOW;
   GqaPlan p;
-  const int st = plan_gqa(B, H_q, H_kv, T_cap, d, dtype, window, ring ? 1 : 0,
+  const int st = plan_gqa(B, H_q * q_len, H_kv, T_cap, d, dtype,
+                          window > 0 ? window + q_len - 1 : 0, ring ? 1 : 0,
                           n_global, num_splits, &p);
   if (st != ATTN_OK) return st;
   plan->kernel = p.mfma;
@@ -164,6 +169,7 @@ int attn_decode_gqa_plan(int B, int H_q, int H_kv, int T_cap, int d, int dtype,
   plan->tile_rows = p.tile_rows;
   plan->waves = p.waves;
   plan->groups = (long long)B * H_kv * p.head_chunks * p.S;
+  plan->workspace_bytes = p.ws_bytes;
   return ATTN_OK;
 }
 
@@ -208,15 +214,23 @@ struct PagedArgs {
 };
 
 // Shared body of the GQA entry points.
+// L query tokens per sequence plan as H_q * L query heads (the (head,
+// token) columns of a KV head) whose visible range is widened by L - 1
+// positions for the earlier tokens' windows.
 int decode_gqa(const void* q, const void* k, const void* v, float* out,
                float* lse_out, const int32_t* seq_lens, const int32_t* ring_head,
-               const int32_t* gpos, int n_global, PagedArgs pg, int B, int H_q,
-               int H_kv, int T_cap, int d, int dtype, int window, float scale,
-               int num_splits, void* workspace, size_t workspace_bytes,
-               void* stream) {
+               const int32_t* gpos, int n_global, PagedArgs pg, int B, int L,
+               int H_q, int H_kv, int T_cap, int d, int dtype, int window,
+               float scale, int num_splits, void* workspace,
+               size_t workspace_bytes, void* stream) {
   const int ring = ring_head != nullptr;
+  if (L < 1 || L > ATTN_MAX_QLEN) return ATTN_ERR_ARG;
+  if (L > 1 && n_global > 0) return ATTN_ERR_UNSUPPORTED;
+  if (H_q > 0 && (long long)H_q * L > (1 << 30)) return ATTN_ERR_SHAPE;
+  if (window < 0) return ATTN_ERR_WINDOW;
+  const int wrange = window > 0 ? window + L - 1 : 0;
   GqaPlan p;
-  int st = plan_gqa(B, H_q, H_kv, T_cap, d, dtype, window, ring, n_global,
+  int st = plan_gqa(B, H_q * L, H_kv, T_cap, d, dtype, wrange, ring, n_global,
                     num_splits, &p);
   if (st != ATTN_OK) return st;
   if (B == 0) return ATTN_OK;  // empty batch: nothing to read or write
@@ -252,8 +266,11 @@ int decode_gqa(const void* q, const void* k, const void* v, float* out,
   a.H_q = H_q;
   a.H_kv = H_kv;
   a.T_cap = T_cap;
-  a.window = window;
+  a.window = wrange;
+  a.L = L;
+  a.wtok = window;
   a.n = H_q / H_kv;
+  a.ncol = a.n * L;
   a.head_chunks = p.head_chunks;
   a.S = p.S;
   a.chunk = p.chunk;
@@ -261,7 +278,7 @@ int decode_gqa(const void* q, const void* k, const void* v, float* out,
   a.o_part = nullptr;
   a.lse_part = nullptr;
   if (p.S > 1) {
-    const size_t rows = (size_t)B * H_q * p.S;
+    const size_t rows = (size_t)B * L * H_q * p.S;
     a.o_part = (float*)workspace;
     a.lse_part = (float*)((char*)workspace + round_up(rows * d * sizeof(float), 256));
   }
@@ -273,7 +290,7 @@ int decode_gqa(const void* q, const void* k, const void* v, float* out,
                               : launch_gqa_valu(a, dtype, d, (int)grid, s);
   if (e != hipSuccess) return ATTN_ERR_HIP;
   if (p.S > 1) {
-    if (launch_combine(a.o_part, a.lse_part, out, lse_out, B, H_q, p.S, d, s) !=
+    if (launch_combine(a.o_part, a.lse_part, out, lse_out, B * L, H_q, p.S, d, s) !=
         hipSuccess)
       return ATTN_ERR_HIP;
   }
@@ -292,8 +309,20 @@ int attn_decode_gqa(const void* q, const void* k, const void* v, float* out,
                     int num_splits, void* workspace, size_t workspace_bytes,
                     void* stream) {
   return decode_gqa(q, k, v, out, lse_out, seq_lens, ring_head, nullptr, 0,
-                    PagedArgs{nullptr, 0, 0, 0}, B, H_q, H_kv, T_cap, d, dtype,
+                    PagedArgs{nullptr, 0, 0, 0}, B, 1, H_q, H_kv, T_cap, d, dtype,
                     window, scale, num_splits, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_gqa_multi(const void* q, const void* k, const void* v,
+                          float* out, float* lse_out, const int32_t* seq_lens,
+                          const int32_t* ring_head, int B, int q_len, int H_q,
+                          int H_kv, int T_cap, int d, int dtype, int window,
+                          float scale, int num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return decode_gqa(q, k, v, out, lse_out, seq_lens, ring_head, nullptr, 0,
+                    PagedArgs{nullptr, 0, 0, 0}, B, q_len, H_q, H_kv, T_cap, d,
+                    dtype, window, scale, num_splits, workspace, workspace_bytes,
+                    stream);
 }
 
 int attn_decode_gqa_global(const void* q, const void* k, const void* v,
@@ -304,26 +333,26 @@ int attn_decode_gqa_global(const void* q, const void* k, const void* v,
                            void* workspace, size_t workspace_bytes,
                            void* stream) {
   return decode_gqa(q, k, v, out, lse_out, seq_lens, nullptr, global_pos,
-                    n_global, PagedArgs{nullptr, 0, 0, 0}, B, H_q, H_kv, T_cap, d,
-                    dtype, window, scale, num_splits, workspace, workspace_bytes,
+                    n_global, PagedArgs{nullptr, 0, 0, 0}, B, 1, H_q, H_kv, T_cap,
+                    d, dtype, window, scale, num_splits, workspace, workspace_bytes,
                     stream);
 }
 
 int attn_decode_gqa_paged(const void* q, const void* k_pages,
                           const void* v_pages, float* out, float* lse_out,
                           const int32_t* seq_lens, const int32_t* block_table,
-                          int max_pages, int B, int H_q, int H_kv, int num_pages,
-                          int page_size, int d, int dtype, int window,
-                          float scale, int num_splits, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          int max_pages, int B, int q_len, int H_q, int H_kv,
+                          int num_pages, int page_size, int d, int dtype,
+                          int window, float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream) {
   int shift = 0;
   const int st = attn_check_pages(max_pages, num_pages, page_size, H_kv, &shift);
   if (st != ATTN_OK) return st;
   if (B > 0 && !block_table) return ATTN_ERR_NULL;
   if (block_table && !aligned(block_table, 4)) return ATTN_ERR_ALIGN;
   return decode_gqa(q, k_pages, v_pages, out, lse_out, seq_lens, nullptr, nullptr,
-                    0, PagedArgs{block_table, max_pages, shift, num_pages}, B, H_q,
-                    H_kv, max_pages * page_size, d, dtype, window, scale,
+                    0, PagedArgs{block_table, max_pages, shift, num_pages}, B, q_len,
+                    H_q, H_kv, max_pages * page_size, d, dtype, window, scale,
                     num_splits, workspace, workspace_bytes, stream);
 }
 

@@ -33,6 +33,7 @@
 // template parameter; on a paged cache each wave fetches the page ids of
 // its next tile with one vector load a tile ahead of the row loads.
 
+#include <limits.h>
 #include <stdlib.h>
 
 #include "device_common.h"
@@ -126,8 +127,8 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   const bool ring = MODE == kAddrDense && a.ring_head != nullptr;
   int p0, p1;  // this split's virtual rows
   split_range(vr, s, a.S, a.chunk, p0, p1);
-  const int h0 = g * a.n + hc * NH;
-  const int nh = min(NH, a.n - hc * NH);
+  const int c0 = hc * NH;                // first column (head, token) served
+  const int nh = min(NH, a.ncol - c0);   // columns actually present
 
   Pages pg{};
   if constexpr (MODE == kAddrPaged)
@@ -143,15 +144,16 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   // Q^T fragments: head li of block hb, elements 32*ks + 8*lg .. +7.
   uint4 qf[HB][KS];
   {
-    const uint16_t* qb = (const uint16_t*)a.q + ((size_t)b * a.H_q + h0) * D;
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
+    for (int hb = 0; hb < HB; ++hb) {
+      const int h = hb * 16 + li;
+      const uint16_t* qh = (const uint16_t*)a.q +
+                           query_row(b, g, min(c0 + h, a.ncol - 1), a.n, a.L, a.H_q) * D;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int h = hb * 16 + li;
-        qf[hb][ks] = h < nh ? *(const uint4*)(qb + (size_t)h * D + 32 * ks + 8 * lg)
+      for (int ks = 0; ks < KS; ++ks)
+        qf[hb][ks] = h < nh ? *(const uint4*)(qh + 32 * ks + 8 * lg)
                             : make_uint4(0, 0, 0, 0);
-      }
+    }
   }
 
   f32x4_t o[DB][HB];  // O^T blocks: d rows 16*db + 4*lg + r, head column li
@@ -167,6 +169,16 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   unsigned char* vt = smem + wave * C::VT_BYTES;
   const int span = p1 - p0;
   const int ntiles = span > 0 ? (span + kTT - 1) / kTT : 0;
+
+  // Several tokens: this lane's column of head block hb sees positions
+  // tw[hb] .. tl[hb] only (unused when L == 1).
+  const bool multi = a.L > 1;
+  int tl[HB], tw[HB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    tl[hb] = vr.hi - a.L + (c0 + hb * 16 + li) % a.L;
+    tw[hb] = a.wtok > 0 ? tl[hb] - a.wtok + 1 : INT_MIN;
+  }
 
   // Cache row (from the K/V base) of row t of the tile at virtual row
   // `base`; rows past the split re-read the tile's first row.
@@ -253,6 +265,13 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           x[4 * tb + r] = valid[tb][r] ? sc[tb][hb][r] * a.scale_log2 : neg_inf();
+      if (multi) {  // uniform: each column's causal limit and window
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int pos = vr.lo + base + 16 * (j >> 2) + 4 * lg + (j & 3);
+          if (pos > tl[hb] || pos < tw[hb]) x[j] = neg_inf();
+        }
+      }
       float mt = x[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
@@ -378,7 +397,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
     const bool empty = !(L > 0.f);
     const float ov = empty ? 0.f : O / L;
     const float lse = empty ? neg_inf() : (M + fast_log2(L)) * kLn2;
-    const size_t row = (size_t)b * a.H_q + h0 + h;
+    const size_t row = query_row(b, g, c0 + h, a.n, a.L, a.H_q);
     if (a.S == 1) {
       a.out[row * D + e] = ov;
       if (e == 0 && a.lse) a.lse[row] = lse;

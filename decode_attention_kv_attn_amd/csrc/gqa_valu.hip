@@ -32,6 +32,8 @@
 // cache the page ids of a wave's next tile are fetched with one vector load
 // a tile ahead, so the row addresses never wait on the block table.
 
+#include <limits.h>
+
 #include "device_common.h"
 #include "internal.h"
 #include "visible.h"
@@ -200,8 +202,8 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
   const bool ring = MODE == kAddrDense && a.ring_head != nullptr;
   int p0, p1;  // this split's virtual rows
   split_range(vr, s, a.S, a.chunk, p0, p1);
-  const int h0 = g * a.n + hc * N;       // first query head served
-  const int nh = min(N, a.n - hc * N);   // heads actually present
+  const int c0 = hc * N;                   // first column (head, token) served
+  const int nh = min(N, a.ncol - c0);      // columns actually present
 
   Pages pg{};
   if constexpr (MODE == kAddrPaged)
@@ -218,13 +220,15 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
   // ---- query chunks for this lane's elements ------------------------------
   uint4 qr[N][CPL];
   {
-    const T* qb = (const T*)a.q + ((size_t)b * a.H_q + h0) * D;
 #pragma unroll
-    for (int h = 0; h < N; ++h)
+    for (int h = 0; h < N; ++h) {
+      const T* qh = (const T*)a.q +
+                    query_row(b, g, min(c0 + h, a.ncol - 1), a.n, a.L, a.H_q) * D;
 #pragma unroll
       for (int k = 0; k < CPL; ++k)
-        qr[h][k] = (h < nh) ? *(const uint4*)(qb + h * D + (cl + k * LPR) * EPC)
+        qr[h][k] = (h < nh) ? *(const uint4*)(qh + (cl + k * LPR) * EPC)
                             : make_uint4(0, 0, 0, 0);
+    }
   }
 
   float m[N], l[N], acc[N][E];
@@ -238,6 +242,16 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
 
   const int span = p1 - p0;
   const int ntiles = span > 0 ? (span + TR - 1) / TR : 0;
+
+  // Several tokens: column h sees positions tl[h] - wtok + 1 .. tl[h] only
+  // (uniform per column; unused when L == 1).
+  const bool multi = a.L > 1;
+  int tl[N], tw[N];
+#pragma unroll
+  for (int h = 0; h < N; ++h) {
+    tl[h] = vr.hi - a.L + (c0 + h) % a.L;
+    tw[h] = a.wtok > 0 ? tl[h] - a.wtok + 1 : INT_MIN;
+  }
 
   // Cache row (from the K/V base) of virtual row vi of the tile at `base`;
   // `pid` holds that tile's page ids on a paged cache.
@@ -311,6 +325,15 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
         const float x = group_sum<LPR>(sc[i][h]) * a.scale_log2;
         sc[i][h] = valid[i] ? x : neg_inf();
       }
+    if (multi) {  // uniform: causal limit and window of each token's column
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) {
+        const int pos = vr.lo + base + rg + i * RPI;
+#pragma unroll
+        for (int h = 0; h < N; ++h)
+          if (pos > tl[h] || pos < tw[h]) sc[i][h] = neg_inf();
+      }
+    }
 
     // lazy maximum
 #pragma unroll
@@ -335,7 +358,8 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
       for (int k = 0; k < CPL; ++k) ET::unpack(vv[i][k], vf[k]);
 #pragma unroll
       for (int h = 0; h < N; ++h) {
-        const float p = valid[i] ? fast_exp2(sc[i][h] - m[h]) : 0.f;
+        // masked entries (-inf) weigh 0, also while m is still -inf
+        const float p = sc[i][h] == neg_inf() ? 0.f : fast_exp2(sc[i][h] - m[h]);
         l[h] += p;
 #pragma unroll
         for (int k = 0; k < CPL; ++k)
@@ -420,7 +444,7 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
     const bool empty = !(L > 0.f);
     const float o = empty ? 0.f : O / L;
     const float lse = empty ? neg_inf() : (M + fast_log2(L)) * kLn2;
-    const size_t row = (size_t)b * a.H_q + h0 + h;
+    const size_t row = query_row(b, g, c0 + h, a.n, a.L, a.H_q);
     if (a.S == 1) {
       a.out[row * D + e] = o;
       if (e == 0 && a.lse) a.lse[row] = lse;
@@ -454,7 +478,7 @@ hipError_t launch_d(const GqaArgs& a, int N, int grid, hipStream_t st) {
 }
 
 hipError_t launch_mode(const GqaArgs& a, int dtype, int d, int grid, hipStream_t st) {
-  const int N = a.n <= 8 ? a.n : 8;
+  const int N = a.ncol <= 8 ? a.ncol : 8;
   if (dtype == 0) {
     if (d == 64) return launch_d<float, 64>(a, N, grid, st);
     if (d == 128) return launch_d<float, 128>(a, N, grid, st);

@@ -25,8 +25,12 @@ struct GqaArgs {
   int n_global;
   const int32_t* block_table;  // paged cache: [B, max_pages], else nullptr
   int max_pages, page_shift, num_pages;
-  int B, H_q, H_kv, T_cap, window;  // paged: T_cap = max_pages << page_shift
+  int B, H_q, H_kv, T_cap;  // paged: T_cap = max_pages << page_shift
+  int window;       // visible-range window: w + L - 1 (0 = none)
+  int L;            // query tokens per sequence (the last L positions)
+  int wtok;         // each token's own window w (0 = none)
   int n;            // query heads per KV head
+  int ncol;         // columns per KV head: n * L (head, token) pairs
   int head_chunks;  // work items per KV head along the query heads
   int S;            // splits of the visible range
   int chunk;        // positions per split
@@ -64,6 +68,7 @@ hipError_t launch_gqa_mfma(const GqaArgs& a, int d, int heads_per_item, int grid
 // Absorbed MLA on the matrix cores (bf16, d_c = 512, d_rope = 64).
 int mla_heads_per_group();
 int mla_tile_rows();
+// L query tokens per sequence (q [B, L, H, 576], outputs [B, L, H, ...]);
 // block_table == nullptr: dense latent [B, T_cap, 576]; else a page pool
 // [num_pages, 2^page_shift, 576] with T_cap = max_pages << page_shift, and
 // `chunk` a multiple of the tile rows.
@@ -71,8 +76,8 @@ hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
                            float* lse, float* o_part, float* lse_part,
                            const int32_t* seq_lens, const int32_t* block_table,
                            int max_pages, int page_shift, int num_pages, int B,
-                           int H, int T_cap, int S, int chunk, int head_chunks,
-                           float scale_log2, hipStream_t stream);
+                           int L, int H, int T_cap, int S, int chunk,
+                           int head_chunks, float scale_log2, hipStream_t stream);
 
 }  // namespace attn
 

@@ -75,13 +75,16 @@ size_t attn_decode_mla_workspace_bytes(int B, int H, int T_cap, int d_c,
 
 namespace {
 
+// L query tokens per sequence plan as H * L (head, token) columns.
 int decode_mla(const void* q, const void* latent, float* out, float* lse_out,
                const int32_t* seq_lens, const int32_t* block_table,
-               int max_pages, int page_shift, int num_pages, int B, int H,
+               int max_pages, int page_shift, int num_pages, int B, int L, int H,
                int T_cap, int d_c, int d_rope, float scale, int num_splits,
                void* workspace, size_t workspace_bytes, void* stream) {
+  if (L < 1 || L > ATTN_MAX_QLEN) return ATTN_ERR_ARG;
+  if (H > 0 && (long long)H * L > (1 << 30)) return ATTN_ERR_SHAPE;
   MlaPlan p;
-  int st = plan_mla(B, H, T_cap, d_c, d_rope, num_splits, &p);
+  int st = plan_mla(B, H * L, T_cap, d_c, d_rope, num_splits, &p);
   if (st != ATTN_OK) return st;
   if (!(scale > 0.f) || isinf(scale)) return ATTN_ERR_ARG;
   if (B == 0) return ATTN_OK;
@@ -94,19 +97,19 @@ int decode_mla(const void* q, const void* latent, float* out, float* lse_out,
   if (p.S > 1) {
     if (!workspace || workspace_bytes < p.ws_bytes) return ATTN_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
-    const size_t rows = (size_t)B * H * p.S;
+    const size_t rows = (size_t)B * L * H * p.S;
     o_part = (float*)workspace;
     lse_part = (float*)((char*)workspace + round_up(rows * d_c * sizeof(float), 256));
   }
   if ((long long)B * p.S * p.head_chunks > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   if (attn::launch_mla_mfma(q, latent, out, lse_out, o_part, lse_part, seq_lens,
-                            block_table, max_pages, page_shift, num_pages, B, H,
-                            T_cap, p.S, p.chunk, p.head_chunks,
+                            block_table, max_pages, page_shift, num_pages, B, L,
+                            H, T_cap, p.S, p.chunk, p.head_chunks,
                             scale * 1.4426950408889634f, s) != hipSuccess)
     return ATTN_ERR_HIP;
-  if (p.S > 1 && attn::launch_combine(o_part, lse_part, out, lse_out, B, H, p.S,
-                                      d_c, s) != hipSuccess)
+  if (p.S > 1 && attn::launch_combine(o_part, lse_part, out, lse_out, B, H * L,
+                                      p.S, d_c, s) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -120,16 +123,26 @@ int attn_decode_mla(const void* q, const void* latent, float* out,
                     int T_cap, int d_c, int d_rope, float scale,
                     int num_splits, void* workspace, size_t workspace_bytes,
                     void* stream) {
-  return decode_mla(q, latent, out, lse_out, seq_lens, nullptr, 0, 0, 0, B, H,
+  return decode_mla(q, latent, out, lse_out, seq_lens, nullptr, 0, 0, 0, B, 1, H,
                     T_cap, d_c, d_rope, scale, num_splits, workspace,
+                    workspace_bytes, stream);
+}
+
+int attn_decode_mla_multi(const void* q, const void* latent, float* out,
+                          float* lse_out, const int32_t* seq_lens, int B,
+                          int q_len, int H, int T_cap, int d_c, int d_rope,
+                          float scale, int num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return decode_mla(q, latent, out, lse_out, seq_lens, nullptr, 0, 0, 0, B, q_len,
+                    H, T_cap, d_c, d_rope, scale, num_splits, workspace,
                     workspace_bytes, stream);
 }
 
 int attn_decode_mla_paged(const void* q, const void* latent_pages, float* out,
                           float* lse_out, const int32_t* seq_lens,
                           const int32_t* block_table, int max_pages, int B,
-                          int H, int num_pages, int page_size, int d_c,
-                          int d_rope, float scale, int num_splits,
+                          int q_len, int H, int num_pages, int page_size,
+                          int d_c, int d_rope, float scale, int num_splits,
                           void* workspace, size_t workspace_bytes,
                           void* stream) {
   int shift = 0;
@@ -138,8 +151,9 @@ int attn_decode_mla_paged(const void* q, const void* latent_pages, float* out,
   if (B > 0 && !block_table) return ATTN_ERR_NULL;
   if (block_table && !aligned(block_table, 4)) return ATTN_ERR_ALIGN;
   return decode_mla(q, latent_pages, out, lse_out, seq_lens, block_table,
-                    max_pages, shift, num_pages, B, H, max_pages * page_size, d_c,
-                    d_rope, scale, num_splits, workspace, workspace_bytes, stream);
+                    max_pages, shift, num_pages, B, q_len, H, max_pages * page_size,
+                    d_c, d_rope, scale, num_splits, workspace, workspace_bytes,
+                    stream);
 }
 
 }  // extern "C"

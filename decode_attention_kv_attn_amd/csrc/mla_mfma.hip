@@ -113,6 +113,8 @@ struct MlaArgs {
   float* lse_part;         // [B, H, S]
   const int32_t* seq_lens;
   int H, T_cap, S, chunk, head_chunks;
+  int L;     // query tokens per sequence (the last L positions)
+  int ncol;  // (head, token) columns: H * L
   float scale_log2;
 };
 
@@ -143,16 +145,21 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
   if constexpr (MODE == kAddrPaged)
     pg = page_view(a.block_table, a.max_pages, b, vr.hi, a.page_shift, a.num_pages, 1);
 
-  // Q^T fragments: head hw0 + 16*hb + li, elements 32*ks + 8*lg .. +7
+  // Q^T fragments: column hw0 + 16*hb + li (a (head, token) pair),
+  // elements 32*ks + 8*lg .. +7
   uint4 qf[2][kKS];
+  int tl[2];  // causal limit of this lane's columns (several tokens)
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
-    const int h = hw0 + 16 * hb + li;
-    const uint16_t* qp = a.q + ((size_t)b * a.H + h) * kDK + 8 * lg;
+    const int c = hw0 + 16 * hb + li;
+    const uint16_t* qp =
+        a.q + query_row(b, 0, min(c, a.ncol - 1), a.H, a.L, a.H) * kDK + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks)
-      qf[hb][ks] = h < a.H ? *(const uint4*)(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
+      qf[hb][ks] = c < a.ncol ? *(const uint4*)(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
+    tl[hb] = vr.hi - a.L + c % a.L;
   }
+  const bool multi = a.L > 1;
 
   f32x4_t o[kDB][2];
   float m[2], l[2];
@@ -290,6 +297,11 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
         for (int j = 0; j < 8; ++j)
           if (base + 16 * (j >> 2) + 4 * lg + (j & 3) >= p1) x[j] = neg_inf();
       }
+      if (multi) {  // uniform: each column's token sees positions <= tl
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (base + 16 * (j >> 2) + 4 * lg + (j & 3) > tl[hb]) x[j] = neg_inf();
+      }
       float mt = x[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
@@ -313,8 +325,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
       for (int j = 0; j < 8; ++j) {
         // m is finite once any row of this head was visible; masked rows
         // (only in a partial tile) get weight 0
-        p[j] = (!full && x[j] == neg_inf()) ? 0.f
-                                             : fast_exp2(fmaf(x[j], a.scale_log2, -m[hb]));
+        p[j] = ((!full || multi) && x[j] == neg_inf())
+                   ? 0.f
+                   : fast_exp2(fmaf(x[j], a.scale_log2, -m[hb]));
         l[hb] += p[j];
       }
 #pragma unroll
@@ -396,12 +409,12 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
   }
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
-    const int h = hw0 + 16 * hb + li;
-    if (h >= a.H) continue;
+    const int c = hw0 + 16 * hb + li;
+    if (c >= a.ncol) continue;
     const bool empty = !(l[hb] > 0.f);
     const float inv = empty ? 0.f : 1.f / l[hb];
     const float lse = empty ? neg_inf() : (m[hb] + fast_log2(l[hb])) * kLn2;
-    const size_t row = (size_t)b * a.H + h;
+    const size_t row = query_row(b, 0, c, a.H, a.L, a.H);
     float* dst = (a.S == 1) ? a.out + row * kDV : a.o_part + (row * a.S + s) * kDV;
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
@@ -425,8 +438,8 @@ hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
                            float* lse, float* o_part, float* lse_part,
                            const int32_t* seq_lens, const int32_t* block_table,
                            int max_pages, int page_shift, int num_pages, int B,
-                           int H, int T_cap, int S, int chunk, int head_chunks,
-                           float scale_log2, hipStream_t stream) {
+                           int L, int H, int T_cap, int S, int chunk,
+                           int head_chunks, float scale_log2, hipStream_t stream) {
   MlaArgs a;
   a.q = (const uint16_t*)q;
   a.latent = (const uint16_t*)latent;
@@ -440,6 +453,8 @@ hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
   a.lse_part = lse_part;
   a.seq_lens = seq_lens;
   a.H = H;
+  a.L = L;
+  a.ncol = H * L;
   a.T_cap = T_cap;
   a.S = S;
   a.chunk = chunk;

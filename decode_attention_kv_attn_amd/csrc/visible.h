@@ -128,6 +128,16 @@ ATTN_DEV void split_range(const VisibleRange& r, int s, int S, int chunk,
   p1 = e < r.n ? (int)e : r.n;
 }
 
+// Several query tokens per sequence (L >= 1, the last L positions of the
+// cache): column c (0 <= c < n*L) of KV head g stands for query head
+// g*n + c / L of token c % L, which sits at position T_b - L + c % L and is
+// stored at row (b*L + token)*H_q + head of q and of the outputs.
+ATTN_DEV size_t query_row(int b, int g, int c, int n, int L, int H_q) {
+  const int hq = c / L;
+  const int tok = c - hq * L;
+  return ((size_t)b * L + tok) * H_q + g * n + hq;
+}
+
 // Addressing modes, fixed per kernel instantiation so that the common case
 // carries no per-row branches: a dense [B, H_kv, T_cap, d] cache (linear or
 // ring), a linear cache with global positions, or a paged cache.

@@ -126,25 +126,58 @@ size_t attn_decode_gqa_workspace_bytes(int B, int H_q, int H_kv, int T_cap,
                                        int d, int dtype, int window, int ring,
                                        int num_splits);
 
-/* How attn_decode_gqa (and its _global / _paged forms) would run a call:
- * which kernel, how the visible range is split, the launch shape. */
+/* How attn_decode_gqa and its _global / _paged / _multi forms would run a
+ * call: which kernel, how the visible range is split, the launch shape and
+ * the workspace it needs. */
 typedef struct {
   int kernel;          /* 0 = vector-ALU kernel, 1 = matrix-core kernel      */
   int splits;          /* pieces of each visible range (1 = no combine pass) */
   int chunk;           /* positions per piece                                */
-  int heads_per_item;  /* query heads one work group serves                  */
+  int heads_per_item;  /* (head, token) columns one work group serves        */
   int tile_rows;       /* positions per wave per tile                        */
   int waves;           /* waves per work group                               */
   long long groups;    /* work groups of the decode kernel                   */
+  size_t workspace_bytes; /* workspace the call needs (0: none)              */
 } attn_gqa_plan;
 
-/* Fills *plan for these arguments (n_global as for attn_decode_gqa_global,
- * 0 otherwise; a paged call plans as T_cap = max_pages * page_size, ring 0).
- * Returns ATTN_OK or the status the decode call would return for the shape
- * arguments; plan must not be NULL (ATTN_ERR_NULL). */
-int attn_decode_gqa_plan(int B, int H_q, int H_kv, int T_cap, int d, int dtype,
-                         int window, int ring, int n_global, int num_splits,
-                         attn_gqa_plan* plan);
+/* Fills *plan for these arguments: q_len query tokens per sequence (1 for
+ * decode), n_global as for attn_decode_gqa_global (0 otherwise); a paged call
+ * plans as T_cap = max_pages * page_size with ring = 0.  Returns ATTN_OK or
+ * the status the call would return for these arguments; plan must not be
+ * NULL (ATTN_ERR_NULL). */
+int attn_decode_gqa_plan(int B, int q_len, int H_q, int H_kv, int T_cap, int d,
+                         int dtype, int window, int ring, int n_global,
+                         int num_splits, attn_gqa_plan* plan);
+
+/* Largest accepted q_len (query tokens per sequence). */
+#define ATTN_MAX_QLEN 1024
+
+/*
+ * attn_decode_gqa_multi -- q_len query tokens per sequence in one call
+ * (speculative-decode verification, chunked prefill).  The tokens are the
+ * last q_len positions of each cache, already written: token l sits at
+ * t_l = T_b - q_len + l and sees exactly what a single decode query at t_l
+ * sees (positions 0..t_l -- causal inside the chunk -- cut to its own
+ * window t_l-w+1..t_l; in ring mode only positions still resident after
+ * the whole chunk).  A token with t_l < 0 sees nothing (out 0, lse -inf).
+ *
+ *   q        [B, q_len, H_q, d]  dtype (token-major)
+ *   out      [B, q_len, H_q, d]  float32
+ *   lse_out  [B, q_len, H_q]     float32, may be NULL
+ *   q_len    1..ATTN_MAX_QLEN; 1 is attn_decode_gqa.
+ *   ring mode requires window + q_len - 1 <= T_cap (the first token's
+ *   window must be resident), else ATTN_ERR_WINDOW.
+ *   Everything else as for attn_decode_gqa; the workspace size comes from
+ *   attn_decode_gqa_plan (q_len as given).
+ * Each (head, token) pair is a column of its KV head's group: the group's
+ * K/V rows are read once for all q_len * H_q / H_kv columns.
+ */
+int attn_decode_gqa_multi(const void* q, const void* k, const void* v,
+                          float* out, float* lse_out, const int32_t* seq_lens,
+                          const int32_t* ring_head, int B, int q_len, int H_q,
+                          int H_kv, int T_cap, int d, int dtype, int window,
+                          float scale, int num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* Largest accepted n_global. */
 #define ATTN_MAX_GLOBAL 65536
@@ -195,9 +228,11 @@ int attn_decode_gqa_global(const void* q, const void* k, const void* v,
  *   num_pages >= 1, max_pages >= 1; max_pages * page_size <= 2^30 and
  *             num_pages * H_kv * page_size < 2^31 (else ATTN_ERR_SHAPE).
  *   window    as for attn_decode_gqa (no ring mode on a paged cache).
+ *   q_len     query tokens per sequence, as for attn_decode_gqa_multi (q,
+ *             out and lse_out then have its token-major shapes); 1 = decode.
  *   Everything else as for attn_decode_gqa.  Split count and workspace are
- *   those of attn_decode_gqa_splits / _workspace_bytes with
- *   T_cap = max_pages * page_size and ring = 0.
+ *   those of attn_decode_gqa_plan with T_cap = max_pages * page_size and
+ *   ring = 0 (for q_len = 1 also attn_decode_gqa_splits / _workspace_bytes).
  *   Table entries are not checked on the host: ids outside [0, num_pages)
  *   are clamped to the pool, so no access leaves it (the result is then
  *   unspecified).
@@ -205,10 +240,10 @@ int attn_decode_gqa_global(const void* q, const void* k, const void* v,
 int attn_decode_gqa_paged(const void* q, const void* k_pages,
                           const void* v_pages, float* out, float* lse_out,
                           const int32_t* seq_lens, const int32_t* block_table,
-                          int max_pages, int B, int H_q, int H_kv, int num_pages,
-                          int page_size, int d, int dtype, int window,
-                          float scale, int num_splits, void* workspace,
-                          size_t workspace_bytes, void* stream);
+                          int max_pages, int B, int q_len, int H_q, int H_kv,
+                          int num_pages, int page_size, int d, int dtype,
+                          int window, float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Split count and workspace bytes of attn_decode_gqa_global, with the same
  * return conventions as attn_decode_gqa_splits / _workspace_bytes. */
@@ -274,18 +309,40 @@ size_t attn_decode_mla_workspace_bytes(int B, int H, int T_cap, int d_c,
  *             to [0, max_pages * page_size].
  *   page_size, num_pages, max_pages: as for attn_decode_gqa_paged (with
  *             H_kv = 1 in the pool-size bound).
+ *   q_len     query tokens per sequence as for attn_decode_mla_multi (its
+ *             q / out / lse_out shapes); 1 = decode.
  *   Everything else as for attn_decode_mla; split count and workspace are
  *   those of attn_decode_mla_splits / _workspace_bytes with
- *   T_cap = max_pages * page_size.  Table ids outside [0, num_pages) are
+ *   T_cap = max_pages * page_size and H * q_len in place of H.  Table ids outside [0, num_pages) are
  *   clamped to the pool.
  */
 int attn_decode_mla_paged(const void* q, const void* latent_pages, float* out,
                           float* lse_out, const int32_t* seq_lens,
                           const int32_t* block_table, int max_pages, int B,
-                          int H, int num_pages, int page_size, int d_c,
-                          int d_rope, float scale, int num_splits,
+                          int q_len, int H, int num_pages, int page_size,
+                          int d_c, int d_rope, float scale, int num_splits,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * attn_decode_mla_multi -- attn_decode_mla with q_len query tokens per
+ * sequence (the last q_len positions of the cache, already written; token l
+ * at t_l = T_b - q_len + l sees positions 0..t_l, as in
+ * attn_decode_gqa_multi).
+ *
+ *   q        [B, q_len, H, d_c + d_rope] bf16 (token-major)
+ *   out      [B, q_len, H, d_c] float32, 16-byte aligned
+ *   lse_out  [B, q_len, H] float32, may be NULL
+ *   q_len    1..ATTN_MAX_QLEN.
+ *   Everything else as for attn_decode_mla; split count and workspace are
+ *   those of attn_decode_mla_splits / _workspace_bytes with H * q_len in
+ *   place of H.  Every latent row is read once for all H * q_len columns.
+ */
+int attn_decode_mla_multi(const void* q, const void* latent, float* out,
+                          float* lse_out, const int32_t* seq_lens, int B,
+                          int q_len, int H, int T_cap, int d_c, int d_rope,
+                          float scale, int num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * attn_combine -- merge results computed over S disjoint parts of each key

@@ -40,6 +40,8 @@ from .attention import (  # noqa: F401
     partial_ref,
     kv_append_ref,
     kv_append_ring_ref,
+    gqa_decode_multi_ref,
+    mla_decode_multi_ref,
     paged_positions,
     gqa_decode_paged_ref,
     mla_decode_paged_ref,

@@ -51,6 +51,8 @@ __all__ = [
     "partial_ref",
     "kv_append_ref",
     "kv_append_ring_ref",
+    "gqa_decode_multi_ref",
+    "mla_decode_multi_ref",
     "paged_positions",
     "gqa_decode_paged_ref",
     "mla_decode_paged_ref",
@@ -496,3 +498,90 @@ def kv_append_paged_ref(pages, new_rows, positions, block_table):
             else:
                 out[page[0], :, row[0]] = new_rows[b]
     return out
+
+
+# --------------------------------------------------------------------------
+# Several query tokens per sequence
+# --------------------------------------------------------------------------
+# Speculative-decode verification and chunked prefill score L new tokens of a
+# sequence in one call (the xuesongtap note, section 6, and the baidu
+# article: longer contexts and more tokens per step are what the cache
+# layouts are for).  The reading taken here: the L tokens are the last L
+# positions of the cache, already written (positions T_b-L .. T_b-1); token
+# l sits at t_l = T_b - L + l and sees what a single decode query at t_l
+# sees -- positions 0..t_l (causal inside the chunk), cut to its own window
+# t_l-w+1..t_l, and in a ring only positions still resident after all L
+# tokens were written (the newest is T_b - 1).  A token with t_l < 0 sees
+# nothing.  Layout: q [B, L, H_q, d] (token-major), outputs [B, L, H_q, d_v]
+# and [B, L, H_q].
+
+
+def _chunk_position(T_b, L, l):
+    """Position of query token l of an L-token chunk that ends the cache."""
+    return T_b - L + l
+
+
+def gqa_decode_multi_ref(q, k, v, seq_lens=None, ring_head=None, window=0,
+                         scale=None):
+    """L query tokens per sequence against a head-shared K/V cache."""
+    q = _as_f64(q)
+    B, L, H_q, d = q.shape
+    _, H_kv, T_cap, _ = tuple(k.shape)
+    d_v = tuple(v.shape)[3]
+    if H_q % H_kv != 0:
+        raise ValueError("H_q must be divisible by H_kv")
+    if ring_head is not None and window + L - 1 > T_cap:
+        raise ValueError("the ring must hold the first token's window")
+    n = H_q // H_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lens = _as_int(seq_lens, B, T_cap)
+    heads = _as_int(ring_head, B, 0) if ring_head is not None else None
+    out = np.zeros((B, L, H_q, d_v))
+    lse = np.full((B, L, H_q), -np.inf)
+    for b in range(B):
+        T_b = lens[b]
+        if heads is None and T_b > T_cap:
+            raise ValueError("seq_len exceeds the cache capacity")
+        newest = T_b - 1
+        for l in range(L):
+            t = _chunk_position(T_b, L, l)
+            if t < 0:
+                continue
+            lo = _window_low(t, window)
+            if heads is not None:
+                lo = max(lo, T_b - T_cap)     # resident after the whole chunk
+            pos = np.arange(lo, t + 1, dtype=np.int64)
+            slots = pos if heads is None else ring_slot(pos, newest, heads[b], T_cap)
+            for g in range(H_kv):
+                hs = [h for h in range(H_q) if _kv_head_for_query(h, n) == g]
+                k_rows = _as_f64(k[b, g])[slots]
+                v_rows = _as_f64(v[b, g])[slots]
+                o, m = attend(q[b, l, hs], k_rows, v_rows, scale)
+                out[b, l, hs] = o
+                lse[b, l, hs] = m
+    return out, lse
+
+
+def mla_decode_multi_ref(q, latent, d_c, scale, seq_lens=None):
+    """Absorbed MLA with L query tokens per sequence (token l at
+    T_b - L + l sees positions 0..T_b-L+l); q [B, L, H, d_c + d_rope]."""
+    q = _as_f64(q)
+    B, L, H, dk = q.shape
+    _, T_cap, _ = tuple(latent.shape)
+    lens = _as_int(seq_lens, B, T_cap)
+    z = np.zeros((B, L, H, d_c))
+    lse = np.full((B, L, H), -np.inf)
+    for b in range(B):
+        if lens[b] > T_cap:
+            raise ValueError("seq_len exceeds the cache capacity")
+        lat = _as_f64(latent[b])
+        for l in range(L):
+            t = _chunk_position(lens[b], L, l)
+            if t < 0:
+                continue
+            rows = lat[:t + 1]
+            o, m = attend(q[b, l], rows, rows[:, :d_c], scale)
+            z[b, l] = o
+            lse[b, l] = m
+    return z, lse

@@ -226,3 +226,48 @@ def mla_decode_paged_brute(q, latent_pages, block_table, d_c, scale, seq_lens):
         out.append(ob)
         lse.append(lb)
     return out, lse
+
+
+def gqa_decode_multi_brute(q, k, v, seq_lens, ring_head=None, window=0,
+                           scale=None):
+    """Scalar loops for L query tokens per sequence: every cache slot is
+    tested against every token (its position from the ring walk of the
+    newest token, then causal and window tests per token)."""
+    q, k, v = _lst(q), _lst(k), _lst(v)
+    B, L, H_q, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    H_kv, T_cap = len(k[0]), len(k[0][0])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lens = [int(x) for x in _lst(seq_lens)]
+    heads = None if ring_head is None else [int(x) for x in _lst(ring_head)]
+    out, lse = [], []
+    for b in range(B):
+        newest = lens[b] - 1
+        ob, lb = [], []
+        for l in range(L):
+            t = lens[b] - L + l
+            seen = []
+            for slot in range(T_cap):
+                pos = slot if heads is None else _slot_position(slot, newest, heads[b], T_cap)
+                if pos < 0 or pos > t:
+                    continue
+                if window > 0 and t - pos >= window:
+                    continue
+                seen.append(slot)
+            ol, ll = [], []
+            for h in range(H_q):
+                g = h * H_kv // H_q
+                if not seen:
+                    ol.append([0.0] * len(v[0][0][0]))
+                    ll.append(-math.inf)
+                    continue
+                sc = [scale * math.fsum(q[b][l][h][i] * k[b][g][s][i] for i in range(d))
+                      for s in seen]
+                o, m = _softmax_weighted(sc, [v[b][g][s] for s in seen])
+                ol.append(o)
+                ll.append(m)
+            ob.append(ol)
+            lb.append(ll)
+        out.append(ob)
+        lse.append(lb)
+    return out, lse

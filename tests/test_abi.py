@@ -169,7 +169,7 @@ def test_global_host_errors(lib):
 def test_paged_host_errors(lib):
     def gp(bt=P16, max_pages=8, num_pages=64, P=16, B=1, H_kv=2, q=P16):
         return lib.attn_decode_gqa_paged(q, P16, P16, P16, None, None, bt, max_pages,
-                                         B, 8, H_kv, num_pages, P, 64, 1, 0, 0.0, 0,
+                                         B, 1, 8, H_kv, num_pages, P, 64, 1, 0, 0.0, 0,
                                          None, 0, None)
     assert gp(bt=None) == -1
     assert gp(P=24) == -4            # not a power of two
@@ -182,7 +182,7 @@ def test_paged_host_errors(lib):
     assert gp(B=0, bt=None, q=None) == 0
 
     def mp(bt=P16, P=64, d_c=512):
-        return lib.attn_decode_mla_paged(P16, P16, P16, None, None, bt, 4, 1, 16, 8,
+        return lib.attn_decode_mla_paged(P16, P16, P16, None, None, bt, 4, 1, 1, 16, 8,
                                          P, d_c, 64, 0.07, 0, None, 0, None)
     assert mp(bt=None) == -1
     assert mp(P=48) == -4
@@ -207,6 +207,32 @@ def test_plan_info(lib):
             assert p["heads_per_item"] in (16, 32) and p["heads_per_item"] >= min(n, 32)
         else:
             assert p["heads_per_item"] == min(n, 8)
-    assert lib.attn_decode_gqa_plan(1, 8, 3, 64, 64, 1, 0, 0, 0, 0, None) == -1
+    assert lib.attn_decode_gqa_plan(1, 1, 8, 3, 64, 64, 1, 0, 0, 0, 0, None) == -1
     with pytest.raises(L.AttnError):
         L.attn_decode_gqa_plan(1, 8, 3, 64, 64, 1)
+
+
+
+def test_multi_token_host_errors(lib):
+    def gm(q_len=4, window=0, rh=None, T=512, q=P16, B=1):
+        return lib.attn_decode_gqa_multi(q, P16, P16, P16, None, None, rh, B, q_len, 8,
+                                         2, T, 64, 1, window, 0.0, 0, None, 0, None)
+    assert gm(q_len=0) == -9
+    assert gm(q_len=1025) == -9
+    assert gm(window=-1) == -5
+    assert gm(rh=P16, window=510) == -5      # ring: 510 + 4 - 1 > 512 slots
+    assert gm(q=None) == -1
+    assert gm(B=0, q=None) == 0
+    # the plan of L tokens: (head, token) columns of a KV head
+    p1 = L.attn_decode_gqa_plan(8, 32, 8, 4096, 128, 1)
+    p4 = L.attn_decode_gqa_plan(8, 32, 8, 4096, 128, 1, q_len=4)
+    assert p4["kernel"] == "mfma" and p4["heads_per_item"] == 16
+    assert p1["heads_per_item"] == 16
+    pv = L.attn_decode_gqa_plan(8, 8, 8, 4096, 128, 1, q_len=3)
+    assert pv["kernel"] == "mfma"  # 3 columns per KV head
+    assert L.attn_decode_gqa_plan(8, 8, 8, 4096, 128, 1)["kernel"] == "valu"
+    for S in (2, 5):
+        p = L.attn_decode_gqa_plan(8, 32, 8, 4096, 128, 1, num_splits=S, q_len=3)
+        assert p["workspace_bytes"] == lib.attn_decode_workspace_bytes(8 * 3, 32, 128, p["splits"])
+    assert lib.attn_decode_mla_multi(P16, P16, P16, None, None, 1, 0, 16, 64, 512, 64,
+                                     0.07, 0, None, 0, None) == -9

@@ -820,3 +820,116 @@ ALL_CHECKS += [check_paged_brute_force, check_paged_contiguous_reduction,
 def test_planted_paging_mistakes_are_caught(monkeypatch, mutant):
     monkeypatch.setattr(A, "paged_positions", mutant)
     assert _caught()
+
+
+# ------------------------------------------------------ several query tokens
+def check_multi_brute_force(seed=22):
+    """L-token reference == scalar slot walk, linear and ring, windows,
+    chunks longer than some sequences."""
+    rng = _rng(seed)
+    for c in range(30):
+        L = int(rng.choice([1, 2, 3, 5]))
+        ring = bool(rng.integers(0, 2))
+        T_cap = int(rng.integers(max(2, L), 12))
+        w = int(rng.choice([0, 1, 2, 4]))
+        if ring and w + L - 1 > T_cap:
+            w = 0 if L > T_cap else max(0, T_cap - L + 1)
+            if w == 0 and ring:
+                ring = False
+        B, H_q, H_kv, d = 2, 4, 2, 3
+        q = rng.standard_normal((B, L, H_q, d))
+        k = rng.standard_normal((B, H_kv, T_cap, d))
+        v = rng.standard_normal((B, H_kv, T_cap, d))
+        if ring:
+            lens = rng.integers(0, 3 * T_cap, size=B)
+            heads = rng.integers(0, T_cap, size=B)
+        else:
+            lens = rng.integers(0, T_cap + 1, size=B)
+            heads = None
+        o, l = oracle.gqa_decode_multi_ref(q, k, v, lens, heads, w, 0.9)
+        ob, lb = BF.gqa_decode_multi_brute(q, k, v, lens, heads, w, 0.9)
+        assert np.allclose(o, np.array(ob), atol=1e-12), c
+        lb = np.array(lb)
+        fin = np.isfinite(l)
+        assert np.array_equal(fin, np.isfinite(lb)) and np.allclose(l[fin], lb[fin], atol=1e-12)
+
+
+def test_multi_brute_force():
+    check_multi_brute_force()
+
+
+def check_multi_token_reductions(seed=23):
+    """One token is the decode reference; token l of a chunk is the decode
+    reference on the cache cut after position T_b - L + l."""
+    rng = _rng(seed)
+    B, L, H_q, H_kv, T, d = 2, 4, 6, 2, 16, 5
+    q = rng.standard_normal((B, L, H_q, d))
+    k = rng.standard_normal((B, H_kv, T, d))
+    v = rng.standard_normal((B, H_kv, T, d))
+    lens = np.array([16, 9])
+    for w in (0, 3):
+        o, l = oracle.gqa_decode_multi_ref(q[:, :1], k, v, lens, window=w)
+        o1, l1 = oracle.gqa_decode_ref(q[:, 0], k, v, lens, window=w)
+        assert np.array_equal(o[:, 0], o1) and np.array_equal(l[:, 0], l1)
+        o, l = oracle.gqa_decode_multi_ref(q, k, v, lens, window=w)
+        for t in range(L):
+            ot, lt = oracle.gqa_decode_ref(q[:, t], k, v, lens - L + t + 1, window=w)
+            assert np.allclose(o[:, t], ot, atol=1e-13) and np.allclose(l[:, t], lt, atol=1e-13)
+
+
+def test_multi_token_reductions():
+    check_multi_token_reductions()
+
+
+def check_multi_torch_causal_sdpa(seed=24):
+    """A chunk over a linear cache without window is causal attention with
+    the chunk aligned to the end of the keys (torch SDPA with an explicit
+    mask, float64)."""
+    rng = _rng(seed)
+    B, L, H, T, d = 1, 5, 3, 11, 4
+    q = rng.standard_normal((B, L, H, d))
+    k = rng.standard_normal((B, H, T, d))
+    v = rng.standard_normal((B, H, T, d))
+    o, _ = oracle.gqa_decode_multi_ref(q, k, v, [T])
+    mask = torch.tensor([[j <= T - L + i for j in range(T)] for i in range(L)])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(0, 2, 1, 3), torch.from_numpy(k),
+        torch.from_numpy(v), attn_mask=mask)
+    assert np.allclose(o, ref.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+
+
+def test_multi_torch_causal_sdpa():
+    check_multi_torch_causal_sdpa()
+
+
+def check_mla_multi(seed=25):
+    """L-token MLA == the decode MLA reference on the truncated cache, and
+    == the scalar MLA loop."""
+    rng = _rng(seed)
+    B, L, H, T, d_c, dk = 2, 3, 2, 9, 4, 6
+    q = rng.standard_normal((B, L, H, dk))
+    lat = rng.standard_normal((B, T, dk))
+    lens = np.array([9, 2])
+    z, l = oracle.mla_decode_multi_ref(q, lat, d_c, 0.6, lens)
+    for t in range(L):
+        zt, lt = oracle.mla_decode_ref(q[:, t], lat, d_c, 0.6, np.maximum(lens - L + t + 1, 0))
+        zb, lb = BF.mla_decode_brute(q[:, t], lat, d_c, 0.6, np.maximum(lens - L + t + 1, 0))
+        assert np.allclose(z[:, t], zt, atol=1e-13)
+        assert np.allclose(z[:, t], np.array(zb), atol=1e-12)
+        fin = np.isfinite(lt)
+        assert np.array_equal(np.isfinite(l[:, t]), fin)
+        assert np.allclose(l[:, t][fin], lt[fin], atol=1e-13)
+
+
+def test_mla_multi():
+    check_mla_multi()
+
+
+ALL_CHECKS += [check_multi_brute_force, check_multi_token_reductions,
+               check_multi_torch_causal_sdpa, check_mla_multi]
+
+
+@pytest.mark.parametrize("shift", [1, -1])
+def test_planted_chunk_position_mistakes_are_caught(monkeypatch, shift):
+    monkeypatch.setattr(A, "_chunk_position", lambda T_b, L, l: T_b - L + l + shift)
+    assert _caught()
