@@ -80,25 +80,37 @@ ATTN_DEV int vt_swz(int t) {
   else return 2 * (t & 3);
 }
 
-template <int D, int NH>
+// DK: key row width (and row stride of the cache); DV: value width.  DK ==
+// DV is a K/V cache; DK > DV is a latent cache whose value is the first DV
+// columns of each row (absorbed MLA: xuesongtap "attention-head" note,
+// sections 5.2-5.3) -- then the V tile is written to LDS from the K
+// fragments already in registers and V is never loaded on its own.
+template <int DK, int DV, int NH>
 struct MfmaCfg {
-  static constexpr int KS = D / 32;   // k-steps of the score product
+  static constexpr bool SHARED_V = DK != DV;
+  static constexpr int KS = DK / 32;  // k-steps of the score product
   static constexpr int HB = NH / 16;  // head blocks
-  static constexpr int DB = D / 16;   // d blocks of the value product
-  static constexpr int VT_BYTES = kTT * D * 2;
-  static constexpr int CPR = D / 8;            // 16-byte chunks per row
-  static constexpr int RPI = 64 / CPR;         // rows per load instruction
-  static constexpr int VLD = kTT / RPI;        // V loads per lane per tile
-  static constexpr int MERGE_BYTES = kNW * NH * (D + 2) * 4;
-  static constexpr int LOOP_BYTES = kNW * VT_BYTES;
+  static constexpr int DB = DV / 16;  // d blocks of the value product
+  static constexpr int VT_BYTES = kTT * DV * 2;
+  static constexpr int CPR = DV / 8;                      // 16-byte chunks per V row
+  static constexpr int RPI = CPR >= 64 ? 1 : 64 / CPR;    // rows per load instruction
+  static constexpr int VLD = SHARED_V ? 0 : kTT / RPI;    // V loads per lane per tile
+  // Q^T fragments live in LDS (shared by the waves, read per k-step) when
+  // they would not fit in registers beside the K stages: the latent case.
+  static constexpr bool Q_LDS = SHARED_V;
+  static constexpr int Q_BYTES = Q_LDS ? HB * KS * 64 * 16 : 0;
+  static constexpr int MERGE_BYTES = kNW * NH * (DV + 2) * 4;
+  static constexpr int LOOP_BYTES = kNW * VT_BYTES + Q_BYTES;
   static constexpr int SMEM = MERGE_BYTES > LOOP_BYTES ? MERGE_BYTES : LOOP_BYTES;
+  static_assert(DV % 32 == 0 && DV <= DK, "value columns");
 };
 
-template <int D, int NH, int MODE>
+template <int DK, int DV, int NH, int MODE>
 __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
-  using C = MfmaCfg<D, NH>;
+  using C = MfmaCfg<DK, DV, NH>;
   constexpr int KS = C::KS, HB = C::HB, DB = C::DB, CPR = C::CPR;
   constexpr int RPI = C::RPI, VLD = C::VLD;
+  constexpr int D = DK;  // row stride of the cache and of q
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
 
   const int lane = threadIdx.x & 63;
@@ -141,9 +153,23 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   const uint16_t* __restrict__ Kbg = (const uint16_t*)a.k + kv_off;
   const uint16_t* __restrict__ Vbg = (const uint16_t*)a.v + kv_off;
 
-  // Q^T fragments: head li of block hb, elements 32*ks + 8*lg .. +7.
-  uint4 qf[HB][KS];
-  {
+  // Q^T fragments: head li of block hb, elements 32*ks + 8*lg .. +7 -- in
+  // registers, or (Q_LDS) in LDS as entry (hb*KS + ks)*64 + lane, filled
+  // once by the whole group.
+  uint4 qf[C::Q_LDS ? 1 : HB][C::Q_LDS ? 1 : KS];
+  uint4* const sq = (uint4*)(smem + kNW * C::VT_BYTES);
+  if constexpr (C::Q_LDS) {
+    for (int e = threadIdx.x; e < HB * KS * 64; e += kNW * 64) {
+      const int ln = e & 63;
+      const int ks = (e >> 6) % KS;
+      const int hb = (e >> 6) / KS;
+      const int h = hb * 16 + (ln & 15);
+      const uint16_t* qh = (const uint16_t*)a.q +
+                           query_row(b, g, min(c0 + h, a.ncol - 1), a.n, a.L, a.H_q) * D;
+      sq[e] = h < nh ? *(const uint4*)(qh + 32 * ks + 8 * (ln >> 4)) : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+  } else {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       const int h = hb * 16 + li;
@@ -155,6 +181,15 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
                             : make_uint4(0, 0, 0, 0);
     }
   }
+  auto q_frag = [&](int hb, int ks) -> uint4 {
+    if constexpr (C::Q_LDS) {
+      // the lane index is recomputed here (cheaper than keeping it live)
+      const int ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      return sq[(hb * KS + ks) * 64 + ln];
+    } else {
+      return qf[hb][ks];
+    }
+  };
 
   f32x4_t o[DB][HB];  // O^T blocks: d rows 16*db + 4*lg + r, head column li
   float m[HB], l[HB];
@@ -204,7 +239,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   // share of the V tile (rows RPI*i + lane/CPR, chunk lane%CPR).
   // A tile index past the split (uniform) reads row 0 of the K/V base
   // instead: in bounds, shared by the work group's waves, never used.
-  auto load_tile = [&](int it, int pv, uint4 (&kf)[2][KS], uint4 (&vr_)[VLD]) {
+  auto load_tile = [&](int it, int pv, uint4 (&kf)[2][KS], uint4 (&vr_)[VLD > 0 ? VLD : 1]) {
     const int base = p0 + it * kTT;
     const bool dummy = it >= ntiles;
     int pid[3];
@@ -222,32 +257,49 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
       const int row = dummy ? 0 : tile_row(base, t, pid);
       vr_[i] = nt_load16(Vbg + (size_t)row * D + 8 * (lane % CPR));
     }
+    (void)vr_;
   };
 
-  auto compute_tile = [&](int it, const uint4 (&kf)[2][KS], const uint4 (&vr_)[VLD]) {
+  auto compute_tile = [&](int it, const uint4 (&kf)[2][KS],
+                          const uint4 (&vr_)[VLD > 0 ? VLD : 1]) {
     const int base = p0 + it * kTT;
     // V tile -> LDS (row t, chunk c stored at chunk c ^ swz(t))
+    if constexpr (C::SHARED_V) {
+      // the value columns are the first DV of the K fragments: row
+      // 16*tb + li, chunk 4*ks + lg
 #pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int t = RPI * i + lane / CPR;
-      const int c = lane % CPR;
-      *(uint4*)(vt + t * (2 * D) + 16 * (c ^ vt_swz<D>(t))) = vr_[i];
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int ks = 0; ks < DV / 32; ++ks) {
+          const int t = 16 * tb + li;
+          const int c = 4 * ks + lg;
+          *(uint4*)(vt + t * (2 * DV) + 16 * (c ^ vt_swz<DV>(t))) = kf[tb][ks];
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VLD; ++i) {
+        const int t = RPI * i + lane / CPR;
+        const int c = lane % CPR;
+        *(uint4*)(vt + t * (2 * DV) + 16 * (c ^ vt_swz<DV>(t))) = vr_[i];
+      }
     }
 
     // scores S^T: token rows 16*tb + 4*lg + r, head column li of block hb
     f32x4_t sc[2][HB];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int hb = 0; hb < HB; ++hb) {
+      f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[tb][ks]),
-                                                         as_bf16x8(qf[hb][ks]), acc,
-                                                         0, 0, 0);
-        sc[tb][hb] = acc;
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t qv = as_bf16x8(q_frag(hb, ks));
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[0][ks]), qv, acc0,
+                                                        0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[1][ks]), qv, acc1,
+                                                        0, 0, 0);
       }
+      sc[0][hb] = acc0;
+      sc[1][hb] = acc1;
+    }
 
     bool valid[2][4];
 #pragma unroll
@@ -301,9 +353,9 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
       const int t0 = 4 * lg + (li >> 2);
       const int col = 16 * db + 4 * (li & 3);
       const int c = col >> 3, half = (col & 7) * 2;
-      const unsigned char* a0 = vt + t0 * (2 * D) + 16 * (c ^ vt_swz<D>(t0)) + half;
+      const unsigned char* a0 = vt + t0 * (2 * DV) + 16 * (c ^ vt_swz<DV>(t0)) + half;
       const unsigned char* a1 =
-          vt + (t0 + 16) * (2 * D) + 16 * (c ^ vt_swz<D>(t0 + 16)) + half;
+          vt + (t0 + 16) * (2 * DV) + 16 * (c ^ vt_swz<DV>(t0 + 16)) + half;
       typedef s16x4_t __attribute__((address_space(3))) * lds_s16x4;
       const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4)(__attribute__((address_space(3))) unsigned char*)a0);
@@ -329,7 +381,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
 
   // two register stages; page ids run a tile ahead, loaded before the
   // current tile's rows so that waiting for them never waits for row data
-  uint4 kA[2][KS], vA[VLD], kB[2][KS], vB[VLD];
+  uint4 kA[2][KS], vA[VLD > 0 ? VLD : 1], kB[2][KS], vB[VLD > 0 ? VLD : 1];
   // The loop body is one pair of tiles with both loads unconditional (a
   // load behind a condition, or a break between the halves, makes the
   // compiler's wait for the current tile also cover the next tile's loads);
@@ -362,15 +414,15 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   }
 
   __syncthreads();  // the V tiles are dead; reuse LDS for the merge
-  float* sm_o = (float*)smem;                       // [NW][NH][D]
-  float* sm_m = sm_o + kNW * NH * D;                // [NW][NH]
+  float* sm_o = (float*)smem;                       // [NW][NH][DV]
+  float* sm_m = sm_o + kNW * NH * DV;               // [NW][NH]
   float* sm_l = sm_m + kNW * NH;                    // [NW][NH]
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int h = hb * 16 + li;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      *(f32x4_t*)(sm_o + ((size_t)wave * NH + h) * D + 16 * db + 4 * lg) = o[db][hb];
+      *(f32x4_t*)(sm_o + ((size_t)wave * NH + h) * DV + 16 * db + 4 * lg) = o[db][hb];
     if (lg == 0) {
       sm_m[wave * NH + h] = m[hb];
       sm_l[wave * NH + h] = l[hb];
@@ -378,9 +430,9 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   }
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < nh * D; idx += kNW * 64) {
-    const int h = idx / D;
-    const int e = idx - h * D;
+  for (int idx = threadIdx.x; idx < nh * DV; idx += kNW * 64) {
+    const int h = idx / DV;
+    const int e = idx - h * DV;
     float M = neg_inf();
 #pragma unroll
     for (int w = 0; w < kNW; ++w) M = fmaxf(M, sm_m[w * NH + h]);
@@ -391,7 +443,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
         const float mw = sm_m[w * NH + h];
         const float wt = (mw == neg_inf()) ? 0.f : fast_exp2(mw - M);
         L = fmaf(wt, sm_l[w * NH + h], L);
-        O = fmaf(wt, sm_o[((size_t)w * NH + h) * D + e], O);
+        O = fmaf(wt, sm_o[((size_t)w * NH + h) * DV + e], O);
       }
     }
     const bool empty = !(L > 0.f);
@@ -399,30 +451,35 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
     const float lse = empty ? neg_inf() : (M + fast_log2(L)) * kLn2;
     const size_t row = query_row(b, g, c0 + h, a.n, a.L, a.H_q);
     if (a.S == 1) {
-      a.out[row * D + e] = ov;
+      a.out[row * DV + e] = ov;
       if (e == 0 && a.lse) a.lse[row] = lse;
     } else {
-      a.o_part[(row * a.S + s) * D + e] = ov;
+      a.o_part[(row * a.S + s) * DV + e] = ov;
       if (e == 0) a.lse_part[row * a.S + s] = lse;
     }
   }
 }
 
-template <int D, int NH, int MODE>
+template <int DK, int DV, int NH, int MODE>
 hipError_t launch_one(const GqaArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((gqa_decode_mfma<D, NH, MODE>), dim3(grid), dim3(kNW * 64), 0,
-                     st, a);
+  hipLaunchKernelGGL((gqa_decode_mfma<DK, DV, NH, MODE>), dim3(grid), dim3(kNW * 64),
+                     0, st, a);
   return hipGetLastError();
 }
 
 template <int MODE>
-hipError_t launch_mode(const GqaArgs& a, int d, int heads_per_item, int grid,
+hipError_t launch_mode(const GqaArgs& a, int dk, int dv, int heads_per_item, int grid,
                        hipStream_t st) {
-  switch (d * 1000 + heads_per_item) {
-    case 64016: return launch_one<64, 16, MODE>(a, grid, st);
-    case 64032: return launch_one<64, 32, MODE>(a, grid, st);
-    case 128016: return launch_one<128, 16, MODE>(a, grid, st);
-    case 128032: return launch_one<128, 32, MODE>(a, grid, st);
+  switch (dk * 1000000 + dv * 1000 + heads_per_item) {
+    case 64064016: return launch_one<64, 64, 16, MODE>(a, grid, st);
+    case 64064032: return launch_one<64, 64, 32, MODE>(a, grid, st);
+    case 128128016: return launch_one<128, 128, 16, MODE>(a, grid, st);
+    case 128128032: return launch_one<128, 128, 32, MODE>(a, grid, st);
+  }
+  if constexpr (MODE != kAddrGlobal) {
+    // latent rows of 256 + 64; 16 columns per group (32 would spill)
+    if (dk == 320 && dv == 256 && heads_per_item == 16)
+      return launch_one<320, 256, 16, MODE>(a, grid, st);
   }
   return hipErrorInvalidValue;
 }
@@ -451,9 +508,16 @@ int mfma_waves() { return kNW; }
 
 hipError_t launch_gqa_mfma(const GqaArgs& a, int d, int heads_per_item, int grid,
                            hipStream_t st) {
-  if (a.block_table) return launch_mode<kAddrPaged>(a, d, heads_per_item, grid, st);
-  if (a.n_global > 0) return launch_mode<kAddrGlobal>(a, d, heads_per_item, grid, st);
-  return launch_mode<kAddrDense>(a, d, heads_per_item, grid, st);
+  return launch_latent_mfma(a, d, d, heads_per_item, grid, st);
+}
+
+hipError_t launch_latent_mfma(const GqaArgs& a, int dk, int dv, int heads_per_item,
+                              int grid, hipStream_t st) {
+  if (a.block_table)
+    return launch_mode<kAddrPaged>(a, dk, dv, heads_per_item, grid, st);
+  if (a.n_global > 0)
+    return launch_mode<kAddrGlobal>(a, dk, dv, heads_per_item, grid, st);
+  return launch_mode<kAddrDense>(a, dk, dv, heads_per_item, grid, st);
 }
 
 }  // namespace attn

@@ -64,6 +64,12 @@ int mfma_tile_rows();
 int mfma_waves();
 hipError_t launch_gqa_mfma(const GqaArgs& a, int d, int heads_per_item, int grid,
                            hipStream_t stream);
+// The same kernel with key width dk and value width dv; dk > dv reads a
+// latent cache whose value is the first dv columns of each row (k == v).
+// Instantiated for (dk, dv) = (64, 64), (128, 128) with 16 or 32 columns per
+// group, and (320, 256) with 16.
+hipError_t launch_latent_mfma(const GqaArgs& a, int dk, int dv, int heads_per_item,
+                              int grid, hipStream_t stream);
 
 // Absorbed MLA on the matrix cores (bf16, d_c = 512, d_rope = 64).
 int mla_heads_per_group();

@@ -273,7 +273,9 @@ size_t attn_decode_gqa_global_workspace_bytes(int B, int H_q, int H_kv,
  *   seq_lens [B] int32, may be NULL (all T_cap); clamped to [0, T_cap].
  *   Scores are scale * (q~ . c_j + q^R . k^R_j): one dot product over the
  *   whole row, one softmax over the sum (section 5.3).
- *   (d_c, d_rope) = (512, 64) is supported.
+ *   (d_c, d_rope) = (512, 64) and (256, 64) are supported (the latter is the
+ *   32-head, latent-256 geometry of the attention-head note's section 6 model
+ *   table; any H works).
  *   scale   must be > 0 and finite: 1/sqrt(d_head_content + d_rope) with the
  *           model's per-head content width (section 5.3 keeps that
  *           denominator; the latent width r does not enter it).

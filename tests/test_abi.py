@@ -186,7 +186,7 @@ def test_paged_host_errors(lib):
                                          P, d_c, 64, 0.07, 0, None, 0, None)
     assert mp(bt=None) == -1
     assert mp(P=48) == -4
-    assert mp(d_c=256) == -4
+    assert mp(d_c=384) == -4
     ap = lib.attn_kv_append_paged
     assert ap(P16, None, P16, None, P16, None, 4, 1, 2, 8, 16, 64, 1, None) == -1
     assert ap(P16, None, P16, None, P16, P16, 4, 1, 2, 8, 12, 64, 1, None) == -4
