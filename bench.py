@@ -34,7 +34,7 @@ METRIC = "decode-attention KV-read GB/s (% of HBM peak) and µs/step per layer"
 DEFAULT_WORKLOAD = "llama3_8b_gqa_t4096"
 SETTLE_S = 0.3  # seconds of untimed calls before the warmup (clock ramp-up)
 KERNEL_SOURCES = {"gqa": ["gqa_valu.hip", "gqa_mfma.hip", "visible.h", "device_common.h"],
-                  "mla": ["mla_mfma.hip", "visible.h", "device_common.h"]}
+                  "mla": ["mla_mfma.hip", "gqa_mfma.hip", "visible.h", "device_common.h"]}
 
 
 def parse():
@@ -441,7 +441,8 @@ def bench_mla(args, w, dev):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(alg_bytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(w["name"], "mla"),
-                     "kernel": "mla_decode_mfma" + ("" if S == 1 else " + lse_combine"),
+                     "kernel": ("mla_decode_mfma" if w["d_c"] == 512 else
+                                "gqa_decode_mfma<320, 256>") + ("" if S == 1 else " + lse_combine"),
                      "kernel_us": round(call_ms * 1e3, 2)},
         "mfma_roofline": {"achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -475,6 +475,7 @@ hipError_t launch_mode(const GqaArgs& a, int dk, int dv, int heads_per_item, int
     case 64064032: return launch_one<64, 64, 32, MODE>(a, grid, st);
     case 128128016: return launch_one<128, 128, 16, MODE>(a, grid, st);
     case 128128032: return launch_one<128, 128, 32, MODE>(a, grid, st);
+    case 256256016: return launch_one<256, 256, 16, MODE>(a, grid, st);
   }
   if constexpr (MODE != kAddrGlobal) {
     // latent rows of 256 + 64; 16 columns per group (32 would spill)
@@ -486,9 +487,9 @@ hipError_t launch_mode(const GqaArgs& a, int dk, int dv, int heads_per_item, int
 
 }  // namespace
 
-// Heads per work item on the matrix-core path (16 or 32), or 0 if the path
-// does not apply (float32 data, d = 256, or groups small enough for the
-// vector kernel).
+// Columns per work item on the matrix-core path (16 or 32; 16 at d = 256),
+// or 0 if the path does not apply (float32 data, or groups small enough for
+// the vector kernel).
 int mfma_heads_per_item(int dtype, int d, int n) {
   // smallest group sent to the matrix cores (overridable for tuning sweeps
   // through ATTN_DECODE_MFMA_MIN_GROUP)
@@ -498,6 +499,7 @@ int mfma_heads_per_item(int dtype, int d, int n) {
     return x > 0 ? x : 3;
   }();
   if (dtype != 1 || n < min_group) return 0;
+  if (d == 256) return 16;  // 32 columns would not fit the registers
   if (d != 64 && d != 128) return 0;
   const int r = (n + 15) / 16 * 16;
   return r < 32 ? r : 32;

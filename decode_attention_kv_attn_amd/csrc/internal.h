@@ -58,7 +58,7 @@ hipError_t launch_gqa_valu_global(const GqaArgs& a, int dtype, int d, int grid,
 hipError_t launch_gqa_valu_paged(const GqaArgs& a, int dtype, int d, int grid,
                                  hipStream_t stream);
 
-// Matrix-core path for bf16 groups of 3 or more heads, d in {64, 128}.
+// Matrix-core path for bf16 groups of 3 or more columns, d in {64, 128, 256}.
 int mfma_heads_per_item(int dtype, int d, int n);
 int mfma_tile_rows();
 int mfma_waves();
@@ -67,7 +67,7 @@ hipError_t launch_gqa_mfma(const GqaArgs& a, int d, int heads_per_item, int grid
 // The same kernel with key width dk and value width dv; dk > dv reads a
 // latent cache whose value is the first dv columns of each row (k == v).
 // Instantiated for (dk, dv) = (64, 64), (128, 128) with 16 or 32 columns per
-// group, and (320, 256) with 16.
+// group, and (256, 256), (320, 256) with 16.
 hipError_t launch_latent_mfma(const GqaArgs& a, int dk, int dv, int heads_per_item,
                               int grid, hipStream_t stream);
 

@@ -197,14 +197,15 @@ def test_plan_info(lib):
     for (H_q, H_kv, d, dt, want) in [(32, 32, 128, 1, "valu"), (16, 8, 128, 1, "valu"),
                                      (24, 8, 128, 1, "mfma"), (32, 8, 128, 1, "mfma"),
                                      (32, 1, 64, 1, "mfma"), (32, 8, 128, 0, "valu"),
-                                     (24, 4, 256, 1, "valu")]:
+                                     (24, 4, 256, 1, "mfma"), (8, 4, 256, 1, "valu")]:
         p = L.attn_decode_gqa_plan(32, H_q, H_kv, 4096, d, dt)
         assert p["kernel"] == want, (H_q, H_kv, d, dt, p)
         assert p["splits"] == lib.attn_decode_gqa_splits(32, H_q, H_kv, 4096, d, dt, 0, 0, 0)
         assert p["groups"] % p["splits"] == 0 and p["groups"] >= 32 * H_kv
         n = H_q // H_kv
         if want == "mfma":
-            assert p["heads_per_item"] in (16, 32) and p["heads_per_item"] >= min(n, 32)
+            assert p["heads_per_item"] in (16, 32)
+            assert p["heads_per_item"] >= min(n, 32 if d < 256 else 16)
         else:
             assert p["heads_per_item"] == min(n, 8)
     assert lib.attn_decode_gqa_plan(1, 1, 8, 3, 64, 64, 1, 0, 0, 0, 0, None) == -1
