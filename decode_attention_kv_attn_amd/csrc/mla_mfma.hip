@@ -34,6 +34,20 @@
 #include "internal.h"
 #include "visible.h"
 
+// Tuning knobs (compile-time; defaults are the measured best).
+#ifndef ATTN_MLA_QK_AHEAD  // k-steps the score operand reads run ahead
+#define ATTN_MLA_QK_AHEAD 2
+#endif
+#ifndef ATTN_MLA_DMA_IN_PV  // issue the next loads in the value loop
+#define ATTN_MLA_DMA_IN_PV 0
+#endif
+#ifndef ATTN_MLA_DMA_EVERY  // value blocks between two of those loads
+#define ATTN_MLA_DMA_EVERY 3
+#endif
+#ifndef ATTN_MLA_WAVES  // waves per group (128 heads split among them)
+#define ATTN_MLA_WAVES 4
+#endif
+
 namespace attn {
 namespace {
 
@@ -44,16 +58,18 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kDK = 576;                 // latent row: 512 content + 64 rope
 constexpr int kDV = 512;                 // value columns (the content part)
 constexpr int kTT = 32;                  // rows per tile
-constexpr int kNW = 4;                   // waves per group
-constexpr int kHW = 32;                  // heads per wave
+constexpr int kNW = ATTN_MLA_WAVES;      // waves per group
+constexpr int kHW = 128 / kNW;           // heads per wave
+constexpr int kHB = kHW / 16;            // 16-head blocks per wave
 constexpr int kHG = kNW * kHW;           // heads per group
 constexpr int kRowBytes = kDK * 2;       // 1152
 constexpr int kCPR = kRowBytes / 16;     // 72 chunks per row
 constexpr int kTileBytes = kTT * kRowBytes;         // 36864
-constexpr int kDmaPerWave = kTileBytes / (kNW * 1024);  // 9 x 1 KiB per wave
+constexpr int kPieces = kTileBytes / 1024;              // 1 KiB loads per tile
+constexpr int kDmaPerWave = (kPieces + kNW - 1) / kNW;  // at most, per wave
 constexpr int kKS = kDK / 32;            // 18 score k-steps
 constexpr int kDB = kDV / 16;            // 32 value blocks
-static_assert(kTileBytes % (kNW * 1024) == 0, "tile split");
+static_assert(kTileBytes % 1024 == 0 && (kNW == 4 || kNW == 8), "tile split");
 
 __shared__ __attribute__((aligned(1024))) unsigned char g_stage0[kTileBytes];
 __shared__ __attribute__((aligned(1024))) unsigned char g_stage1[kTileBytes];
@@ -118,7 +134,9 @@ struct MlaArgs {
   float scale_log2;
 };
 
-template <int MODE>
+// MULTI: several query tokens per sequence (per-column causal limits); a
+// separate instantiation so the single-token path carries none of it.
+template <int MODE, bool MULTI>
 __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
   const int lane = threadIdx.x & 63;
   // uniform across the wave: keep wave-derived offsets in scalar registers
@@ -147,10 +165,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
 
   // Q^T fragments: column hw0 + 16*hb + li (a (head, token) pair),
   // elements 32*ks + 8*lg .. +7
-  uint4 qf[2][kKS];
-  int tl[2];  // causal limit of this lane's columns (several tokens)
+  uint4 qf[kHB][kKS];
+  int tl[kHB];  // causal limit of this lane's columns (several tokens)
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
+  for (int hb = 0; hb < kHB; ++hb) {
     const int c = hw0 + 16 * hb + li;
     const uint16_t* qp =
         a.q + query_row(b, 0, min(c, a.ncol - 1), a.H, a.L, a.H) * kDK + 8 * lg;
@@ -159,12 +177,12 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
       qf[hb][ks] = c < a.ncol ? *(const uint4*)(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
     tl[hb] = vr.hi - a.L + c % a.L;
   }
-  const bool multi = a.L > 1;
+  constexpr bool multi = MULTI;
 
-  f32x4_t o[kDB][2];
-  float m[2], l[2];
+  f32x4_t o[kDB][kHB];
+  float m[kHB], l[kHB];
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
+  for (int hb = 0; hb < kHB; ++hb) {
     m[hb] = neg_inf();
     l[hb] = 0.f;
 #pragma unroll
@@ -176,11 +194,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
   // Per-lane byte offsets inside a full tile of this wave's direct-to-LDS
   // loads: LDS chunk p = blk*64 + lane holds row p/72, logical chunk
   // (p%72) ^ swz(row).  Offsets are < 2^16, two per register.
+  // This wave's loads are blocks wave, wave + kNW, ... of the tile's kPieces.
+  const int my_pieces = (kPieces - wave + kNW - 1) / kNW;
   uint32_t dma_off[(kDmaPerWave + 1) / 2];
   uint32_t hi_rows = 0;  // bit j: load j of this lane is in the tile's rows 16..31
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j) {
-    const int p = (wave * kDmaPerWave + j) * 64 + lane;
+    const int p = min(wave + j * kNW, kPieces - 1) * 64 + lane;
     const int t = p / kCPR;
     const uint32_t off = t * kRowBytes + 16 * ((p - t * kCPR) ^ swz(t));
     if (j & 1) dma_off[j >> 1] |= off << 16;
@@ -201,7 +221,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
     constexpr int I = decltype(stage_tag)::value;
     const int base = p0 + it * kTT;
     const int nvalid = p1 - base;  // rows of this tile inside the split
-    const int blk = wave * kDmaPerWave + j;
+    const int blk = wave + j * kNW;
     uint32_t off = (dma_off[j >> 1] >> (16 * (j & 1))) & 0xffffu;
     bool hi = (hi_rows >> j) & 1;
     if (nvalid < kTT) {  // uniform: the split's last, partial tile
@@ -232,7 +252,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
   };
   auto issue_tile = [&](auto stage_tag, int it) {
 #pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) issue_piece(stage_tag, it, j);
+    for (int j = 0; j < kDmaPerWave; ++j)
+      if (j < my_pieces) issue_piece(stage_tag, it, j);
   };
 
   // Computes tile `it` from stage I; when `pf` is set, the loads of tile
@@ -248,7 +269,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
 
     // scores.  Chunk (4*ks + lg) ^ swz(t) = 8*(ks/2) + ((4*(ks&1) + lg) ^ swz(t)):
     // two base addresses per row block, the rest is an immediate offset.
-    const unsigned char* abase[2][2];
+    const unsigned char* abase[2][2];  // [row block][chunk parity]
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       const int t = 16 * tb + li;
@@ -256,35 +277,40 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
       for (int e = 0; e < 2; ++e)
         abase[tb][e] = tile + t * kRowBytes + 16 * ((4 * e + lg) ^ swz(t));
     }
-    f32x4_t sc[2][2] = {};
-    // operand reads run one k-step ahead of the MFMAs that use them
-    uint4 af[2][2];
+    f32x4_t sc[2][kHB] = {};
+    // operand reads run kAhead k-steps ahead of the MFMAs that use them
+    constexpr int kAhead = ATTN_MLA_QK_AHEAD;
+    uint4 af[kAhead + 1][2];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) af[0][tb] = *(const uint4*)(abase[tb][0]);
+    for (int k0 = 0; k0 < kAhead; ++k0)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        af[k0][tb] = *(const uint4*)(abase[tb][k0 & 1] + 128 * (k0 >> 1));
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      if (pf && (ks & 1) == 0 && (ks >> 1) < kDmaPerWave)
+      if (!ATTN_MLA_DMA_IN_PV && pf && (ks & 1) == 0 && (ks >> 1) < kDmaPerWave &&
+          (ks >> 1) < my_pieces)
         issue_piece(std::integral_constant<int, (I + 2) % 3>{}, it + 2, ks >> 1);
-      const int cur = ks & 1;
-      if (ks + 1 < kKS) {
+      const int cur = ks % (kAhead + 1);
+      const int kn = ks + kAhead;
+      if (kn < kKS) {
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
-          af[cur ^ 1][tb] =
-              *(const uint4*)(abase[tb][(ks + 1) & 1] + 128 * ((ks + 1) >> 1));
+          af[kn % (kAhead + 1)][tb] = *(const uint4*)(abase[tb][kn & 1] + 128 * (kn >> 1));
       }
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
+        for (int hb = 0; hb < kHB; ++hb)
           sc[tb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               as_bf16x8(af[cur][tb]), as_bf16x8(qf[hb][ks]), sc[tb][hb], 0, 0, 0);
     }
 
     // online softmax per head (lazy maximum); weights split into bf16 hi+lo
     const bool full = base + kTT <= p1;  // uniform: no masked row in the tile
-    uint32_t phi[2][4], plo[2][4];
+    uint32_t phi[kHB][4], plo[kHB][4];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+    for (int hb = 0; hb < kHB; ++hb) {
       // raw scores; the scale (> 0) is applied once to the maximum and fused
       // into the exponent below
       float x[8];
@@ -297,7 +323,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
         for (int j = 0; j < 8; ++j)
           if (base + 16 * (j >> 2) + 4 * lg + (j & 3) >= p1) x[j] = neg_inf();
       }
-      if (multi) {  // uniform: each column's token sees positions <= tl
+      if constexpr (multi) {  // each column's token sees positions <= tl
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           if (base + 16 * (j >> 2) + 4 * lg + (j & 3) > tl[hb]) x[j] = neg_inf();
@@ -357,22 +383,28 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
       return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     typedef short s16x8_t __attribute__((ext_vector_type(8)));
-    const bf16x8_t bh[2] = {
-        as_bf16x8(make_uint4(phi[0][0], phi[0][1], phi[0][2], phi[0][3])),
-        as_bf16x8(make_uint4(phi[1][0], phi[1][1], phi[1][2], phi[1][3]))};
-    const bf16x8_t bl[2] = {
-        as_bf16x8(make_uint4(plo[0][0], plo[0][1], plo[0][2], plo[0][3])),
-        as_bf16x8(make_uint4(plo[1][0], plo[1][1], plo[1][2], plo[1][3]))};
+    bf16x8_t bh[kHB], bl[kHB];
+#pragma unroll
+    for (int hb = 0; hb < kHB; ++hb) {
+      bh[hb] = as_bf16x8(make_uint4(phi[hb][0], phi[hb][1], phi[hb][2], phi[hb][3]));
+      bl[hb] = as_bf16x8(make_uint4(plo[hb][0], plo[hb][1], plo[hb][2], plo[hb][3]));
+    }
     // transposed value reads run one block ahead of their MFMAs
     s16x8_t vf[2];
     vf[0] = read_v(0);
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
+      // the loads of tile it+2 go out between the value MFMAs, where the
+      // matrix pipe, not instruction issue, sets the pace
+      if (ATTN_MLA_DMA_IN_PV && pf && db % ATTN_MLA_DMA_EVERY == 0 &&
+          db / ATTN_MLA_DMA_EVERY < kDmaPerWave && db / ATTN_MLA_DMA_EVERY < my_pieces)
+        issue_piece(std::integral_constant<int, (I + 2) % 3>{}, it + 2,
+                    db / ATTN_MLA_DMA_EVERY);
       const int cur = db & 1;
       if (db + 1 < kDB) vf[cur ^ 1] = read_v(db + 1);
       const bf16x8_t av = __builtin_bit_cast(bf16x8_t, vf[cur]);
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
+      for (int hb = 0; hb < kHB; ++hb) {
         o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh[hb], o[db][hb], 0, 0, 0);
         o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl[hb], o[db][hb], 0, 0, 0);
       }
@@ -384,7 +416,11 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
   auto step = [&](auto stage_tag, int it) {
     constexpr int I = decltype(stage_tag)::value;
     if (it >= ntiles) return;
-    if (it + 1 < ntiles) wait_vmcnt<kDmaPerWave>();
+    if (it + 1 < ntiles) {
+      // the next tile's loads (this wave's share) may still be in flight
+      if (my_pieces == kDmaPerWave) wait_vmcnt<kDmaPerWave>();
+      else wait_vmcnt<kDmaPerWave - 1>();
+    }
     else wait_vmcnt<0>();
     lds_barrier();
     compute_tile(stage_tag, it, it + 2 < ntiles);
@@ -403,12 +439,12 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
 
   // per-head sums of the four lane groups, then write this wave's heads
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
+  for (int hb = 0; hb < kHB; ++hb) {
     l[hb] += xor16(l[hb]);
     l[hb] += xor32(l[hb]);
   }
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
+  for (int hb = 0; hb < kHB; ++hb) {
     const int c = hw0 + 16 * hb + li;
     if (c >= a.ncol) continue;
     const bool empty = !(l[hb] > 0.f);
@@ -461,12 +497,14 @@ hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
   a.head_chunks = head_chunks;
   a.scale_log2 = scale_log2;
   const long long grid = (long long)B * S * head_chunks;
-  if (block_table)
-    hipLaunchKernelGGL(mla_decode_mfma<kAddrPaged>, dim3((unsigned)grid),
-                       dim3(kNW * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL(mla_decode_mfma<kAddrDense>, dim3((unsigned)grid),
-                       dim3(kNW * 64), 0, stream, a);
+  const dim3 g((unsigned)grid), blk(kNW * 64);
+  if (block_table) {
+    if (L > 1) hipLaunchKernelGGL((mla_decode_mfma<kAddrPaged, true>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((mla_decode_mfma<kAddrPaged, false>), g, blk, 0, stream, a);
+  } else {
+    if (L > 1) hipLaunchKernelGGL((mla_decode_mfma<kAddrDense, true>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((mla_decode_mfma<kAddrDense, false>), g, blk, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
