@@ -387,6 +387,11 @@ def main():
             "kernel_us": round(call_ms * 1e3, 2),
         },
     }
+    del ks[1:], vs[1:]
+    probe = probe_read_gbs(dev)
+    res["read_probe"] = {"GBps": round(probe, 1),
+                         "value_pct": round(100 * value / probe, 1),
+                         "achieved_pct": round(100 * achieved / probe, 1)}
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
@@ -451,7 +456,45 @@ def bench_mla(args, w, dev):
     }
     print(f"bench: {ms * 1e3:.1f} us/step, {value:.0f} GB/s, {tflops:.0f} TFLOP/s",
           file=sys.stderr, flush=True)
+    del lats[1:]
+    probe = probe_read_gbs(dev)
+    res["read_probe"] = {"GBps": round(probe, 1),
+                         "value_pct": round(100 * value / probe, 1)}
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline_mla(w, inp, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_mla(w, inp, seconds):
+    """The float64 MLA oracle on the host over whole sequences of the
+    workload, repeated until `seconds` have passed."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    q = inp["q"].cpu()
+    lat = inp["latent"].cpu()
+    sl = None if inp["seq_lens"] is None else inp["seq_lens"].cpu()
+    B, T = w["B"], w["T_cap"]
+    row_bytes = (w["d_c"] + w["d_rope"]) * 2
+    done, n, i = 0, 0, 0
+    t0 = time.perf_counter()
+    while True:
+        b = i % B
+        oracle.mla_decode_ref(q, lat, w["d_c"], w["scale"], sl, batches=[b])
+        done += row_bytes * (T if sl is None else int(sl[b].clamp(0, T)))
+        n += 1
+        i += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} sequences of {w['name']} ({B} per step) in {dt:.1f} s, "
+                      "float64 numpy"}
 
 
 if __name__ == "__main__":
