@@ -38,11 +38,8 @@
 #ifndef ATTN_MLA_QK_AHEAD  // k-steps the score operand reads run ahead
 #define ATTN_MLA_QK_AHEAD 2
 #endif
-#ifndef ATTN_MLA_DMA_IN_PV  // issue the next loads in the value loop
-#define ATTN_MLA_DMA_IN_PV 0
-#endif
-#ifndef ATTN_MLA_DMA_EVERY  // value blocks between two of those loads
-#define ATTN_MLA_DMA_EVERY 3
+#ifndef ATTN_MLA_STAGES  // LDS tile stages
+#define ATTN_MLA_STAGES 4
 #endif
 #ifndef ATTN_MLA_WAVES  // waves per group (128 heads split among them)
 #define ATTN_MLA_WAVES 4
@@ -54,6 +51,11 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// s_buffer_load_dword (uniform offset, through the scalar cache).
+__device__ int scalar_buffer_load_i32(u32x4 rsrc, int offset, int cachepolicy) __asm(
+    "llvm.amdgcn.s.buffer.load.i32");
 
 constexpr int kDK = 576;                 // latent row: 512 content + 64 rope
 constexpr int kDV = 512;                 // value columns (the content part)
@@ -69,24 +71,34 @@ constexpr int kPieces = kTileBytes / 1024;              // 1 KiB loads per tile
 constexpr int kDmaPerWave = (kPieces + kNW - 1) / kNW;  // at most, per wave
 constexpr int kKS = kDK / 32;            // 18 score k-steps
 constexpr int kDB = kDV / 16;            // 32 value blocks
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor flags (gfx9)
 static_assert(kTileBytes % 1024 == 0 && (kNW == 4 || kNW == 8), "tile split");
 
+constexpr int kStages = ATTN_MLA_STAGES;  // tiles in LDS: kStages - 1 loading
+static_assert(kStages == 3 || kStages == 4, "stages");
 __shared__ __attribute__((aligned(1024))) unsigned char g_stage0[kTileBytes];
 __shared__ __attribute__((aligned(1024))) unsigned char g_stage1[kTileBytes];
 __shared__ __attribute__((aligned(1024))) unsigned char g_stage2[kTileBytes];
+#if ATTN_MLA_STAGES == 4
+__shared__ __attribute__((aligned(1024))) unsigned char g_stage3[kTileBytes];
+#endif
 
 template <int I>
 ATTN_DEV unsigned char* stage() {
   if constexpr (I == 0) return g_stage0;
   else if constexpr (I == 1) return g_stage1;
-  else return g_stage2;
+  else if constexpr (I == 2) return g_stage2;
+#if ATTN_MLA_STAGES == 4
+  else return g_stage3;
+#endif
 }
 
-// Chunk swizzle: logical 16-byte chunk c of row t sits at chunk c ^ swz(t).
-// Sixteen consecutive rows at one chunk (score operand) and four consecutive
-// rows at two adjacent chunks (transposed value operand) land on distinct
-// banks.  The xor stays inside an aligned group of 8 chunks.
-ATTN_DEV int swz(int t) { return 2 * ((t >> 1) & 3) + ((t >> 3) & 1); }
+// Chunk swizzle: logical 16-byte chunk c of row t sits at chunk c ^ swz(t);
+// the xor stays inside an aligned group of 8 chunks.  Chosen by measured LDS
+// read rate of the two read patterns (16 rows at one chunk for the score
+// operand, 16 rows at two adjacent chunks for the transposed value operand).
+// swz(t + 16) = swz(t): the two 16-row halves of a tile share their layout.
+ATTN_DEV int swz(int t) { return t & 7; }
 
 ATTN_DEV bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
@@ -101,6 +113,46 @@ ATTN_DEV void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
   const float ra = a - __uint_as_float(hi << 16);
   const float rb = b - __uint_as_float(hi & 0xffff0000u);
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{ra, rb}, bf16x2_v));
+}
+
+// The MFMAs are written out (v_mfma_f32_16x16x32_bf16, accumulating in
+// place).  The compiler's own form keeps no accumulator in place once the
+// 256 AGPRs are all taken by o: it routes each result through a scratch
+// register and shuttles accumulators between the register files, and an
+// MFMA that overwrites a register an earlier one still reads stalls the
+// matrix pipe; in-place accumulation back to back runs at full rate.  The
+// score accumulators are VGPRs, the value accumulators AGPRs.  Since the
+// compiler does not see these as MFMAs, the hazards it would cover are
+// covered here: VALU reads of an MFMA result wait out its latency
+// (mfma_drain_*), and operands written by VALU instructions get wait states
+// before their first MFMA (the s_nop in the value product's prologue).
+ATTN_DEV void mfma_first_v(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+ATTN_DEV void mfma_v(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+ATTN_DEV void mfma_a(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+#define ATTN_MFMA_DRAIN "s_nop 15\n\ts_nop 15"
+
+// One direct-to-LDS buffer load: lane l copies the 16 bytes at `base` + voff
+// (the descriptor covers `bytes`) to LDS address lds + 16 l.  Written out so
+// the compiler does not track it: its own form makes every later LDS read
+// it cannot tell apart from the destination wait for all such loads, which
+// empties the prefetch pipeline.  Every wait on these loads is explicit
+// (wait_vmcnt before the barrier that publishes a tile, and at the end).
+ATTN_DEV void dma_16B(const void* base, uint32_t bytes, uint32_t voff, uint32_t lds) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const u32x4 rsrc = {(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, bytes, (uint32_t)kBufferWord3};
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %2, 0 offen lds"
+      :
+      : "v"(voff), "s"(lds), "s"(rsrc)
+      : "m0");
 }
 
 // Work-group barrier that is also a compiler memory barrier, without the
@@ -189,66 +241,82 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
     for (int db = 0; db < kDB; ++db) o[db][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Direct-to-LDS loads of tile `it` into stage I: this wave's 9 KiB.  LDS
-  // chunk p of the tile holds row p / 72, logical chunk (p % 72) ^ swz(row).
-  // Per-lane byte offsets inside a full tile of this wave's direct-to-LDS
-  // loads: LDS chunk p = blk*64 + lane holds row p/72, logical chunk
-  // (p%72) ^ swz(row).  Offsets are < 2^16, two per register.
-  // This wave's loads are blocks wave, wave + kNW, ... of the tile's kPieces.
-  const int my_pieces = (kPieces - wave + kNW - 1) / kNW;
+  // Direct-to-LDS loads of a tile: LDS chunk p = blk*64 + lane holds row
+  // p / 72, logical chunk (p % 72) ^ swz(row).  A 1 KiB block blk < 18 lies
+  // in rows 0..15, the others in rows 16..31, so every load reads from one
+  // 16-row half (one page of a paged cache).  This wave's loads are blocks
+  // wave, wave + kNW, ... of the tile's kPieces; their per-lane byte offsets
+  // from the start of their half are < 2^16, two per register.
+  const int my_pieces =
+      kPieces % kNW == 0 ? kDmaPerWave : (kPieces - wave + kNW - 1) / kNW;
   uint32_t dma_off[(kDmaPerWave + 1) / 2];
-  uint32_t hi_rows = 0;  // bit j: load j of this lane is in the tile's rows 16..31
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j) {
     const int p = min(wave + j * kNW, kPieces - 1) * 64 + lane;
     const int t = p / kCPR;
-    const uint32_t off = t * kRowBytes + 16 * ((p - t * kCPR) ^ swz(t));
+    const uint32_t off = (t & 15) * kRowBytes + 16 * ((p - t * kCPR) ^ swz(t));
     if (j & 1) dma_off[j >> 1] |= off << 16;
     else dma_off[j >> 1] = off;
-    hi_rows |= (t >= 16 ? 1u : 0u) << j;
   }
 
-  // Page ids of the tile in each stage (paged caches only): lane k holds
-  // id k of the tile's pages.
-  int pidv[3] = {0, 0, 0};
+  // Pages of the two 16-row halves of the tile in each stage (paged caches
+  // only), clamped to the pool.  Scalar buffer loads of the sequence's
+  // table row (the scalar counter keeps them out of the vector-load waits
+  // of the tile pipeline), a tile ahead of their use.
+  int pid[kStages][2] = {};
+  u32x4 table_rsrc = {};
+  if constexpr (MODE == kAddrPaged) {
+    const uint64_t t = (uint64_t)(uintptr_t)pg.table;
+    table_rsrc = u32x4{(uint32_t)t, (uint32_t)(t >> 32) & 0xffffu,
+                       (uint32_t)a.max_pages * 4u, (uint32_t)kBufferWord3};
+  }
   auto fetch_pages = [&](auto stage_tag, int it) {
     constexpr int I = decltype(stage_tag)::value;
-    if constexpr (MODE == kAddrPaged) pidv[I] = tile_pages_lanes(pg, p0 + it * kTT, lane);
+    if constexpr (MODE == kAddrPaged) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = min((p0 + it * kTT + 16 * h) >> pg.shift, pg.last);
+        const int v = scalar_buffer_load_i32(table_rsrc, 4 * j, 0);
+        pid[I][h] = v < 0 ? 0 : (v >= pg.num_pages ? pg.num_pages - 1 : v);
+      }
+    }
+  };
+  // waits for the page ids of the tile whose loads go out next (issued a
+  // tile earlier) right after the barrier, where no LDS read is in flight
+  auto pages_ready = [&](auto stage_tag) {
+    constexpr int I = decltype(stage_tag)::value;
+    if constexpr (MODE == kAddrPaged) {
+      const int lo = pid[I][0], hi = pid[I][1];
+      asm volatile("" ::"s"(lo), "s"(hi));
+    }
   };
 
-  // Direct-to-LDS load j (of kDmaPerWave) of tile `it` into stage I.
+  // Direct-to-LDS load j (of kDmaPerWave) of tile `it` into stage I: a
+  // buffer load whose descriptor starts at the first row of the block's
+  // half.
   auto issue_piece = [&](auto stage_tag, int it, int j) {
     constexpr int I = decltype(stage_tag)::value;
     const int base = p0 + it * kTT;
-    const int nvalid = p1 - base;  // rows of this tile inside the split
+    const int nvalid = p1 - base;  // rows of this tile inside the split (>= 1)
     const int blk = wave + j * kNW;
     uint32_t off = (dma_off[j >> 1] >> (16 * (j & 1))) & 0xffffu;
-    bool hi = (hi_rows >> j) & 1;
-    if (nvalid < kTT) {  // uniform: the split's last, partial tile
-      const int p = blk * 64 + lane;
-      const int t = p / kCPR;
-      // a row past the split reads the same chunk of the tile's first row
-      if (t >= nvalid) {
-        off = 16 * (p - t * kCPR);
-        hi = false;
-      }
-    }
-    const unsigned char* src;
+    // Rows past the split (the split's last tile may be partial) read chunk
+    // `lane` of the first row of the half instead, or of the tile when the
+    // whole upper half is past the split: finite data that the softmax
+    // masks.  A lane's row is past the split iff its offset from the half is
+    // at least (nvalid - 16 * half) rows.
+    int half = blk >= kPieces / 2 ? 1 : 0;  // uniform
+    const int lim = (nvalid - 16 * half) * kRowBytes;
+    if (nvalid <= 16) half = 0;
+    off = (int)off < lim ? off : 16u * lane;
+    long long row;  // first row of the half in the latent (or pool) rows
     if constexpr (MODE == kAddrPaged) {
-      // rows 0..15 sit in one page, rows 16..31 in one page; `off` counts
-      // rows from the tile's start, so the upper half's base is shifted back
-      // by 16 rows (the sum stays inside the pool)
-      int id[3];
-      page_ids_from_lanes(pg, pidv[I], id);
-      const int rlo = paged_row(pg, id, base, base);
-      const int rhi = paged_row(pg, id, base, base + 16) - 16;
-      src = lat_b + ((long long)(hi ? rhi : rlo) * kRowBytes + off);
+      row = (long long)pid[I][half] * pg.stride + ((base + 16 * half) & ((1 << pg.shift) - 1));
     } else {
-      src = lat_b + (size_t)base * kRowBytes + off;
+      row = base + 16 * half;
     }
-    __builtin_amdgcn_global_load_lds(
-        (const void*)src,
-        (__attribute__((address_space(3))) void*)(stage<I>() + blk * 1024), 16, 0, 0);
+    dma_16B(lat_b + row * kRowBytes, kTileBytes / 2, off,
+            (uint32_t)(uintptr_t)(stage<I>() + blk * 1024));
   };
   auto issue_tile = [&](auto stage_tag, int it) {
 #pragma unroll
@@ -256,16 +324,20 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
       if (j < my_pieces) issue_piece(stage_tag, it, j);
   };
 
-  // Computes tile `it` from stage I; when `pf` is set, the loads of tile
-  // it+2 (into stage (I+2)%3) are issued piece by piece between the score
-  // MFMAs, so their issue stalls overlap matrix work.
-  auto compute_tile = [&](auto stage_tag, int it, bool pf) {
+  // Computes tile `it` from stage I.  The loads of tile it+2 (into stage
+  // (I+2)%3) are issued piece by piece between the score MFMAs, so their
+  // issue stalls overlap matrix work.  Past the last tile they reload the
+  // last tile (an L2 hit, never used): every step issues the same loads, so
+  // the score loop has no branch and the vmcnt waits are the same for all
+  // steps.
+  auto compute_tile = [&](auto stage_tag, int it) {
     constexpr int I = decltype(stage_tag)::value;
     const unsigned char* tile = stage<I>();
     const int base = p0 + it * kTT;
+    const int next = min(it + kStages - 1, ntiles - 1);
     // page ids of tile it+3 (its stage is this one), ahead of the loads of
     // tile it+2 below
-    fetch_pages(stage_tag, it + 3);
+    fetch_pages(stage_tag, min(it + kStages, ntiles - 1));
 
     // scores.  Chunk (4*ks + lg) ^ swz(t) = 8*(ks/2) + ((4*(ks&1) + lg) ^ swz(t)):
     // two base addresses per row block, the rest is an immediate offset.
@@ -277,7 +349,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
       for (int e = 0; e < 2; ++e)
         abase[tb][e] = tile + t * kRowBytes + 16 * ((4 * e + lg) ^ swz(t));
     }
-    f32x4_t sc[2][kHB] = {};
+    f32x4_t sc[2][kHB];
     // operand reads run kAhead k-steps ahead of the MFMAs that use them
     constexpr int kAhead = ATTN_MLA_QK_AHEAD;
     uint4 af[kAhead + 1][2];
@@ -288,9 +360,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
         af[k0][tb] = *(const uint4*)(abase[tb][k0 & 1] + 128 * (k0 >> 1));
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      if (!ATTN_MLA_DMA_IN_PV && pf && (ks & 1) == 0 && (ks >> 1) < kDmaPerWave &&
-          (ks >> 1) < my_pieces)
-        issue_piece(std::integral_constant<int, (I + 2) % 3>{}, it + 2, ks >> 1);
+      if ((ks & 1) == 0 && (ks >> 1) < kDmaPerWave && (ks >> 1) < my_pieces)
+        issue_piece(std::integral_constant<int, (I + kStages - 1) % kStages>{}, next, ks >> 1);
       const int cur = ks % (kAhead + 1);
       const int kn = ks + kAhead;
       if (kn < kKS) {
@@ -301,10 +372,15 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int hb = 0; hb < kHB; ++hb)
-          sc[tb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(af[cur][tb]), as_bf16x8(qf[hb][ks]), sc[tb][hb], 0, 0, 0);
+        for (int hb = 0; hb < kHB; ++hb) {
+          if (ks == 0) mfma_first_v(sc[tb][hb], as_bf16x8(af[cur][tb]), as_bf16x8(qf[hb][ks]));
+          else mfma_v(sc[tb][hb], as_bf16x8(af[cur][tb]), as_bf16x8(qf[hb][ks]));
+        }
     }
+    // the softmax reads the scores with VALU instructions
+    static_assert(kHB == 2, "score drain lists four accumulators");
+    asm volatile(ATTN_MFMA_DRAIN
+                 : "+v"(sc[0][0]), "+v"(sc[0][1]), "+v"(sc[1][0]), "+v"(sc[1][1]));
 
     // online softmax per head (lazy maximum); weights split into bf16 hi+lo
     const bool full = base + kTT <= p1;  // uniform: no masked row in the tile
@@ -337,6 +413,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
       if (mt > m[hb] + 8.f) {
         const float al = fast_exp2(m[hb] - mt);
         l[hb] *= al;
+        asm volatile(ATTN_MFMA_DRAIN ::: "memory");
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
           // keep the accumulators in AGPRs across this rare VALU update
@@ -362,24 +439,24 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
 
     // values: transposed 4x16 reads of rows 4*lg + li/4 (and +16), columns
     // 16*db + 4*(li&3).  Chunk 2*db + ((li&3)>>1) swizzled = 8*(db/4) +
-    // ((2*(db&3) + ((li&3)>>1)) ^ swz(t)): four bases per row, immediate rest.
+    // ((2*(db&3) + ((li&3)>>1)) ^ swz(t)): four bases, the rest (including
+    // the +16 rows, which share the swizzle) an immediate offset.  (One base
+    // per read pair also keeps the alias information on every read, so the
+    // compiler does not wait for the direct-to-LDS loads of other stages.)
     const int t0 = 4 * lg + (li >> 2);
     const int half = ((li & 3) & 1) * 8;
-    const unsigned char* vbase[2][4];
+    const unsigned char* vbase[4];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int t = t0 + 16 * r;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        vbase[r][e] = tile + t * kRowBytes + 16 * ((2 * e + ((li & 3) >> 1)) ^ swz(t)) + half;
-    }
+    for (int e = 0; e < 4; ++e)
+      vbase[e] = tile + t0 * kRowBytes + 16 * ((2 * e + ((li & 3) >> 1)) ^ swz(t0)) + half;
     typedef s16x4_t __attribute__((address_space(3))) * lds_s16x4;
     auto read_v = [&](int db) {
       const int imm = 128 * (db >> 2);
       const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4)(__attribute__((address_space(3))) unsigned char*)(vbase[0][db & 3] + imm));
+          (lds_s16x4)(__attribute__((address_space(3))) unsigned char*)(vbase[db & 3] + imm));
       const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4)(__attribute__((address_space(3))) unsigned char*)(vbase[1][db & 3] + imm));
+          (lds_s16x4)(__attribute__((address_space(3))) unsigned char*)(vbase[db & 3] +
+                                                                      (16 * kRowBytes + imm)));
       return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     typedef short s16x8_t __attribute__((ext_vector_type(8)));
@@ -389,24 +466,20 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
       bh[hb] = as_bf16x8(make_uint4(phi[hb][0], phi[hb][1], phi[hb][2], phi[hb][3]));
       bl[hb] = as_bf16x8(make_uint4(plo[hb][0], plo[hb][1], plo[hb][2], plo[hb][3]));
     }
+    // wait states between the VALU writes of the weights and their MFMAs
+    asm volatile("s_nop 4" ::"v"(bh[0]), "v"(bl[0]), "v"(bh[1]), "v"(bl[1]));
     // transposed value reads run one block ahead of their MFMAs
     s16x8_t vf[2];
     vf[0] = read_v(0);
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
-      // the loads of tile it+2 go out between the value MFMAs, where the
-      // matrix pipe, not instruction issue, sets the pace
-      if (ATTN_MLA_DMA_IN_PV && pf && db % ATTN_MLA_DMA_EVERY == 0 &&
-          db / ATTN_MLA_DMA_EVERY < kDmaPerWave && db / ATTN_MLA_DMA_EVERY < my_pieces)
-        issue_piece(std::integral_constant<int, (I + 2) % 3>{}, it + 2,
-                    db / ATTN_MLA_DMA_EVERY);
       const int cur = db & 1;
       if (db + 1 < kDB) vf[cur ^ 1] = read_v(db + 1);
       const bf16x8_t av = __builtin_bit_cast(bf16x8_t, vf[cur]);
 #pragma unroll
       for (int hb = 0; hb < kHB; ++hb) {
-        o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh[hb], o[db][hb], 0, 0, 0);
-        o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl[hb], o[db][hb], 0, 0, 0);
+        mfma_a(o[db][hb], av, bh[hb]);
+        mfma_a(o[db][hb], av, bl[hb]);
       }
     }
   };
@@ -416,27 +489,41 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
   auto step = [&](auto stage_tag, int it) {
     constexpr int I = decltype(stage_tag)::value;
     if (it >= ntiles) return;
-    if (it + 1 < ntiles) {
-      // the next tile's loads (this wave's share) may still be in flight
-      if (my_pieces == kDmaPerWave) wait_vmcnt<kDmaPerWave>();
-      else wait_vmcnt<kDmaPerWave - 1>();
-    }
-    else wait_vmcnt<0>();
+    // the next tile's loads (this wave's share) may still be in flight
+    if (my_pieces == kDmaPerWave) wait_vmcnt<(kStages - 2) * kDmaPerWave>();
+    else wait_vmcnt<(kStages - 2) * (kDmaPerWave - 1)>();
     lds_barrier();
-    compute_tile(stage_tag, it, it + 2 < ntiles);
+    pages_ready(std::integral_constant<int, (I + kStages - 1) % kStages>{});
+    compute_tile(stage_tag, it);
   };
 
-  fetch_pages(std::integral_constant<int, 0>{}, 0);
-  fetch_pages(std::integral_constant<int, 1>{}, 1);
-  fetch_pages(std::integral_constant<int, 2>{}, 2);
-  if (ntiles > 0) issue_tile(std::integral_constant<int, 0>{}, 0);
-  if (ntiles > 1) issue_tile(std::integral_constant<int, 1>{}, 1);
-  for (int it = 0; it < ntiles; it += 3) {
-    step(std::integral_constant<int, 0>{}, it);
-    step(std::integral_constant<int, 1>{}, it + 1);
-    step(std::integral_constant<int, 2>{}, it + 2);
+  if (ntiles > 0) {
+    fetch_pages(std::integral_constant<int, 0>{}, 0);
+    fetch_pages(std::integral_constant<int, 1>{}, min(1, ntiles - 1));
+    fetch_pages(std::integral_constant<int, 2>{}, min(2, ntiles - 1));
+    if constexpr (kStages == 4) fetch_pages(std::integral_constant<int, 3>{}, min(3, ntiles - 1));
+    issue_tile(std::integral_constant<int, 0>{}, 0);
+    issue_tile(std::integral_constant<int, 1>{}, min(1, ntiles - 1));
+    if constexpr (kStages == 4) issue_tile(std::integral_constant<int, 2>{}, min(2, ntiles - 1));
+    // the query fragments (and the first tiles) land here, once: the loop
+    // then carries no wait on the query loads
+    wait_vmcnt<0>();
+    for (int it = 0; it < ntiles; it += kStages) {
+      step(std::integral_constant<int, 0>{}, it);
+      step(std::integral_constant<int, 1>{}, it + 1);
+      step(std::integral_constant<int, 2>{}, it + 2);
+      if constexpr (kStages == 4) step(std::integral_constant<int, 3 % kStages>{}, it + 3);
+    }
+    // the last two steps' loads (unused) must land before the group's LDS
+    // is released
+    wait_vmcnt<0>();
   }
 
+  asm volatile(ATTN_MFMA_DRAIN ::: "memory");
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
+#pragma unroll
+    for (int hb = 0; hb < kHB; ++hb) asm volatile("" : "+a"(o[db][hb]));
   // per-head sums of the four lane groups, then write this wave's heads
 #pragma unroll
   for (int hb = 0; hb < kHB; ++hb) {
