@@ -76,22 +76,10 @@ static_assert(kTileBytes % 1024 == 0 && (kNW == 4 || kNW == 8), "tile split");
 
 constexpr int kStages = ATTN_MLA_STAGES;  // tiles in LDS: kStages - 1 loading
 static_assert(kStages == 3 || kStages == 4, "stages");
-__shared__ __attribute__((aligned(1024))) unsigned char g_stage0[kTileBytes];
-__shared__ __attribute__((aligned(1024))) unsigned char g_stage1[kTileBytes];
-__shared__ __attribute__((aligned(1024))) unsigned char g_stage2[kTileBytes];
-#if ATTN_MLA_STAGES == 4
-__shared__ __attribute__((aligned(1024))) unsigned char g_stage3[kTileBytes];
-#endif
+__shared__ __attribute__((aligned(1024))) unsigned char g_stages[kStages * kTileBytes];
 
-template <int I>
-ATTN_DEV unsigned char* stage() {
-  if constexpr (I == 0) return g_stage0;
-  else if constexpr (I == 1) return g_stage1;
-  else if constexpr (I == 2) return g_stage2;
-#if ATTN_MLA_STAGES == 4
-  else return g_stage3;
-#endif
-}
+// LDS of the stage that holds tile `it`
+ATTN_DEV unsigned char* stage_of(int it) { return g_stages + (it % kStages) * kTileBytes; }
 
 // Chunk swizzle: logical 16-byte chunk c of row t sits at chunk c ^ swz(t);
 // the xor stays inside an aligned group of 8 chunks.  Chosen by measured LDS
@@ -263,30 +251,31 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
   // only), clamped to the pool.  Scalar buffer loads of the sequence's
   // table row (the scalar counter keeps them out of the vector-load waits
   // of the tile pipeline), a tile ahead of their use.
-  int pid[kStages][2] = {};
+  int pid_cur[2] = {}, pid_next[2] = {};  // tile it + kStages - 1, tile it + kStages
   u32x4 table_rsrc = {};
   if constexpr (MODE == kAddrPaged) {
     const uint64_t t = (uint64_t)(uintptr_t)pg.table;
     table_rsrc = u32x4{(uint32_t)t, (uint32_t)(t >> 32) & 0xffffu,
                        (uint32_t)a.max_pages * 4u, (uint32_t)kBufferWord3};
   }
-  auto fetch_pages = [&](auto stage_tag, int it) {
-    constexpr int I = decltype(stage_tag)::value;
+  auto fetch_pages = [&](int it, int (&pid)[2]) {
     if constexpr (MODE == kAddrPaged) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int j = min((p0 + it * kTT + 16 * h) >> pg.shift, pg.last);
         const int v = scalar_buffer_load_i32(table_rsrc, 4 * j, 0);
-        pid[I][h] = v < 0 ? 0 : (v >= pg.num_pages ? pg.num_pages - 1 : v);
+        pid[h] = v < 0 ? 0 : (v >= pg.num_pages ? pg.num_pages - 1 : v);
       }
     }
   };
-  // waits for the page ids of the tile whose loads go out next (issued a
-  // tile earlier) right after the barrier, where no LDS read is in flight
-  auto pages_ready = [&](auto stage_tag) {
-    constexpr int I = decltype(stage_tag)::value;
+  // the page ids of the tile whose loads go out next (fetched a tile
+  // earlier) become current; their wait lands right after the barrier,
+  // where no LDS read is in flight
+  auto pages_ready = [&]() {
     if constexpr (MODE == kAddrPaged) {
-      const int lo = pid[I][0], hi = pid[I][1];
+      pid_cur[0] = pid_next[0];
+      pid_cur[1] = pid_next[1];
+      const int lo = pid_cur[0], hi = pid_cur[1];
       asm volatile("" ::"s"(lo), "s"(hi));
     }
   };
@@ -294,8 +283,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
   // Direct-to-LDS load j (of kDmaPerWave) of tile `it` into stage I: a
   // buffer load whose descriptor starts at the first row of the block's
   // half.
-  auto issue_piece = [&](auto stage_tag, int it, int j) {
-    constexpr int I = decltype(stage_tag)::value;
+  auto issue_piece = [&](const int (&pid)[2], int it, int j) {
     const int base = p0 + it * kTT;
     const int nvalid = p1 - base;  // rows of this tile inside the split (>= 1)
     const int blk = wave + j * kNW;
@@ -311,17 +299,17 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
     off = (int)off < lim ? off : 16u * lane;
     long long row;  // first row of the half in the latent (or pool) rows
     if constexpr (MODE == kAddrPaged) {
-      row = (long long)pid[I][half] * pg.stride + ((base + 16 * half) & ((1 << pg.shift) - 1));
+      row = (long long)pid[half] * pg.stride + ((base + 16 * half) & ((1 << pg.shift) - 1));
     } else {
       row = base + 16 * half;
     }
     dma_16B(lat_b + row * kRowBytes, kTileBytes / 2, off,
-            (uint32_t)(uintptr_t)(stage<I>() + blk * 1024));
+            (uint32_t)(uintptr_t)(stage_of(it) + blk * 1024));
   };
-  auto issue_tile = [&](auto stage_tag, int it) {
+  auto issue_tile = [&](const int (&pid)[2], int it) {
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j)
-      if (j < my_pieces) issue_piece(stage_tag, it, j);
+      if (j < my_pieces) issue_piece(pid, it, j);
   };
 
   // Computes tile `it` from stage I.  The loads of tile it+2 (into stage
@@ -330,14 +318,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
   // last tile (an L2 hit, never used): every step issues the same loads, so
   // the score loop has no branch and the vmcnt waits are the same for all
   // steps.
-  auto compute_tile = [&](auto stage_tag, int it) {
-    constexpr int I = decltype(stage_tag)::value;
-    const unsigned char* tile = stage<I>();
+  auto compute_tile = [&](int it) {
+    const unsigned char* tile = stage_of(it);
     const int base = p0 + it * kTT;
     const int next = min(it + kStages - 1, ntiles - 1);
     // page ids of tile it+3 (its stage is this one), ahead of the loads of
     // tile it+2 below
-    fetch_pages(stage_tag, min(it + kStages, ntiles - 1));
+    fetch_pages(min(it + kStages, ntiles - 1), pid_next);
 
     // scores.  Chunk (4*ks + lg) ^ swz(t) = 8*(ks/2) + ((4*(ks&1) + lg) ^ swz(t)):
     // two base addresses per row block, the rest is an immediate offset.
@@ -361,7 +348,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
       if ((ks & 1) == 0 && (ks >> 1) < kDmaPerWave && (ks >> 1) < my_pieces)
-        issue_piece(std::integral_constant<int, (I + kStages - 1) % kStages>{}, next, ks >> 1);
+        issue_piece(pid_cur, next, ks >> 1);
       const int cur = ks % (kAhead + 1);
       const int kn = ks + kAhead;
       if (kn < kKS) {
@@ -486,34 +473,28 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
 
   // One pipeline step: tile `it` lives in stage I; tile it+2 goes to stage
   // (I+2)%3, which every wave finished reading before the barrier.
-  auto step = [&](auto stage_tag, int it) {
-    constexpr int I = decltype(stage_tag)::value;
+  auto step = [&](int it) {
     if (it >= ntiles) return;
     // the next tile's loads (this wave's share) may still be in flight
     if (my_pieces == kDmaPerWave) wait_vmcnt<(kStages - 2) * kDmaPerWave>();
     else wait_vmcnt<(kStages - 2) * (kDmaPerWave - 1)>();
     lds_barrier();
-    pages_ready(std::integral_constant<int, (I + kStages - 1) % kStages>{});
-    compute_tile(stage_tag, it);
+    pages_ready();
+    compute_tile(it);
   };
 
   if (ntiles > 0) {
-    fetch_pages(std::integral_constant<int, 0>{}, 0);
-    fetch_pages(std::integral_constant<int, 1>{}, min(1, ntiles - 1));
-    fetch_pages(std::integral_constant<int, 2>{}, min(2, ntiles - 1));
-    if constexpr (kStages == 4) fetch_pages(std::integral_constant<int, 3>{}, min(3, ntiles - 1));
-    issue_tile(std::integral_constant<int, 0>{}, 0);
-    issue_tile(std::integral_constant<int, 1>{}, min(1, ntiles - 1));
-    if constexpr (kStages == 4) issue_tile(std::integral_constant<int, 2>{}, min(2, ntiles - 1));
+#pragma unroll
+    for (int t = 0; t + 1 < kStages; ++t) {
+      int pid[2];
+      fetch_pages(min(t, ntiles - 1), pid);
+      issue_tile(pid, min(t, ntiles - 1));
+    }
+    fetch_pages(min(kStages - 1, ntiles - 1), pid_next);
     // the query fragments (and the first tiles) land here, once: the loop
     // then carries no wait on the query loads
     wait_vmcnt<0>();
-    for (int it = 0; it < ntiles; it += kStages) {
-      step(std::integral_constant<int, 0>{}, it);
-      step(std::integral_constant<int, 1>{}, it + 1);
-      step(std::integral_constant<int, 2>{}, it + 2);
-      if constexpr (kStages == 4) step(std::integral_constant<int, 3 % kStages>{}, it + 3);
-    }
+    for (int it = 0; it < ntiles; ++it) step(it);
     // the last two steps' loads (unused) must land before the group's LDS
     // is released
     wait_vmcnt<0>();
