@@ -11,10 +11,9 @@
 // One work group = one (sequence, split) and up to 128 heads: four waves,
 // each owning 32 heads, share every latent tile, so the latent is read from
 // HBM once.  Tiles of 32 rows (36 KiB) go straight from HBM into LDS with
-// 16-byte direct-to-LDS loads, two tiles ahead of the one being computed,
-// through three separate stage buffers (the loop is unrolled by three so
-// each stage is a distinct LDS object; the waits on those loads are
-// explicit).  Score operands are read from the row-major tile; value
+// 16-byte direct-to-LDS buffer loads, three tiles ahead of the one being
+// computed, through four stage buffers; every wait on those loads is
+// explicit.  Score operands are read from the row-major tile; value
 // operands come transposed through ds_read_b64_tr_b16.  Rows are swizzled
 // in 16-byte chunks so both read patterns are free of bank conflicts.
 //
@@ -24,9 +23,8 @@
 // Paged latent caches ([num_pages, P, 576], P a power of two >= 16; the
 // paging the baidu article, section 四.3, names for MLA): splits and tiles
 // start at multiples of 32 positions, so each 16-row half of a tile lies in
-// one page and a tile needs two page ids.  They are fetched a tile ahead
-// with one vector load, issued before the direct-to-LDS loads of the tile
-// two ahead, so the pipeline's own vmcnt wait already covers it.
+// one page and a tile needs two page ids, read with scalar loads a step
+// ahead of the tile's loads.
 
 #include <type_traits>
 
@@ -283,8 +281,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
   // Direct-to-LDS load j (of kDmaPerWave) of tile `it` into stage I: a
   // buffer load whose descriptor starts at the first row of the block's
   // half.
-  auto issue_piece = [&](const int (&pid)[2], int it, int j) {
-    const int base = p0 + it * kTT;
+  // Load j of tile `src` into the stage of tile `dst` (dst = src, or a
+  // tile past the end whose free stage receives a copy of the last tile).
+  auto issue_piece = [&](const int (&pid)[2], int src, int dst, int j) {
+    const int base = p0 + src * kTT;
     const int nvalid = p1 - base;  // rows of this tile inside the split (>= 1)
     const int blk = wave + j * kNW;
     uint32_t off = (dma_off[j >> 1] >> (16 * (j & 1))) & 0xffffu;
@@ -304,26 +304,26 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
       row = base + 16 * half;
     }
     dma_16B(lat_b + row * kRowBytes, kTileBytes / 2, off,
-            (uint32_t)(uintptr_t)(stage_of(it) + blk * 1024));
+            (uint32_t)(uintptr_t)(stage_of(dst) + blk * 1024));
   };
-  auto issue_tile = [&](const int (&pid)[2], int it) {
+  auto issue_tile = [&](const int (&pid)[2], int src, int dst) {
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j)
-      if (j < my_pieces) issue_piece(pid, it, j);
+      if (j < my_pieces) issue_piece(pid, src, dst, j);
   };
 
-  // Computes tile `it` from stage I.  The loads of tile it+2 (into stage
-  // (I+2)%3) are issued piece by piece between the score MFMAs, so their
-  // issue stalls overlap matrix work.  Past the last tile they reload the
-  // last tile (an L2 hit, never used): every step issues the same loads, so
-  // the score loop has no branch and the vmcnt waits are the same for all
-  // steps.
+  // Computes tile `it` from its stage.  The loads of tile it+3 (into the
+  // stage of tile it-1, which every wave finished before the barrier) are
+  // issued piece by piece between the score MFMAs, so their issue stalls
+  // overlap matrix work.  Past the last tile they load a copy of the last
+  // tile into that free stage (an L2 hit, never used): every step issues the
+  // same loads, so the score loop has no branch and the vmcnt waits are the
+  // same for all steps.
   auto compute_tile = [&](int it) {
     const unsigned char* tile = stage_of(it);
     const int base = p0 + it * kTT;
     const int next = min(it + kStages - 1, ntiles - 1);
-    // page ids of tile it+3 (its stage is this one), ahead of the loads of
-    // tile it+2 below
+    // page ids of tile it+4, a step ahead of its loads
     fetch_pages(min(it + kStages, ntiles - 1), pid_next);
 
     // scores.  Chunk (4*ks + lg) ^ swz(t) = 8*(ks/2) + ((4*(ks&1) + lg) ^ swz(t)):
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
       if ((ks & 1) == 0 && (ks >> 1) < kDmaPerWave && (ks >> 1) < my_pieces)
-        issue_piece(pid_cur, next, ks >> 1);
+        issue_piece(pid_cur, next, it + kStages - 1, ks >> 1);
       const int cur = ks % (kAhead + 1);
       const int kn = ks + kAhead;
       if (kn < kKS) {
@@ -471,8 +471,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
     }
   };
 
-  // One pipeline step: tile `it` lives in stage I; tile it+2 goes to stage
-  // (I+2)%3, which every wave finished reading before the barrier.
+  // One pipeline step: tile `it` is computed while tiles it+1 and it+2 land
+  // and tile it+3 is issued.
   auto step = [&](int it) {
     if (it >= ntiles) return;
     // the next tile's loads (this wave's share) may still be in flight
@@ -488,7 +488,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
     for (int t = 0; t + 1 < kStages; ++t) {
       int pid[2];
       fetch_pages(min(t, ntiles - 1), pid);
-      issue_tile(pid, min(t, ntiles - 1));
+      issue_tile(pid, min(t, ntiles - 1), t);
     }
     fetch_pages(min(kStages - 1, ntiles - 1), pid_next);
     // the query fragments (and the first tiles) land here, once: the loop
