@@ -446,13 +446,13 @@ def bench_mla(args, w, dev):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(alg_bytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(w["name"], "mla"),
-                     "kernel": ("mla_decode_mfma" if w["d_c"] == 512 else
-                                "gqa_decode_mfma<320, 256>") + ("" if S == 1 else " + lse_combine"),
+                     "kernel": "mla_decode_mfma" + ("" if S == 1 else " + lse_combine"),
                      "kernel_us": round(call_ms * 1e3, 2)},
         "mfma_roofline": {"achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                           "note": "algorithmic flops 2*H*(d_c+d_rope+d_c) per position; "
-                                  "the kernel issues 1.47x that (bf16 hi+lo weights)"},
+                                  "the kernel issues %.2fx that (bf16 hi+lo weights)"
+                                  % ((3 * w["d_c"] + w["d_rope"]) / (2 * w["d_c"] + w["d_rope"]))},
     }
     print(f"bench: {ms * 1e3:.1f} us/step, {value:.0f} GB/s, {tflops:.0f} TFLOP/s",
           file=sys.stderr, flush=True)

@@ -80,29 +80,21 @@ ATTN_DEV int vt_swz(int t) {
   else return 2 * (t & 3);
 }
 
-// DK: key row width (and row stride of the cache); DV: value width.  DK ==
-// DV is a K/V cache; DK > DV is a latent cache whose value is the first DV
-// columns of each row (absorbed MLA: xuesongtap "attention-head" note,
-// sections 5.2-5.3) -- then the V tile is written to LDS from the K
-// fragments already in registers and V is never loaded on its own.
+// DK: key row width (and row stride of the cache); DV: value width (equal
+// for a K/V cache).
 template <int DK, int DV, int NH>
 struct MfmaCfg {
-  static constexpr bool SHARED_V = DK != DV;
   static constexpr int KS = DK / 32;  // k-steps of the score product
   static constexpr int HB = NH / 16;  // head blocks
   static constexpr int DB = DV / 16;  // d blocks of the value product
   static constexpr int VT_BYTES = kTT * DV * 2;
   static constexpr int CPR = DV / 8;                      // 16-byte chunks per V row
   static constexpr int RPI = CPR >= 64 ? 1 : 64 / CPR;    // rows per load instruction
-  static constexpr int VLD = SHARED_V ? 0 : kTT / RPI;    // V loads per lane per tile
-  // Q^T fragments live in LDS (shared by the waves, read per k-step) when
-  // they would not fit in registers beside the K stages: the latent case.
-  static constexpr bool Q_LDS = SHARED_V;
-  static constexpr int Q_BYTES = Q_LDS ? HB * KS * 64 * 16 : 0;
+  static constexpr int VLD = kTT / RPI;                   // V loads per lane per tile
   static constexpr int MERGE_BYTES = kNW * NH * (DV + 2) * 4;
-  static constexpr int LOOP_BYTES = kNW * VT_BYTES + Q_BYTES;
+  static constexpr int LOOP_BYTES = kNW * VT_BYTES;
   static constexpr int SMEM = MERGE_BYTES > LOOP_BYTES ? MERGE_BYTES : LOOP_BYTES;
-  static_assert(DV % 32 == 0 && DV <= DK, "value columns");
+  static_assert(DV % 32 == 0 && DV == DK, "value columns");
 };
 
 template <int DK, int DV, int NH, int MODE>
@@ -153,43 +145,18 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   const uint16_t* __restrict__ Kbg = (const uint16_t*)a.k + kv_off;
   const uint16_t* __restrict__ Vbg = (const uint16_t*)a.v + kv_off;
 
-  // Q^T fragments: head li of block hb, elements 32*ks + 8*lg .. +7 -- in
-  // registers, or (Q_LDS) in LDS as entry (hb*KS + ks)*64 + lane, filled
-  // once by the whole group.
-  uint4 qf[C::Q_LDS ? 1 : HB][C::Q_LDS ? 1 : KS];
-  uint4* const sq = (uint4*)(smem + kNW * C::VT_BYTES);
-  if constexpr (C::Q_LDS) {
-    for (int e = threadIdx.x; e < HB * KS * 64; e += kNW * 64) {
-      const int ln = e & 63;
-      const int ks = (e >> 6) % KS;
-      const int hb = (e >> 6) / KS;
-      const int h = hb * 16 + (ln & 15);
-      const uint16_t* qh = (const uint16_t*)a.q +
-                           query_row(b, g, min(c0 + h, a.ncol - 1), a.n, a.L, a.H_q) * D;
-      sq[e] = h < nh ? *(const uint4*)(qh + 32 * ks + 8 * (ln >> 4)) : make_uint4(0, 0, 0, 0);
-    }
-    __syncthreads();
-  } else {
+  // Q^T fragments: head li of block hb, elements 32*ks + 8*lg .. +7
+  uint4 qf[HB][KS];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      const int h = hb * 16 + li;
-      const uint16_t* qh = (const uint16_t*)a.q +
-                           query_row(b, g, min(c0 + h, a.ncol - 1), a.n, a.L, a.H_q) * D;
+  for (int hb = 0; hb < HB; ++hb) {
+    const int h = hb * 16 + li;
+    const uint16_t* qh = (const uint16_t*)a.q +
+                         query_row(b, g, min(c0 + h, a.ncol - 1), a.n, a.L, a.H_q) * D;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qf[hb][ks] = h < nh ? *(const uint4*)(qh + 32 * ks + 8 * lg)
-                            : make_uint4(0, 0, 0, 0);
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      qf[hb][ks] = h < nh ? *(const uint4*)(qh + 32 * ks + 8 * lg) : make_uint4(0, 0, 0, 0);
   }
-  auto q_frag = [&](int hb, int ks) -> uint4 {
-    if constexpr (C::Q_LDS) {
-      // the lane index is recomputed here (cheaper than keeping it live)
-      const int ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-      return sq[(hb * KS + ks) * 64 + ln];
-    } else {
-      return qf[hb][ks];
-    }
-  };
+  auto q_frag = [&](int hb, int ks) -> uint4 { return qf[hb][ks]; };
 
   f32x4_t o[DB][HB];  // O^T blocks: d rows 16*db + 4*lg + r, head column li
   float m[HB], l[HB];
@@ -264,24 +231,11 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
                           const uint4 (&vr_)[VLD > 0 ? VLD : 1]) {
     const int base = p0 + it * kTT;
     // V tile -> LDS (row t, chunk c stored at chunk c ^ swz(t))
-    if constexpr (C::SHARED_V) {
-      // the value columns are the first DV of the K fragments: row
-      // 16*tb + li, chunk 4*ks + lg
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int ks = 0; ks < DV / 32; ++ks) {
-          const int t = 16 * tb + li;
-          const int c = 4 * ks + lg;
-          *(uint4*)(vt + t * (2 * DV) + 16 * (c ^ vt_swz<DV>(t))) = kf[tb][ks];
-        }
-    } else {
-#pragma unroll
-      for (int i = 0; i < VLD; ++i) {
-        const int t = RPI * i + lane / CPR;
-        const int c = lane % CPR;
-        *(uint4*)(vt + t * (2 * DV) + 16 * (c ^ vt_swz<DV>(t))) = vr_[i];
-      }
+    for (int i = 0; i < VLD; ++i) {
+      const int t = RPI * i + lane / CPR;
+      const int c = lane % CPR;
+      *(uint4*)(vt + t * (2 * DV) + 16 * (c ^ vt_swz<DV>(t))) = vr_[i];
     }
 
     // scores S^T: token rows 16*tb + 4*lg + r, head column li of block hb
@@ -477,11 +431,6 @@ hipError_t launch_mode(const GqaArgs& a, int dk, int dv, int heads_per_item, int
     case 128128032: return launch_one<128, 128, 32, MODE>(a, grid, st);
     case 256256016: return launch_one<256, 256, 16, MODE>(a, grid, st);
   }
-  if constexpr (MODE != kAddrGlobal) {
-    // latent rows of 256 + 64; 16 columns per group (32 would spill)
-    if (dk == 320 && dv == 256 && heads_per_item == 16)
-      return launch_one<320, 256, 16, MODE>(a, grid, st);
-  }
   return hipErrorInvalidValue;
 }
 
@@ -510,16 +459,9 @@ int mfma_waves() { return kNW; }
 
 hipError_t launch_gqa_mfma(const GqaArgs& a, int d, int heads_per_item, int grid,
                            hipStream_t st) {
-  return launch_latent_mfma(a, d, d, heads_per_item, grid, st);
-}
-
-hipError_t launch_latent_mfma(const GqaArgs& a, int dk, int dv, int heads_per_item,
-                              int grid, hipStream_t st) {
-  if (a.block_table)
-    return launch_mode<kAddrPaged>(a, dk, dv, heads_per_item, grid, st);
-  if (a.n_global > 0)
-    return launch_mode<kAddrGlobal>(a, dk, dv, heads_per_item, grid, st);
-  return launch_mode<kAddrDense>(a, dk, dv, heads_per_item, grid, st);
+  if (a.block_table) return launch_mode<kAddrPaged>(a, d, d, heads_per_item, grid, st);
+  if (a.n_global > 0) return launch_mode<kAddrGlobal>(a, d, d, heads_per_item, grid, st);
+  return launch_mode<kAddrDense>(a, d, d, heads_per_item, grid, st);
 }
 
 }  // namespace attn

@@ -64,25 +64,20 @@ int mfma_tile_rows();
 int mfma_waves();
 hipError_t launch_gqa_mfma(const GqaArgs& a, int d, int heads_per_item, int grid,
                            hipStream_t stream);
-// The same kernel with key width dk and value width dv; dk > dv reads a
-// latent cache whose value is the first dv columns of each row (k == v).
-// Instantiated for (dk, dv) = (64, 64), (128, 128) with 16 or 32 columns per
-// group, and (256, 256), (320, 256) with 16.
-hipError_t launch_latent_mfma(const GqaArgs& a, int dk, int dv, int heads_per_item,
-                              int grid, hipStream_t stream);
 
-// Absorbed MLA on the matrix cores (bf16, d_c = 512, d_rope = 64).
-int mla_heads_per_group();
+// Absorbed MLA on the matrix cores (bf16, d_rope = 64, d_c = 512 or 256).
+int mla_heads_per_group(int d_c);  // (head, token) columns per work group
+int mla_groups_per_cu(int d_c);    // work groups one CU holds at once (LDS)
 int mla_tile_rows();
-// L query tokens per sequence (q [B, L, H, 576], outputs [B, L, H, ...]);
-// block_table == nullptr: dense latent [B, T_cap, 576]; else a page pool
-// [num_pages, 2^page_shift, 576] with T_cap = max_pages << page_shift, and
-// `chunk` a multiple of the tile rows.
+// L query tokens per sequence (q [B, L, H, DK], outputs [B, L, H, ...]) with
+// DK = d_c + 64; block_table == nullptr: dense latent [B, T_cap, DK]; else a
+// page pool [num_pages, 2^page_shift, DK] with T_cap = max_pages <<
+// page_shift, and `chunk` a multiple of the tile rows.
 hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
                            float* lse, float* o_part, float* lse_part,
                            const int32_t* seq_lens, const int32_t* block_table,
                            int max_pages, int page_shift, int num_pages, int B,
-                           int L, int H, int T_cap, int S, int chunk,
+                           int L, int H, int T_cap, int d_c, int S, int chunk,
                            int head_chunks, float scale_log2, hipStream_t stream);
 
 }  // namespace attn

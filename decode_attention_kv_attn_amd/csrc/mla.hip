@@ -9,20 +9,15 @@ namespace {
 
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Supported latent geometries: (512, 64) on the shared-tile MLA kernel and
-// (256, 64) on the latent variant of the matrix-core GQA kernel (one latent
-// "KV head" read by every query head; xuesongtap "attention-head" note,
-// section 6: a 32-head model with latent width 256 and RoPE width 64).
-bool wide_latent(int d_c) { return d_c == 512; }
-
+// Supported latent geometries: (512, 64) and (256, 64) (xuesongtap
+// "attention-head" note, section 6: a 32-head model with latent width 256
+// and RoPE width 64), both on the shared-tile MLA kernel.
 int check_mla(int B, int H, int T_cap, int d_c, int d_rope) {
   if (B < 0 || H <= 0 || T_cap <= 0) return ATTN_ERR_SHAPE;
   if (!((d_c == 512 || d_c == 256) && d_rope == 64)) return ATTN_ERR_UNSUPPORTED;
   if ((long long)B * H > (1LL << 30)) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
-
-constexpr int kLatentCols = 16;  // columns per group of the (256, 64) path
 
 struct MlaPlan {
   int head_chunks, S, chunk;
@@ -34,17 +29,18 @@ int plan_mla(int B, int H, int T_cap, int d_c, int d_rope, int num_splits,
   const int st = check_mla(B, H, T_cap, d_c, d_rope);
   if (st != ATTN_OK) return st;
   if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_ARG;
-  const int hg = wide_latent(d_c) ? attn::mla_heads_per_group() : kLatentCols;
+  const int hg = attn::mla_heads_per_group(d_c);
   p->head_chunks = (H + hg - 1) / hg;
-  const int waves = wide_latent(d_c) ? 1 : attn::mfma_waves();
   long long S;
   if (num_splits > 0) {
     S = num_splits;
   } else {
-    // one work group per CU; keep at least two tiles per group
+    // fill every CU with the groups it holds at once; keep at least two
+    // tiles per group
     const long long units = (long long)(B > 0 ? B : 1) * p->head_chunks;
-    S = (attn::kNumCUs + units - 1) / units;
-    long long smax = T_cap / (2LL * waves * attn::mla_tile_rows());
+    const long long target = (long long)attn::kNumCUs * attn::mla_groups_per_cu(d_c);
+    S = (target + units - 1) / units;
+    long long smax = T_cap / (2LL * attn::mla_tile_rows());
     if (smax < 1) smax = 1;
     if (S > smax) S = smax;
   }
@@ -112,44 +108,11 @@ int decode_mla(const void* q, const void* latent, float* out, float* lse_out,
   }
   if ((long long)B * p.S * p.head_chunks > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
-  if (wide_latent(d_c)) {
-    if (attn::launch_mla_mfma(q, latent, out, lse_out, o_part, lse_part, seq_lens,
-                              block_table, max_pages, page_shift, num_pages, B, L,
-                              H, T_cap, p.S, p.chunk, p.head_chunks,
-                              scale * 1.4426950408889634f, s) != hipSuccess)
-      return ATTN_ERR_HIP;
-  } else {
-    // H query heads x L tokens as the columns of one latent "KV head"
-    attn::GqaArgs a = {};
-    a.q = q;
-    a.k = latent;
-    a.v = latent;
-    a.out = out;
-    a.lse = lse_out;
-    a.o_part = o_part;
-    a.lse_part = lse_part;
-    a.seq_lens = seq_lens;
-    a.block_table = block_table;
-    a.max_pages = max_pages;
-    a.page_shift = page_shift;
-    a.num_pages = num_pages;
-    a.B = B;
-    a.H_q = H;
-    a.H_kv = 1;
-    a.T_cap = T_cap;
-    a.L = L;
-    a.n = H;
-    a.ncol = H * L;
-    a.head_chunks = p.head_chunks;
-    a.S = p.S;
-    a.chunk = p.chunk;
-    a.scale_log2 = scale * 1.4426950408889634f;
-    const long long grid = (long long)B * p.head_chunks * p.S;
-    a.xcd_remap = (p.head_chunks > 1 && grid % attn::kNumXCDs == 0) ? 1 : 0;
-    if (attn::launch_latent_mfma(a, d_c + d_rope, d_c, kLatentCols, (int)grid, s) !=
-        hipSuccess)
-      return ATTN_ERR_HIP;
-  }
+  if (attn::launch_mla_mfma(q, latent, out, lse_out, o_part, lse_part, seq_lens,
+                            block_table, max_pages, page_shift, num_pages, B, L, H,
+                            T_cap, d_c, p.S, p.chunk, p.head_chunks,
+                            scale * 1.4426950408889634f, s) != hipSuccess)
+    return ATTN_ERR_HIP;
   if (p.S > 1 && attn::launch_combine(o_part, lse_part, out, lse_out, B, H * L,
                                       p.S, d_c, s) != hipSuccess)
     return ATTN_ERR_HIP;

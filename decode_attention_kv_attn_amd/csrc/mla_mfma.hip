@@ -36,12 +36,6 @@
 #ifndef ATTN_MLA_QK_AHEAD  // k-steps the score operand reads run ahead
 #define ATTN_MLA_QK_AHEAD 2
 #endif
-#ifndef ATTN_MLA_STAGES  // LDS tile stages
-#define ATTN_MLA_STAGES 4
-#endif
-#ifndef ATTN_MLA_WAVES  // waves per group (128 heads split among them)
-#define ATTN_MLA_WAVES 4
-#endif
 
 namespace attn {
 namespace {
@@ -55,29 +49,37 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ int scalar_buffer_load_i32(u32x4 rsrc, int offset, int cachepolicy) __asm(
     "llvm.amdgcn.s.buffer.load.i32");
 
-constexpr int kDK = 576;                 // latent row: 512 content + 64 rope
-constexpr int kDV = 512;                 // value columns (the content part)
-constexpr int kTT = 32;                  // rows per tile
-constexpr int kNW = ATTN_MLA_WAVES;      // waves per group
-constexpr int kHW = 128 / kNW;           // heads per wave
-constexpr int kHB = kHW / 16;            // 16-head blocks per wave
-constexpr int kHG = kNW * kHW;           // heads per group
-constexpr int kRowBytes = kDK * 2;       // 1152
-constexpr int kCPR = kRowBytes / 16;     // 72 chunks per row
-constexpr int kTileBytes = kTT * kRowBytes;         // 36864
-constexpr int kPieces = kTileBytes / 1024;              // 1 KiB loads per tile
-constexpr int kDmaPerWave = (kPieces + kNW - 1) / kNW;  // at most, per wave
-constexpr int kKS = kDK / 32;            // 18 score k-steps
-constexpr int kDB = kDV / 16;            // 32 value blocks
+constexpr int kTT = 32;                   // rows per tile
+constexpr int kStages = 4;                // tiles in LDS: three loading
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor flags (gfx9)
-static_assert(kTileBytes % 1024 == 0 && (kNW == 4 || kNW == 8), "tile split");
 
-constexpr int kStages = ATTN_MLA_STAGES;  // tiles in LDS: kStages - 1 loading
-static_assert(kStages == 3 || kStages == 4, "stages");
-__shared__ __attribute__((aligned(1024))) unsigned char g_stages[kStages * kTileBytes];
-
-// LDS of the stage that holds tile `it`
-ATTN_DEV unsigned char* stage_of(int it) { return g_stages + (it % kStages) * kTileBytes; }
+// Latent geometry and group shape: rows of DK = d_c + d_rope bf16, the first
+// DV columns are the values; NW waves of HW (head, token) columns each.
+template <int DK, int DV, int NW, int HW>
+struct MlaGeo {
+  static constexpr int kDK = DK, kDV = DV, kNW = NW, kHW = HW;
+  static constexpr int kHB = HW / 16;                     // 16-column blocks per wave
+  static constexpr int kHG = NW * HW;                     // columns per group
+  static constexpr int kRowBytes = DK * 2;
+  static constexpr int kCPR = kRowBytes / 16;             // 16-byte chunks per row
+  static constexpr int kTileBytes = kTT * kRowBytes;
+  static constexpr int kPieces = kTileBytes / 1024;       // 1 KiB loads per tile
+  static constexpr int kDmaPerWave = (kPieces + NW - 1) / NW;
+  static constexpr int kKS = DK / 32;                     // score k-steps
+  static constexpr int kDB = DV / 16;                     // value blocks
+  static_assert(DK % 32 == 0 && DV % 16 == 0 && DV <= DK, "latent widths");
+  static_assert(kCPR % 8 == 0, "the swizzle permutes aligned groups of 8 chunks");
+  // each 1 KiB load lies in one 16-row half of the tile (one page)
+  static_assert((16 * kRowBytes) % 1024 == 0, "tile halves are whole loads");
+  static_assert(16 * kRowBytes <= 65536, "per-lane offsets in a half fit 16 bits");
+  static_assert(HW % 16 == 0 && (HW / 16 == 1 || HW / 16 == 2), "column blocks");
+};
+// (512, 64): four waves of 32 heads; (256, 64): two waves of 16, two groups
+// per CU (the LDS of one is 80 KiB).
+using GeoWide = MlaGeo<576, 512, 4, 32>;
+using GeoNarrow = MlaGeo<320, 256, 2, 16>;
+template <class G>
+constexpr int groups_per_cu() { return G::kTileBytes * kStages <= 80 * 1024 ? 2 : 1; }
 
 // Chunk swizzle: logical 16-byte chunk c of row t sits at chunk c ^ swz(t);
 // the xor stays inside an aligned group of 8 chunks.  Chosen by measured LDS
@@ -157,13 +159,13 @@ ATTN_DEV void wait_vmcnt() {
 }
 
 struct MlaArgs {
-  const uint16_t* q;       // [B, H, 576]
-  const uint16_t* latent;  // [B, T_cap, 576], or the page pool [num_pages, P, 576]
+  const uint16_t* q;       // [B, H, DK]
+  const uint16_t* latent;  // [B, T_cap, DK], or the page pool [num_pages, P, DK]
   const int32_t* block_table;  // [B, max_pages] (paged only)
   int max_pages, page_shift, num_pages;
-  float* out;              // [B, H, 512] when S == 1
+  float* out;              // [B, H, DV] when S == 1
   float* lse;              // [B, H] (nullable) when S == 1
-  float* o_part;           // [B, H, S, 512]
+  float* o_part;           // [B, H, S, DV]
   float* lse_part;         // [B, H, S]
   const int32_t* seq_lens;
   int H, T_cap, S, chunk, head_chunks;
@@ -174,8 +176,16 @@ struct MlaArgs {
 
 // MULTI: several query tokens per sequence (per-column causal limits); a
 // separate instantiation so the single-token path carries none of it.
-template <int MODE, bool MULTI>
-__global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
+template <class G, int MODE, bool MULTI>
+__global__ __launch_bounds__(G::kNW * 64, groups_per_cu<G>()) void mla_decode_mfma(MlaArgs a) {
+  constexpr int kDK = G::kDK, kDV = G::kDV, kNW = G::kNW, kHW = G::kHW, kHB = G::kHB;
+  constexpr int kHG = G::kHG, kRowBytes = G::kRowBytes, kCPR = G::kCPR;
+  constexpr int kTileBytes = G::kTileBytes, kPieces = G::kPieces;
+  constexpr int kDmaPerWave = G::kDmaPerWave, kKS = G::kKS, kDB = G::kDB;
+  __shared__ __attribute__((aligned(1024))) unsigned char stages[kStages * kTileBytes];
+  // LDS of the stage that holds tile `it`
+  auto stage_of = [&](int it) { return stages + (it % kStages) * kTileBytes; };
+
   const int lane = threadIdx.x & 63;
   // uniform across the wave: keep wave-derived offsets in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -289,14 +299,14 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
     const int blk = wave + j * kNW;
     uint32_t off = (dma_off[j >> 1] >> (16 * (j & 1))) & 0xffffu;
     // Rows past the split (the split's last tile may be partial) read chunk
-    // `lane` of the first row of the half instead, or of the tile when the
-    // whole upper half is past the split: finite data that the softmax
+    // lane % kCPR of the first row of the half instead, or of the tile when
+    // the whole upper half is past the split: finite data that the softmax
     // masks.  A lane's row is past the split iff its offset from the half is
     // at least (nvalid - 16 * half) rows.
     int half = blk >= kPieces / 2 ? 1 : 0;  // uniform
     const int lim = (nvalid - 16 * half) * kRowBytes;
     if (nvalid <= 16) half = 0;
-    off = (int)off < lim ? off : 16u * lane;
+    off = (int)off < lim ? off : 16u * (lane % kCPR);
     long long row;  // first row of the half in the latent (or pool) rows
     if constexpr (MODE == kAddrPaged) {
       row = (long long)pid[half] * pg.stride + ((base + 16 * half) & ((1 << pg.shift) - 1));
@@ -347,8 +357,11 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
         af[k0][tb] = *(const uint4*)(abase[tb][k0 & 1] + 128 * (k0 >> 1));
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      if ((ks & 1) == 0 && (ks >> 1) < kDmaPerWave && (ks >> 1) < my_pieces)
-        issue_piece(pid_cur, next, it + kStages - 1, ks >> 1);
+      // this wave's loads spread evenly over the k-steps
+#pragma unroll
+      for (int j = 0; j < kDmaPerWave; ++j)
+        if ((j * kKS) / kDmaPerWave == ks && j < my_pieces)
+          issue_piece(pid_cur, next, it + kStages - 1, j);
       const int cur = ks % (kAhead + 1);
       const int kn = ks + kAhead;
       if (kn < kKS) {
@@ -365,9 +378,11 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
         }
     }
     // the softmax reads the scores with VALU instructions
-    static_assert(kHB == 2, "score drain lists four accumulators");
-    asm volatile(ATTN_MFMA_DRAIN
-                 : "+v"(sc[0][0]), "+v"(sc[0][1]), "+v"(sc[1][0]), "+v"(sc[1][1]));
+    if constexpr (kHB == 2)
+      asm volatile(ATTN_MFMA_DRAIN
+                   : "+v"(sc[0][0]), "+v"(sc[0][kHB - 1]), "+v"(sc[1][0]), "+v"(sc[1][kHB - 1]));
+    else
+      asm volatile(ATTN_MFMA_DRAIN : "+v"(sc[0][0]), "+v"(sc[1][0]));
 
     // online softmax per head (lazy maximum); weights split into bf16 hi+lo
     const bool full = base + kTT <= p1;  // uniform: no masked row in the tile
@@ -454,7 +469,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
       bl[hb] = as_bf16x8(make_uint4(plo[hb][0], plo[hb][1], plo[hb][2], plo[hb][3]));
     }
     // wait states between the VALU writes of the weights and their MFMAs
-    asm volatile("s_nop 4" ::"v"(bh[0]), "v"(bl[0]), "v"(bh[1]), "v"(bl[1]));
+    if constexpr (kHB == 2)
+      asm volatile("s_nop 4" ::"v"(bh[0]), "v"(bl[0]), "v"(bh[kHB - 1]), "v"(bl[kHB - 1]));
+    else
+      asm volatile("s_nop 4" ::"v"(bh[0]), "v"(bl[0]));
     // transposed value reads run one block ahead of their MFMAs
     s16x8_t vf[2];
     vf[0] = read_v(0);
@@ -535,14 +553,31 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_mfma(MlaArgs a) {
 
 }  // namespace
 
-int mla_heads_per_group() { return kHG; }
+int mla_heads_per_group(int d_c) { return d_c == 512 ? GeoWide::kHG : GeoNarrow::kHG; }
+int mla_groups_per_cu(int d_c) {
+  return d_c == 512 ? groups_per_cu<GeoWide>() : groups_per_cu<GeoNarrow>();
+}
 int mla_tile_rows() { return kTT; }
+
+namespace {
+template <class G>
+void launch_geo(const MlaArgs& a, dim3 g, bool paged, hipStream_t stream) {
+  const dim3 blk(G::kNW * 64);
+  if (paged) {
+    if (a.L > 1) hipLaunchKernelGGL((mla_decode_mfma<G, kAddrPaged, true>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((mla_decode_mfma<G, kAddrPaged, false>), g, blk, 0, stream, a);
+  } else {
+    if (a.L > 1) hipLaunchKernelGGL((mla_decode_mfma<G, kAddrDense, true>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((mla_decode_mfma<G, kAddrDense, false>), g, blk, 0, stream, a);
+  }
+}
+}  // namespace
 
 hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
                            float* lse, float* o_part, float* lse_part,
                            const int32_t* seq_lens, const int32_t* block_table,
                            int max_pages, int page_shift, int num_pages, int B,
-                           int L, int H, int T_cap, int S, int chunk,
+                           int L, int H, int T_cap, int d_c, int S, int chunk,
                            int head_chunks, float scale_log2, hipStream_t stream) {
   MlaArgs a;
   a.q = (const uint16_t*)q;
@@ -564,15 +599,9 @@ hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
   a.chunk = chunk;
   a.head_chunks = head_chunks;
   a.scale_log2 = scale_log2;
-  const long long grid = (long long)B * S * head_chunks;
-  const dim3 g((unsigned)grid), blk(kNW * 64);
-  if (block_table) {
-    if (L > 1) hipLaunchKernelGGL((mla_decode_mfma<kAddrPaged, true>), g, blk, 0, stream, a);
-    else hipLaunchKernelGGL((mla_decode_mfma<kAddrPaged, false>), g, blk, 0, stream, a);
-  } else {
-    if (L > 1) hipLaunchKernelGGL((mla_decode_mfma<kAddrDense, true>), g, blk, 0, stream, a);
-    else hipLaunchKernelGGL((mla_decode_mfma<kAddrDense, false>), g, blk, 0, stream, a);
-  }
+  const dim3 g((unsigned)((long long)B * S * head_chunks));
+  if (d_c == 512) launch_geo<GeoWide>(a, g, block_table != nullptr, stream);
+  else launch_geo<GeoNarrow>(a, g, block_table != nullptr, stream);
   return hipGetLastError();
 }
 
