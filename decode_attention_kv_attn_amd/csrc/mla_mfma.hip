@@ -50,14 +50,15 @@ __device__ int scalar_buffer_load_i32(u32x4 rsrc, int offset, int cachepolicy) _
     "llvm.amdgcn.s.buffer.load.i32");
 
 constexpr int kTT = 32;                   // rows per tile
-constexpr int kStages = 4;                // tiles in LDS: three loading
+constexpr int kLdsPerCU = 160 * 1024;
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor flags (gfx9)
 
 // Latent geometry and group shape: rows of DK = d_c + d_rope bf16, the first
-// DV columns are the values; NW waves of HW (head, token) columns each.
-template <int DK, int DV, int NW, int HW>
+// DV columns are the values; NW waves of HW (head, token) columns each;
+// STAGES tiles in LDS (STAGES - 1 loading while one is computed).
+template <int DK, int DV, int NW, int HW, int STAGES>
 struct MlaGeo {
-  static constexpr int kDK = DK, kDV = DV, kNW = NW, kHW = HW;
+  static constexpr int kDK = DK, kDV = DV, kNW = NW, kHW = HW, kStages = STAGES;
   static constexpr int kHB = HW / 16;                     // 16-column blocks per wave
   static constexpr int kHG = NW * HW;                     // columns per group
   static constexpr int kRowBytes = DK * 2;
@@ -73,13 +74,16 @@ struct MlaGeo {
   static_assert((16 * kRowBytes) % 1024 == 0, "tile halves are whole loads");
   static_assert(16 * kRowBytes <= 65536, "per-lane offsets in a half fit 16 bits");
   static_assert(HW % 16 == 0 && (HW / 16 == 1 || HW / 16 == 2), "column blocks");
+  static_assert(STAGES >= 2 && STAGES * kTileBytes <= kLdsPerCU, "stages");
+  static constexpr int kGroupsPerCU = kLdsPerCU / (STAGES * kTileBytes);
 };
-// (512, 64): four waves of 32 heads; (256, 64): two waves of 16, two groups
-// per CU (the LDS of one is 80 KiB).
-using GeoWide = MlaGeo<576, 512, 4, 32>;
-using GeoNarrow = MlaGeo<320, 256, 2, 16>;
-template <class G>
-constexpr int groups_per_cu() { return G::kTileBytes * kStages <= 80 * 1024 ? 2 : 1; }
+// (512, 64): four waves of 32 heads, four stages (144 KiB, one group per
+// CU); (256, 64): two waves of 16 heads, ATTN_MLA_NARROW_STAGES stages.
+#ifndef ATTN_MLA_NARROW_STAGES
+#define ATTN_MLA_NARROW_STAGES 4
+#endif
+using GeoWide = MlaGeo<576, 512, 4, 32, 4>;
+using GeoNarrow = MlaGeo<320, 256, 2, 16, ATTN_MLA_NARROW_STAGES>;
 
 // Chunk swizzle: logical 16-byte chunk c of row t sits at chunk c ^ swz(t);
 // the xor stays inside an aligned group of 8 chunks.  Chosen by measured LDS
@@ -177,11 +181,12 @@ struct MlaArgs {
 // MULTI: several query tokens per sequence (per-column causal limits); a
 // separate instantiation so the single-token path carries none of it.
 template <class G, int MODE, bool MULTI>
-__global__ __launch_bounds__(G::kNW * 64, groups_per_cu<G>()) void mla_decode_mfma(MlaArgs a) {
+__global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(MlaArgs a) {
   constexpr int kDK = G::kDK, kDV = G::kDV, kNW = G::kNW, kHW = G::kHW, kHB = G::kHB;
   constexpr int kHG = G::kHG, kRowBytes = G::kRowBytes, kCPR = G::kCPR;
   constexpr int kTileBytes = G::kTileBytes, kPieces = G::kPieces;
   constexpr int kDmaPerWave = G::kDmaPerWave, kKS = G::kKS, kDB = G::kDB;
+  constexpr int kStages = G::kStages;
   __shared__ __attribute__((aligned(1024))) unsigned char stages[kStages * kTileBytes];
   // LDS of the stage that holds tile `it`
   auto stage_of = [&](int it) { return stages + (it % kStages) * kTileBytes; };
@@ -555,7 +560,7 @@ __global__ __launch_bounds__(G::kNW * 64, groups_per_cu<G>()) void mla_decode_mf
 
 int mla_heads_per_group(int d_c) { return d_c == 512 ? GeoWide::kHG : GeoNarrow::kHG; }
 int mla_groups_per_cu(int d_c) {
-  return d_c == 512 ? groups_per_cu<GeoWide>() : groups_per_cu<GeoNarrow>();
+  return d_c == 512 ? GeoWide::kGroupsPerCU : GeoNarrow::kGroupsPerCU;
 }
 int mla_tile_rows() { return kTT; }
 
