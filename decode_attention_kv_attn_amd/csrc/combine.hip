@@ -7,10 +7,14 @@
 // "attention-head" note, section 1).  Parts with lse = -inf are empty and get
 // weight 0; if every part is empty the output is 0 and lse is -inf.
 //
-// One work group of 256 lanes per (b, h): lanes cover the columns (up to
-// 256 at a time) and, when the value is narrower than 256, the remaining
-// lanes split the parts between them and meet in LDS.  Loads over the parts
-// are independent and unrolled, so many are in flight per lane.
+// Value widths that are a multiple of 64 up to 512 (every width the decode
+// kernels produce): one wave per (b, h), each lane owning d_v / 64 adjacent
+// columns, read as one vector per part; the loads of four parts are in
+// flight at once, and the weights come from the same wave, so one row costs
+// about two memory round trips.  Other widths: one work group of 256 lanes
+// per (b, h): lanes cover the columns (up to 256 at a time) and, when the
+// value is narrower than 256, the remaining lanes split the parts between
+// them and meet in LDS.
 
 #include "device_common.h"
 #include "internal.h"
@@ -97,14 +101,109 @@ __global__ __launch_bounds__(kThreads) void lse_combine(
   }
 }
 
+template <int N>
+struct VecOf;
+template <> struct VecOf<1> { typedef float type; };
+template <> struct VecOf<2> { typedef float2 type; };
+template <> struct VecOf<4> { typedef float4 type; };
+
+template <int N>
+ATTN_DEV void fma_vec(float (&acc)[N], float w, const typename VecOf<N>::type& x) {
+  const float* xs = reinterpret_cast<const float*>(&x);
+#pragma unroll
+  for (int i = 0; i < N; ++i) acc[i] = add_part(acc[i], w, xs[i]);
+}
+
+// CPL = d_v / 64 columns per lane, read as CPL / VW vectors of VW floats.
+template <int CPL>
+__global__ __launch_bounds__(kThreads) void lse_combine_rows(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part,
+    float* __restrict__ out, float* __restrict__ lse_out, int rows, int S) {
+  constexpr int VW = CPL >= 4 ? 4 : CPL;
+  constexpr int NV = CPL / VW;
+  constexpr int d_v = 64 * CPL;
+  typedef typename VecOf<VW>::type vec;
+  __shared__ float wts[kThreads / 64][kMaxS];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * (kThreads / 64) + wave;
+  if (row >= (size_t)rows) return;
+  const float* lp = lse_part + row * S;
+  float* w_s = wts[wave];
+
+  // weights of the parts (natural-log input, log2 inside); this wave's own
+  // LDS row, so no barrier is needed between writing and reading it
+  float M = neg_inf();
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[s] * kLog2e);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float tot = 0.f;
+  for (int s = lane; s < S; s += 64) {
+    const float x = lp[s];
+    const float w = (x == neg_inf() || M == neg_inf()) ? 0.f : fast_exp2(x * kLog2e - M);
+    w_s[s] = w;
+    tot += w;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
+  if (lane == 0 && lse_out)
+    lse_out[row] = (tot > 0.f) ? (M + fast_log2(tot)) * kLn2 : neg_inf();
+  const float inv = (tot > 0.f) ? 1.f / tot : 0.f;
+
+  // lane owns columns VW*(lane + 64 v) .. +VW-1 for v < NV
+  const vec* op = reinterpret_cast<const vec*>(o_part + row * (size_t)S * d_v) + lane;
+  float acc[NV][VW] = {};
+  int s = 0;
+  for (; s + 4 <= S; s += 4) {
+    vec x[4][NV];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int v = 0; v < NV; ++v) x[k][v] = op[(size_t)(s + k) * (d_v / VW) + 64 * v];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int v = 0; v < NV; ++v) fma_vec<VW>(acc[v], w_s[s + k], x[k][v]);
+  }
+  for (; s < S; ++s) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      fma_vec<VW>(acc[v], w_s[s], op[(size_t)s * (d_v / VW) + 64 * v]);
+  }
+  vec* dst = reinterpret_cast<vec*>(out + row * d_v) + lane;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    vec r;
+    float* rs = reinterpret_cast<float*>(&r);
+#pragma unroll
+    for (int i = 0; i < VW; ++i) rs[i] = acc[v][i] * inv;
+    dst[64 * v] = r;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const float* o_part, const float* lse_part,
                           float* out, float* lse, int B, int H, int S, int d_v,
                           hipStream_t stream) {
   if (S > kMaxS) return hipErrorInvalidValue;
+  const int rows = B * H;
+  const bool vec_ok = ((uintptr_t)o_part % 16 == 0) && ((uintptr_t)out % 16 == 0);
+  const int cpl = d_v % 64 == 0 ? d_v / 64 : 0;  // columns per lane, one wave per row
+  if (vec_ok && (cpl == 1 || cpl == 2 || cpl == 4 || cpl == 8)) {
+    const dim3 g((unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64))), blk(kThreads);
+    if (cpl == 1)
+      hipLaunchKernelGGL(lse_combine_rows<1>, g, blk, 0, stream, o_part, lse_part, out, lse, rows, S);
+    else if (cpl == 2)
+      hipLaunchKernelGGL(lse_combine_rows<2>, g, blk, 0, stream, o_part, lse_part, out, lse, rows, S);
+    else if (cpl == 4)
+      hipLaunchKernelGGL(lse_combine_rows<4>, g, blk, 0, stream, o_part, lse_part, out, lse, rows, S);
+    else
+      hipLaunchKernelGGL(lse_combine_rows<8>, g, blk, 0, stream, o_part, lse_part, out, lse, rows, S);
+    return hipGetLastError();
+  }
   const int cl = d_v >= 256 ? 256 : (d_v > 128 ? 256 : (d_v > 64 ? 128 : 64));
-  hipLaunchKernelGGL(lse_combine, dim3((unsigned)B * H), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL(lse_combine, dim3((unsigned)rows), dim3(kThreads), 0, stream,
                      o_part, lse_part, out, lse, S, d_v, cl);
   return hipGetLastError();
 }

@@ -131,6 +131,25 @@ def test_split_invariance(num_splits):
     _check(q, k, v, sl, None, num_splits=num_splits, what=f"S={num_splits}")
 
 
+@pytest.mark.parametrize("d_v", [64, 128, 256, 512])
+@pytest.mark.parametrize("S", [1, 3, 6, 9])
+def test_combine_widths(d_v, S):
+    """The one-wave-per-row merge at every width the decode kernels emit:
+    7 rows (not a multiple of the 4 rows per group), part counts around the
+    4-part unroll, empty parts and an all-empty row."""
+    B, H = 1, 7
+    g = torch.Generator(device="cpu").manual_seed(6520 + d_v + S)
+    o = torch.randn(B, H, S, d_v, generator=g)
+    l = torch.randn(B, H, S, generator=g) * 4
+    l[0, 2, S - 1] = -math.inf
+    l[0, 5, :] = -math.inf
+    out, lse = L.attn_combine(o.to(DEV), l.to(DEV))
+    ro, rl = oracle.combine_ref(o.double().numpy(), l.double().numpy())
+    assert_parity(out, ro, f"combine d_v={d_v} S={S}")
+    assert_lse(lse, rl, f"combine d_v={d_v} S={S}")
+    assert torch.all(out[0, 5] == 0) and torch.isneginf(lse[0, 5])
+
+
 def test_combine_entry():
     """attn_combine on its own, with empty parts and an all-empty row."""
     B, H, S, d_v = 3, 5, 9, 96
