@@ -37,7 +37,17 @@ struct GqaPlan {
   int waves;        // waves per work group
   int tile_rows;    // positions per wave per tile
   size_t ws_bytes;  // workspace needed
+  size_t ws_fixed;  // workspace of the fixed splits alone
+  int cap;          // > 0: items of the balanced work list (calls with lengths)
 };
+
+// Workspace of a balanced list of `cap` items of N columns: o_part, lse_part
+// and the per-sequence (first item, pieces) pairs.
+size_t balanced_bytes(int cap, int N, int d, int B) {
+  const size_t rows = (size_t)cap * N;
+  return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256) +
+         round_up((size_t)B * 2 * sizeof(int), 256);
+}
 
 // Largest number of positions a non-global query can have visible (a query
 // that is itself a global position sees more; the last split takes the rest).
@@ -123,7 +133,17 @@ int plan_gqa(int B, int H_q, int H_kv, int T_cap, int d, int dtype, int window,
   if (S > mv) S = mv;
   p->chunk = (int)((mv + S - 1) / S);
   p->S = (mv + p->chunk - 1) / p->chunk;
-  p->ws_bytes = attn_decode_workspace_bytes(B, H_q, d, p->S);
+  p->ws_fixed = attn_decode_workspace_bytes(B, H_q, d, p->S);
+  p->ws_bytes = p->ws_fixed;
+  // Balanced work list: when the fixed plan splits (fewer units than work
+  // groups), a call with lengths cuts each sequence by its own visible rows.
+  p->cap = 0;
+  if (p->mfma && num_splits == 0 && p->S > 1 && B >= 1 && B <= kBalanceMaxB &&
+      target_groups() <= ATTN_MAX_SPLITS) {
+    p->cap = target_groups();
+    const size_t bb = balanced_bytes(p->cap, p->N, d, B);
+    if (bb > p->ws_bytes) p->ws_bytes = bb;
+  }
   return ATTN_OK;
 }
 
@@ -170,6 +190,7 @@ int attn_decode_gqa_plan(int B, int q_len, int H_q, int H_kv, int T_cap, int d,
   plan->waves = p.waves;
   plan->groups = (long long)B * H_kv * p.head_chunks * p.S;
   plan->workspace_bytes = p.ws_bytes;
+  plan->balanced_groups = p.cap;
   return ATTN_OK;
 }
 
@@ -243,8 +264,13 @@ int decode_gqa(const void* q, const void* k, const void* v, float* out,
       (lse_out && !aligned(lse_out, 4)) || (seq_lens && !aligned(seq_lens, 4)) ||
       (ring_head && !aligned(ring_head, 4)))
     return ATTN_ERR_ALIGN;
-  if (p.S > 1) {
-    if (!workspace || workspace_bytes < p.ws_bytes) return ATTN_ERR_WORKSPACE;
+  // balanced work list: lengths given, out 16-byte aligned (the merge writes
+  // whole vectors) and room for its parts; else the fixed splits
+  const bool bal = p.cap > 0 && seq_lens && aligned(out, 16) && workspace &&
+                   aligned(workspace, 16) &&
+                   workspace_bytes >= balanced_bytes(p.cap, p.N, d, B);
+  if (p.S > 1 && !bal) {
+    if (!workspace || workspace_bytes < p.ws_fixed) return ATTN_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
   }
 
@@ -277,19 +303,31 @@ int decode_gqa(const void* q, const void* k, const void* v, float* out,
   a.scale_log2 = scale * 1.4426950408889634f;
   a.o_part = nullptr;
   a.lse_part = nullptr;
-  if (p.S > 1) {
+  a.balanced = bal ? 1 : 0;
+  a.cap = bal ? p.cap : 0;
+  a.meta = nullptr;
+  if (bal) {
+    const size_t rows = (size_t)p.cap * p.N;
+    a.o_part = (float*)workspace;
+    a.lse_part = (float*)((char*)workspace + round_up(rows * d * sizeof(float), 256));
+    a.meta = (int*)((char*)a.lse_part + round_up(rows * sizeof(float), 256));
+  } else if (p.S > 1) {
     const size_t rows = (size_t)B * L * H_q * p.S;
     a.o_part = (float*)workspace;
     a.lse_part = (float*)((char*)workspace + round_up(rows * d * sizeof(float), 256));
   }
-  const long long grid = (long long)B * H_kv * p.head_chunks * p.S;
+  const long long grid = bal ? p.cap : (long long)B * H_kv * p.head_chunks * p.S;
   if (grid > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   a.xcd_remap = (p.head_chunks > 1 && grid % kNumXCDs == 0) ? 1 : 0;
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = p.mfma ? launch_gqa_mfma(a, d, p.N, (int)grid, s)
                               : launch_gqa_valu(a, dtype, d, (int)grid, s);
   if (e != hipSuccess) return ATTN_ERR_HIP;
-  if (p.S > 1) {
+  if (bal) {
+    if (launch_combine_balanced(a.o_part, a.lse_part, a.meta, out, lse_out, B, L, H_q,
+                                a.n, p.head_chunks, p.N, d, s) != hipSuccess)
+      return ATTN_ERR_HIP;
+  } else if (p.S > 1) {
     if (launch_combine(a.o_part, a.lse_part, out, lse_out, B * L, H_q, p.S, d, s) !=
         hipSuccess)
       return ATTN_ERR_HIP;

@@ -114,11 +114,23 @@ ATTN_DEV void fma_vec(float (&acc)[N], float w, const typename VecOf<N>::type& x
   for (int i = 0; i < N; ++i) acc[i] = add_part(acc[i], w, xs[i]);
 }
 
+// Balanced work list (the GQA matrix-core kernel's): output row
+// (b * L + token) * H_q + head belongs to column c = (head % n) * L + token of
+// KV head head / n, i.e. column c % nh of head chunk c / nh; piece s of it is
+// item meta[2b] + (g * k + s) * hc + c / nh with k = meta[2b + 1].
+struct BalancedMap {
+  const int* meta;
+  int L, H_q, n, hc, nh;
+};
+
 // CPL = d_v / 64 columns per lane, read as CPL / VW vectors of VW floats.
-template <int CPL>
+// BAL: the parts come from a balanced work list (`bm`), else S parts per row
+// stored next to each other.
+template <int CPL, bool BAL>
 __global__ __launch_bounds__(kThreads) void lse_combine_rows(
     const float* __restrict__ o_part, const float* __restrict__ lse_part,
-    float* __restrict__ out, float* __restrict__ lse_out, int rows, int S) {
+    float* __restrict__ out, float* __restrict__ lse_out, int rows, int S,
+    BalancedMap bm) {
   constexpr int VW = CPL >= 4 ? 4 : CPL;
   constexpr int NV = CPL / VW;
   constexpr int d_v = 64 * CPL;
@@ -128,18 +140,33 @@ __global__ __launch_bounds__(kThreads) void lse_combine_rows(
   const int lane = threadIdx.x & 63;
   const size_t row = (size_t)blockIdx.x * (kThreads / 64) + wave;
   if (row >= (size_t)rows) return;
-  const float* lp = lse_part + row * S;
+  size_t base = row * S;  // part row of part 0
+  int stride = 1;         // part rows between consecutive parts
+  if constexpr (BAL) {
+    const int per_b = bm.L * bm.H_q;
+    const int b = (int)(row / per_b);
+    const int rem = (int)(row - (size_t)b * per_b);
+    const int tok = rem / bm.H_q, head = rem - tok * bm.H_q;
+    S = bm.meta[2 * b + 1];
+    if (S == 1) return;  // one piece: the decode kernel wrote this row
+    const int g = head / bm.n;
+    const int c = (head - g * bm.n) * bm.L + tok;
+    const int chunk = c / bm.nh;
+    base = (size_t)(bm.meta[2 * b] + g * S * bm.hc + chunk) * bm.nh + (c - chunk * bm.nh);
+    stride = bm.hc * bm.nh;
+  }
+  const float* lp = lse_part + base;
   float* w_s = wts[wave];
 
   // weights of the parts (natural-log input, log2 inside); this wave's own
   // LDS row, so no barrier is needed between writing and reading it
   float M = neg_inf();
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[s] * kLog2e);
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[(size_t)s * stride] * kLog2e);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float tot = 0.f;
   for (int s = lane; s < S; s += 64) {
-    const float x = lp[s];
+    const float x = lp[(size_t)s * stride];
     const float w = (x == neg_inf() || M == neg_inf()) ? 0.f : fast_exp2(x * kLog2e - M);
     w_s[s] = w;
     tot += w;
@@ -151,7 +178,8 @@ __global__ __launch_bounds__(kThreads) void lse_combine_rows(
   const float inv = (tot > 0.f) ? 1.f / tot : 0.f;
 
   // lane owns columns VW*(lane + 64 v) .. +VW-1 for v < NV
-  const vec* op = reinterpret_cast<const vec*>(o_part + row * (size_t)S * d_v) + lane;
+  const vec* op = reinterpret_cast<const vec*>(o_part + base * d_v) + lane;
+  const size_t step = (size_t)stride * (d_v / VW);  // vectors between parts
   float acc[NV][VW] = {};
   int s = 0;
   for (; s + 4 <= S; s += 4) {
@@ -159,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_rows(
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int v = 0; v < NV; ++v) x[k][v] = op[(size_t)(s + k) * (d_v / VW) + 64 * v];
+      for (int v = 0; v < NV; ++v) x[k][v] = op[(size_t)(s + k) * step + 64 * v];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
@@ -167,8 +195,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_rows(
   }
   for (; s < S; ++s) {
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
-      fma_vec<VW>(acc[v], w_s[s], op[(size_t)s * (d_v / VW) + 64 * v]);
+    for (int v = 0; v < NV; ++v) fma_vec<VW>(acc[v], w_s[s], op[(size_t)s * step + 64 * v]);
   }
   vec* dst = reinterpret_cast<vec*>(out + row * d_v) + lane;
 #pragma unroll
@@ -181,6 +208,33 @@ __global__ __launch_bounds__(kThreads) void lse_combine_rows(
   }
 }
 
+template <bool BAL>
+hipError_t launch_rows(int cpl, const float* o_part, const float* lse_part, float* out,
+                       float* lse, int rows, int S, const BalancedMap& bm,
+                       hipStream_t stream) {
+  const dim3 g((unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64))), blk(kThreads);
+  switch (cpl) {
+    case 1:
+      hipLaunchKernelGGL((lse_combine_rows<1, BAL>), g, blk, 0, stream, o_part, lse_part,
+                         out, lse, rows, S, bm);
+      break;
+    case 2:
+      hipLaunchKernelGGL((lse_combine_rows<2, BAL>), g, blk, 0, stream, o_part, lse_part,
+                         out, lse, rows, S, bm);
+      break;
+    case 4:
+      hipLaunchKernelGGL((lse_combine_rows<4, BAL>), g, blk, 0, stream, o_part, lse_part,
+                         out, lse, rows, S, bm);
+      break;
+    case 8:
+      hipLaunchKernelGGL((lse_combine_rows<8, BAL>), g, blk, 0, stream, o_part, lse_part,
+                         out, lse, rows, S, bm);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_combine(const float* o_part, const float* lse_part,
@@ -190,22 +244,25 @@ hipError_t launch_combine(const float* o_part, const float* lse_part,
   const int rows = B * H;
   const bool vec_ok = ((uintptr_t)o_part % 16 == 0) && ((uintptr_t)out % 16 == 0);
   const int cpl = d_v % 64 == 0 ? d_v / 64 : 0;  // columns per lane, one wave per row
-  if (vec_ok && (cpl == 1 || cpl == 2 || cpl == 4 || cpl == 8)) {
-    const dim3 g((unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64))), blk(kThreads);
-    if (cpl == 1)
-      hipLaunchKernelGGL(lse_combine_rows<1>, g, blk, 0, stream, o_part, lse_part, out, lse, rows, S);
-    else if (cpl == 2)
-      hipLaunchKernelGGL(lse_combine_rows<2>, g, blk, 0, stream, o_part, lse_part, out, lse, rows, S);
-    else if (cpl == 4)
-      hipLaunchKernelGGL(lse_combine_rows<4>, g, blk, 0, stream, o_part, lse_part, out, lse, rows, S);
-    else
-      hipLaunchKernelGGL(lse_combine_rows<8>, g, blk, 0, stream, o_part, lse_part, out, lse, rows, S);
-    return hipGetLastError();
-  }
+  if (vec_ok && (cpl == 1 || cpl == 2 || cpl == 4 || cpl == 8))
+    return launch_rows<false>(cpl, o_part, lse_part, out, lse, rows, S, BalancedMap{},
+                              stream);
   const int cl = d_v >= 256 ? 256 : (d_v > 128 ? 256 : (d_v > 64 ? 128 : 64));
   hipLaunchKernelGGL(lse_combine, dim3((unsigned)rows), dim3(kThreads), 0, stream,
                      o_part, lse_part, out, lse, S, d_v, cl);
   return hipGetLastError();
+}
+
+hipError_t launch_combine_balanced(const float* o_part, const float* lse_part,
+                                   const int* meta, float* out, float* lse, int B,
+                                   int L, int H_q, int n, int head_chunks,
+                                   int heads_per_item, int d_v, hipStream_t stream) {
+  if ((uintptr_t)o_part % 16 != 0 || (uintptr_t)out % 16 != 0 || d_v % 64 != 0 ||
+      d_v > 256)
+    return hipErrorInvalidValue;
+  const BalancedMap bm{meta, L, H_q, n, head_chunks, heads_per_item};
+  return launch_rows<true>(d_v / 64, o_part, lse_part, out, lse, B * L * H_q, 0, bm,
+                           stream);
 }
 
 }  // namespace attn

@@ -28,6 +28,9 @@
 // four waves take the split's 32-token tiles in turn and are merged by the
 // log-sum-exp rule through LDS.  Softmax state is per head and lives in the
 // lanes that own that head (lane % 16), so rescaling O^T is lane-local.
+// With lengths given and fewer (sequence, KV head, head chunk) units than the
+// grid, the splits come from a list by visible rows instead (balance.h), so
+// that short sequences take fewer work groups and the longest piece shrinks.
 //
 // The addressing mode (dense linear/ring, global positions, paged) is a
 // template parameter; on a paged cache each wave fetches the page ids of
@@ -36,6 +39,7 @@
 #include <limits.h>
 #include <stdlib.h>
 
+#include "balance.h"
 #include "device_common.h"
 #include "internal.h"
 #include "visible.h"
@@ -116,12 +120,37 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
     const int per = gridDim.x / kNumXCDs;
     bid = (bid % kNumXCDs) * per + bid / kNumXCDs;
   }
-  const int hc = bid % a.head_chunks;
-  bid /= a.head_chunks;
-  const int s = bid % a.S;
-  bid /= a.S;
-  const int g = bid % a.H_kv;
-  const int b = bid / a.H_kv;
+  const int item = bid;
+  int hc, s, g, b, n_split = a.S, chunk = a.chunk;
+  if (a.balanced) {
+    // item r of sequence b: ((g * k + s) * head_chunks + hc), so the head
+    // chunks of one piece, which read the same rows, are neighbours
+    const WorkItem wi = balanced_item(
+        a.seq_lens, MODE == kAddrDense ? a.ring_head : nullptr, a.B, a.T_cap,
+        a.window, MODE == kAddrGlobal ? a.gpos : nullptr,
+        MODE == kAddrGlobal ? a.n_global : 0, a.H_kv * a.head_chunks, a.cap,
+        kNW * kTT, 2 * kNW * kTT, item);
+    if (!wi.valid) return;  // uniform over the work group
+    b = wi.b;
+    n_split = wi.k;
+    chunk = wi.chunk;
+    int r = wi.r;
+    hc = r % a.head_chunks;
+    r /= a.head_chunks;
+    s = r % wi.k;
+    g = r / wi.k;
+    if (wi.r == 0 && threadIdx.x == 0) {
+      a.meta[2 * b] = wi.first;
+      a.meta[2 * b + 1] = wi.k;
+    }
+  } else {
+    hc = bid % a.head_chunks;
+    bid /= a.head_chunks;
+    s = bid % a.S;
+    bid /= a.S;
+    g = bid % a.H_kv;
+    b = bid / a.H_kv;
+  }
 
   const VisibleRange vr =
       MODE == kAddrGlobal
@@ -130,7 +159,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
                           a.T_cap, a.window);
   const bool ring = MODE == kAddrDense && a.ring_head != nullptr;
   int p0, p1;  // this split's virtual rows
-  split_range(vr, s, a.S, a.chunk, p0, p1);
+  split_range(vr, s, n_split, chunk, p0, p1);
   const int c0 = hc * NH;                // first column (head, token) served
   const int nh = min(NH, a.ncol - c0);   // columns actually present
 
@@ -404,12 +433,13 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
     const float ov = empty ? 0.f : O / L;
     const float lse = empty ? neg_inf() : (M + fast_log2(L)) * kLn2;
     const size_t row = query_row(b, g, c0 + h, a.n, a.L, a.H_q);
-    if (a.S == 1) {
+    if (n_split == 1) {
       a.out[row * DV + e] = ov;
       if (e == 0 && a.lse) a.lse[row] = lse;
     } else {
-      a.o_part[(row * a.S + s) * DV + e] = ov;
-      if (e == 0) a.lse_part[row * a.S + s] = lse;
+      const size_t prow = a.balanced ? (size_t)item * NH + h : row * a.S + s;
+      a.o_part[prow * DV + e] = ov;
+      if (e == 0) a.lse_part[prow] = lse;
     }
   }
 }

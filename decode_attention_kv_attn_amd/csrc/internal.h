@@ -10,6 +10,9 @@ namespace attn {
 constexpr int kNumCUs = 256;  // MI355X: 8 XCDs x 32 CUs
 constexpr int kNumXCDs = 8;
 
+// Most sequences a balanced work list handles (4 per lane of a wave).
+constexpr int kBalanceMaxB = 256;
+
 // Arguments of one MHA/GQA/MQA decode launch.
 struct GqaArgs {
   const void* q;
@@ -36,6 +39,15 @@ struct GqaArgs {
   int chunk;        // positions per split
   int xcd_remap;    // 1: map consecutive work items onto one XCD
   float scale_log2; // softmax scale * log2(e)
+  // Balanced work list (matrix-core kernel only): work item w is item w of
+  // the list by visible rows (balance.h) instead of a fixed split; pieces of
+  // a sequence's units go to o_part / lse_part row w * heads_per_item + column,
+  // and meta[2b], meta[2b+1] receive the sequence's first item and its pieces
+  // per unit.  A sequence cut into one piece per unit is written to out / lse
+  // directly.
+  int balanced;
+  int cap;          // items the list may hold (the grid)
+  int* meta;        // [B, 2]
 };
 
 // Per-instantiation geometry of the VALU kernel, reported to the planner.
@@ -92,5 +104,15 @@ namespace attn {
 hipError_t launch_combine(const float* o_part, const float* lse_part,
                           float* out, float* lse, int B, int H, int S, int d_v,
                           hipStream_t stream);
+
+// Merge of a balanced work list's pieces (GqaArgs::balanced): output row
+// (b * L + token) * H_q + head, for heads_per_item columns per item and
+// head_chunks items per KV head; rows whose sequence has one piece per unit
+// are left as the decode kernel wrote them.  o_part and out 16-byte aligned,
+// d_v in {64, 128, 256}.
+hipError_t launch_combine_balanced(const float* o_part, const float* lse_part,
+                                   const int* meta, float* out, float* lse, int B,
+                                   int L, int H_q, int n, int head_chunks,
+                                   int heads_per_item, int d_v, hipStream_t stream);
 
 }  // namespace attn

@@ -105,7 +105,12 @@ enum {
  *             0 = chosen by the library (attn_decode_gqa_splits tells which).
  *   workspace, workspace_bytes  scratch for split results; required when the
  *             split count is > 1, size from attn_decode_gqa_workspace_bytes.
- *             Contents on entry are ignored.
+ *             Contents on entry are ignored.  When the library picks the
+ *             splits and the batch has fewer (sequence, KV head) units than
+ *             work groups, a call with seq_lens assigns pieces by visible
+ *             length instead (attn_gqa_plan.balanced_groups); a workspace
+ *             smaller than that size but large enough for the fixed splits
+ *             runs the fixed splits.
  *   stream    hipStream_t.
  */
 int attn_decode_gqa(const void* q, const void* k, const void* v, float* out,
@@ -138,6 +143,11 @@ typedef struct {
   int waves;           /* waves per work group                               */
   long long groups;    /* work groups of the decode kernel                   */
   size_t workspace_bytes; /* workspace the call needs (0: none)              */
+  int balanced_groups; /* > 0: a call that passes seq_lens (with out 16-byte
+                        * aligned and this workspace) cuts each sequence's
+                        * visible rows by its own length into pieces of one
+                        * common size, over at most this many work groups,
+                        * instead of `splits` fixed pieces; 0: never         */
 } attn_gqa_plan;
 
 /* Fills *plan for these arguments: q_len query tokens per sequence (1 for

@@ -110,7 +110,18 @@ def test_planner(lib):
         chunk = -(-mv // S)
         assert (S - 1) * chunk < mv
         ws = lib.attn_decode_gqa_workspace_bytes(*args, 0)
-        assert ws == (0 if S == 1 else lib.attn_decode_workspace_bytes(args[0], args[1], args[4], S))
+        fixed = 0 if S == 1 else lib.attn_decode_workspace_bytes(args[0], args[1], args[4], S)
+        B, H_q, H_kv, _, d, dt, w, ring = args
+        plan = L.attn_decode_gqa_plan(B, H_q, H_kv, T, d, dt, w, ring)
+        cap = plan["balanced_groups"]
+        # the balanced list is planned only where the fixed plan splits, for
+        # the matrix-core kernel, and keeps one round of work groups
+        assert cap == 0 or (S > 1 and plan["kernel"] == "mfma" and
+                            B * H_kv * -(-H_q // H_kv // plan["heads_per_item"]) < cap)
+        up = lambda x: -(-x // 256) * 256
+        rows = cap * plan["heads_per_item"]
+        bal = up(rows * d * 4) + up(rows * 4) + up(B * 8) if cap else 0
+        assert ws == max(fixed, bal) == plan["workspace_bytes"]
     for S in (1, 2, 7, 64, 1024):
         got = lib.attn_decode_gqa_splits(4, 16, 4, 2000, 128, 1, 0, 0, S)
         assert 1 <= got <= S
@@ -160,7 +171,9 @@ def test_global_host_errors(lib):
         assert (S - 1) * chunk < mv
         ws = lib.attn_decode_gqa_global_workspace_bytes(16, 32, 8, 32768, 128, 1,
                                                         window, n, 0)
-        assert ws == (0 if S == 1 else lib.attn_decode_workspace_bytes(16, 32, 128, S))
+        plan = L.attn_decode_gqa_plan(16, 32, 8, 32768, 128, 1, window, False, n)
+        assert ws == plan["workspace_bytes"]
+        assert ws >= (0 if S == 1 else lib.attn_decode_workspace_bytes(16, 32, 128, S))
     # without global positions the plan is attn_decode_gqa's
     assert (lib.attn_decode_gqa_global_splits(8, 32, 8, 4096, 128, 1, 512, 0, 0)
             == lib.attn_decode_gqa_splits(8, 32, 8, 4096, 128, 1, 512, 0, 0))

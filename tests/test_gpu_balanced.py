@@ -1,0 +1,240 @@
+"""GPU parity of the balanced work list against the float64 oracle.
+
+When the library picks the splits and a batch has fewer (sequence, KV head)
+units than work groups, a call that passes lengths cuts each sequence's
+visible rows by its own length (pieces of one common size, at least one per
+sequence) instead of cutting every sequence into the same number of fixed
+pieces.  The list is derived on the device from seq_lens, so these tests
+cover its edges: empty and one-row sequences, a single long sequence among
+empty ones, every sequence in one piece, the most sequences the list takes
+(four per lane), two head chunks per KV head, several query tokens, rings,
+global positions and paged pools.  Bar: max-abs <= 2e-3, relative L2 <=
+1e-3; visited rows bit-exact through integer recovery.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_kv_attn_amd as L
+import oracle
+import synth
+from oracle import bruteforce as BF
+from helpers import assert_lse, assert_parity, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _balanced(B, H_q, H_kv, T, d, window=0, ring=False, n_global=0, q_len=1):
+    p = L.attn_decode_gqa_plan(B, H_q, H_kv, T, d, 1, window, ring, n_global, 0, q_len)
+    return p["balanced_groups"] > 0
+
+
+def _inputs(lens, H_q, H_kv, T, d, seed, Lq=None):
+    B = len(lens)
+    qs = (B, H_q, d) if Lq is None else (B, Lq, H_q, d)
+    q = synth.draw(qs, seed, "bf16", DEV)
+    k = synth.draw((B, H_kv, T, d), seed + 1, "bf16", DEV)
+    v = synth.draw((B, H_kv, T, d), seed + 2, "bf16", DEV)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    return q, k, v, sl
+
+
+MIXES = {
+    "extreme": [0, 1, 2048, 1500, 129, 128, 257, 2047, 1024, 3, 640, 2000],
+    "one_long": [2048] + [0] * 15,
+    "all_empty": [0] * 8,
+    "uniform": [2048] * 8,
+    "all_one_piece": [1, 2, 3, 100, 127, 255, 256, 200],
+}
+# (d, H_q, H_kv): MQA-sized groups, two KV heads of 16, d = 256, and 48 heads
+# per KV head (two head chunks of 32 columns)
+KERNELS = [(128, 32, 1), (64, 32, 2), (256, 16, 2), (128, 96, 2)]
+
+
+@pytest.mark.parametrize("d,H_q,H_kv", KERNELS, ids=[f"d{a}-{b}x{c}" for a, b, c in KERNELS])
+@pytest.mark.parametrize("mix", list(MIXES))
+def test_length_mixes(d, H_q, H_kv, mix):
+    lens = MIXES[mix]
+    T = 2048
+    assert _balanced(len(lens), H_q, H_kv, T, d)
+    q, k, v, sl = _inputs(lens, H_q, H_kv, T, d, 12000 + d + H_q + len(mix))
+    out, lse = L.attn_decode_gqa(q, k, v, sl)
+    torch.cuda.synchronize()
+    ro, rl = oracle.gqa_decode_ref(q, k, v, sl)
+    assert_parity(out, ro, f"balanced {mix} d={d} {H_q}/{H_kv}")
+    assert_lse(lse, rl, f"balanced {mix}")
+    if mix == "all_empty":
+        assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    # the fixed splits give the same result within the bar
+    S = L.attn_decode_gqa_splits(len(lens), H_q, H_kv, T, d, 1)
+    out2, _ = L.attn_decode_gqa(q, k, v, sl, num_splits=S)
+    torch.cuda.synchronize()
+    assert_parity(out2, ro, f"fixed {mix}")
+
+
+def test_integer_recovery_balanced():
+    """Zero keys give every visible position weight 1/n_vis; value column i
+    holds bit i of the position (last column 1): out * n_vis must round to
+    the exact counts, so every visible row is read exactly once whichever
+    piece holds it."""
+    d, T = 64, 2048
+    lens = [0, 1, 2048, 1000, 129, 1500, 300, 2047, 4096, 640]
+    B = len(lens)
+    assert _balanced(B, 32, 1, T, d)
+    k = torch.zeros(B, 1, T, d, dtype=torch.bfloat16, device=DEV)
+    pos = np.arange(T)
+    vv = np.zeros((T, d), np.float32)
+    for i in range(d - 1):
+        vv[:, i] = (pos >> i) & 1
+    vv[:, d - 1] = 1
+    v = torch.from_numpy(vv).to(torch.bfloat16).to(DEV).expand(B, 1, T, d).contiguous()
+    gen = torch.Generator(device="cpu").manual_seed(12100)
+    q = torch.randn(B, 32, d, generator=gen).to(torch.bfloat16).to(DEV)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out, lse = L.attn_decode_gqa(q, k, v, sl)
+    torch.cuda.synchronize()
+    o = to64(out)
+    for b, T_b in enumerate(lens):
+        n_vis = min(T_b, T)
+        if n_vis == 0:
+            assert np.all(o[b] == 0) and torch.isneginf(lse[b]).all()
+            continue
+        want = [int(((np.arange(n_vis) >> i) & 1).sum()) for i in range(d - 1)] + [n_vis]
+        for h in (0, 13, 31):
+            got = np.rint(o[b, h] * n_vis).astype(np.int64).tolist()
+            assert got == want, (b, h)
+
+
+def test_poison_past_lengths():
+    """Rows past each length hold K = 1e4 and V = NaN: no piece may read them."""
+    lens = [0, 1, 2048, 700, 129, 1999]
+    q, k, v, sl = _inputs(lens, 32, 1, 2048, 128, 12200)
+    for b, T_b in enumerate(lens):
+        k[b, :, T_b:] = 1e4
+        v[b, :, T_b:] = float("nan")
+    out, lse = L.attn_decode_gqa(q, k, v, sl)
+    torch.cuda.synchronize()
+    ro, rl = oracle.gqa_decode_ref(q, k, v, sl)
+    assert_parity(out, ro, "balanced poison")
+    assert_lse(lse, rl, "balanced poison")
+
+
+def test_most_sequences():
+    """200 sequences (four rounds of 64 lanes), lengths uniform on 0..1024;
+    257 sequences fall back to the fixed splits."""
+    B, T = 200, 1024
+    assert _balanced(B, 32, 1, T, 64)
+    assert not _balanced(257, 32, 1, T, 64)
+    lens = synth.draw_ints(B, 0, T, 12300).tolist()
+    q, k, v, sl = _inputs(lens, 32, 1, T, 64, 12301)
+    out, lse = L.attn_decode_gqa(q, k, v, sl)
+    torch.cuda.synchronize()
+    ro, rl = oracle.gqa_decode_ref(q, k, v, sl)
+    assert_parity(out, ro, "balanced B=200")
+    assert_lse(lse, rl, "balanced B=200")
+
+
+@pytest.mark.parametrize("window", [0, 700, 1023])
+def test_ring(window):
+    """Ring of 1024 slots, lengths before and far past the wrap."""
+    slots = 1024
+    lens = [0, 5, 1024, 1500, 100000, 700, 701, 3000]
+    heads = np.random.default_rng(12400 + window).integers(0, slots, len(lens)).tolist()
+    assert _balanced(len(lens), 32, 1, slots, 128, window, True)
+    q, k, v, sl = _inputs(lens, 32, 1, slots, 128, 12400 + window)
+    rh = torch.tensor(heads, dtype=torch.int32, device=DEV)
+    out, lse = L.attn_decode_gqa(q, k, v, sl, rh, window)
+    torch.cuda.synchronize()
+    ro, rl = oracle.gqa_decode_ref(q, k, v, sl, rh, window)
+    assert_parity(out, ro, f"balanced ring w={window}")
+    assert_lse(lse, rl, "balanced ring")
+
+
+def test_global_positions():
+    """Window plus global positions; sequence 3's query is itself global and
+    sees every earlier position."""
+    T, window = 2048, 512
+    G = [0, 1, 2, 100, 1000]
+    lens = [2048, 600, 0, 1001, 3, 1500, 513, 1999]
+    assert _balanced(len(lens), 32, 1, T, 64, window, False, len(G))
+    q, k, v, sl = _inputs(lens, 32, 1, T, 64, 12500)
+    g = torch.tensor(G, dtype=torch.int32, device=DEV)
+    out, lse = L.attn_decode_gqa_global(q, k, v, g, window, sl)
+    torch.cuda.synchronize()
+    ro, rl = oracle.gqa_decode_ref(q, k, v, sl, None, window, global_pos=G)
+    assert_parity(out, ro, "balanced global")
+    assert_lse(lse, rl, "balanced global")
+
+
+@pytest.mark.parametrize("Lq,window", [(4, 0), (3, 600)])
+def test_multi_token(Lq, window):
+    """Several query tokens: 2 KV heads x 16 heads x Lq tokens = two head
+    chunks of 32 columns at Lq = 4."""
+    T = 2048
+    lens = [2048, 3, 0, 1000, 1, 1777]
+    assert _balanced(len(lens), 32, 2, T, 128, window, False, 0, Lq)
+    q, k, v, sl = _inputs(lens, 32, 2, T, 128, 12600 + Lq, Lq=Lq)
+    out, lse = L.attn_decode_gqa_multi(q, k, v, sl, None, window)
+    torch.cuda.synchronize()
+    ro, rl = oracle.gqa_decode_multi_ref(q, k, v, sl, None, window)
+    assert_parity(out, ro, f"balanced multi L={Lq} w={window}")
+    assert_lse(lse, rl, "balanced multi")
+
+
+def test_paged_equals_dense_bitwise():
+    """A shuffled pool of 16-position pages: the same list, the same bits as
+    the dense cache."""
+    T, P = 2048, 16
+    lens = [2048, 1, 0, 1500, 17, 385, 2047, 640]
+    q, k, v, sl = _inputs(lens, 32, 1, T, 128, 12700)
+    B = len(lens)
+    npb = T // P
+    perm = torch.randperm(B * npb + 3, generator=torch.Generator().manual_seed(12701))
+    table = perm[:B * npb].reshape(B, npb).to(torch.int32).to(DEV)
+
+    def pool(x):
+        p = torch.full((B * npb + 3, 1, P, 128), float("nan"), dtype=x.dtype, device=DEV)
+        p[table.reshape(-1).long()] = x.reshape(B, 1, npb, P, 128).permute(
+            0, 2, 1, 3, 4).reshape(B * npb, 1, P, 128)
+        return p
+
+    out, lse = L.attn_decode_gqa_paged(q, pool(k), pool(v), table, sl)
+    ref_o, ref_l = L.attn_decode_gqa(q, k, v, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+    ro, rl = oracle.gqa_decode_ref(q, k, v, sl)
+    assert_parity(out, ro, "balanced paged")
+
+
+def test_fallbacks_to_fixed_splits():
+    """A workspace that holds only the fixed splits' parts runs the fixed
+    splits, bit for bit the call with the split count given; an output that
+    is not 16-byte aligned runs them too."""
+    lens = [2048, 1, 0, 1500, 129, 640]
+    B, T, d = len(lens), 2048, 128
+    q, k, v, sl = _inputs(lens, 32, 1, T, d, 12800)
+    S = L.attn_decode_gqa_splits(B, 32, 1, T, d, 1)
+    assert S > 1 and _balanced(B, 32, 1, T, d)
+    fixed_o, fixed_l = L.attn_decode_gqa(q, k, v, sl, num_splits=S)
+    buf = torch.empty(B * 32 * d + 1, dtype=torch.float32, device=DEV)
+    out = buf[1:].view(B, 32, d)
+    o1, l1 = L.attn_decode_gqa(q, k, v, sl, out=out)
+    # through the C ABI: the binding would grow a small workspace itself
+    nb = L.attn_decode_workspace_bytes(B, 32, d, S)
+    assert nb < L.attn_decode_gqa_workspace_bytes(B, 32, 1, T, d, 1)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    o2 = torch.empty_like(fixed_o)
+    l2 = torch.empty_like(fixed_l)
+    st = L.library().attn_decode_gqa(
+        L._ptr(q), L._ptr(k), L._ptr(v), L._ptr(o2), L._ptr(l2), L._ptr(sl), None,
+        B, 32, 1, T, d, 1, 0, 0.0, 0, L._ptr(ws), nb, L._stream(None, q.device))
+    assert st == 0
+    torch.cuda.synchronize()
+    # the unaligned output also takes the merge's scalar form (another order
+    # of the sums), so it is held to the oracle rather than to the bits
+    ro, rl = oracle.gqa_decode_ref(q, k, v, sl)
+    assert_parity(o1, ro, "unaligned out")
+    assert_lse(l1, rl, "unaligned out")
+    assert torch.equal(o2, fixed_o) and torch.equal(l2, fixed_l)
