@@ -137,9 +137,12 @@ int plan_gqa(int B, int H_q, int H_kv, int T_cap, int d, int dtype, int window,
   p->ws_bytes = p->ws_fixed;
   // Balanced work list: when the fixed plan splits (fewer units than work
   // groups), a call with lengths cuts each sequence by its own visible rows.
+  // Not for rings: once a sequence has wrapped its visible range is the
+  // whole ring (or its window), the same for every sequence, and the list's
+  // setup (about a microsecond per group) would buy nothing.
   p->cap = 0;
-  if (p->mfma && num_splits == 0 && p->S > 1 && B >= 1 && B <= kBalanceMaxB &&
-      target_groups() <= ATTN_MAX_SPLITS) {
+  if (p->mfma && num_splits == 0 && p->S > 1 && !ring && B >= 1 &&
+      B <= kBalanceMaxB && target_groups() <= ATTN_MAX_SPLITS) {
     p->cap = target_groups();
     const size_t bb = balanced_bytes(p->cap, p->N, d, B);
     if (bb > p->ws_bytes) p->ws_bytes = bb;

@@ -28,6 +28,8 @@ namespace attn {
 
 struct WorkItem {
   int b;        // sequence
+  int len;      // seq_lens[b] as stored
+  int head;     // ring_head[b] as stored (ring mode), else 0
   int r;        // item of the sequence, 0 .. U*k - 1
   int k;        // pieces per unit of this sequence
   int chunk;    // rows per piece (C)
@@ -35,27 +37,56 @@ struct WorkItem {
   bool valid;   // false: the list has fewer than w + 1 items
 };
 
+// Sum and maximum over the 64 lanes, every lane receiving the result: DPP
+// moves inside rows of 16 lanes, then the permlane swaps across rows (the
+// pattern of group_sum, on integers).
+ATTN_DEV int lane_xor16_i(int x) {
+  const unsigned u = (unsigned)x;
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return (int)((__lane_id() & 16) ? p[0] : p[1]);
+}
+ATTN_DEV int lane_xor32_i(int x) {
+  const unsigned u = (unsigned)x;
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return (int)((__lane_id() & 32) ? p[0] : p[1]);
+}
+template <int CTRL>
+ATTN_DEV int dpp_i(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true);
+}
 ATTN_DEV int wave_sum_i(int x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+  x += dpp_i<kDppQuadXor1>(x);
+  x += dpp_i<kDppQuadXor2>(x);
+  x += dpp_i<kDppHalfMirror>(x);
+  x += dpp_i<kDppRowMirror>(x);
+  x += lane_xor16_i(x);
+  return x + lane_xor32_i(x);
 }
-
 ATTN_DEV int wave_max_i(int x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off));
-  return x;
+  x = max(x, dpp_i<kDppQuadXor1>(x));
+  x = max(x, dpp_i<kDppQuadXor2>(x));
+  x = max(x, dpp_i<kDppHalfMirror>(x));
+  x = max(x, dpp_i<kDppRowMirror>(x));
+  x = max(x, lane_xor16_i(x));
+  return max(x, lane_xor32_i(x));
 }
 
-// Inclusive prefix sum over the lanes of the wave.
+// Inclusive prefix sum over the lanes of the wave: shifts inside each row of
+// 16 lanes (out-of-row sources read 0), then the totals of the rows before.
+template <int CTRL>
+ATTN_DEV int dpp_shr_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
+}
 ATTN_DEV int wave_incl_scan_i(int x) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  return x;
+  x += dpp_shr_i<0x111>(x);  // row_shr:1
+  x += dpp_shr_i<0x112>(x);  // row_shr:2
+  x += dpp_shr_i<0x114>(x);  // row_shr:4
+  x += dpp_shr_i<0x118>(x);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15);
+  const int r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = __lane_id() >> 4;
+  return x + (row == 0 ? 0 : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2);
 }
 
 // Item w of the list.  B <= kBalanceMaxB sequences, U units each, with
@@ -68,16 +99,22 @@ ATTN_DEV WorkItem balanced_item(const int32_t* seq_lens, const int32_t* ring_hea
   constexpr int kPer = kBalanceMaxB / 64;
   const int lane = __lane_id();
   const int rounds = (B + 63) >> 6;
-  // visible rows of each held sequence, in tiles (-1: no sequence)
-  int nt[kPer];
+  // visible rows of each held sequence, in tiles (-1: no sequence); the
+  // stored length and ring head stay in the lane, so the item's sequence
+  // needs no second load
+  int nt[kPer], len[kPer], head[kPer];
   int sum_t = 0, max_t = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int b = 64 * i + lane;
     nt[i] = -1;
+    len[i] = 0;
+    head[i] = 0;
     if (i < rounds && b < B) {
-      const int n =
-          visible_range(seq_lens, ring_head, b, T_cap, window, gpos, n_global).n;
+      len[i] = seq_lens[b];
+      head[i] = ring_head ? ring_head[b] : 0;
+      const int n = visible_range_of(len[i], ring_head != nullptr, head[i], T_cap,
+                                     window, gpos, n_global).n;
       nt[i] = (n + tile - 1) / tile;
       sum_t += nt[i];
       max_t = max(max_t, nt[i]);
@@ -106,6 +143,7 @@ ATTN_DEV WorkItem balanced_item(const int32_t* seq_lens, const int32_t* ring_hea
   int hi = max(max_t, 1);
   if (slots > B) hi = min(hi, (sum_t + (slots - B) - 1) / (slots - B));
   hi = max(hi, lo);
+  if (count(lo) <= slots) hi = lo;  // the common case: the lower bound fits
   while (lo < hi) {  // smallest m in [lo, hi] whose list fits
     const int mid = (lo + hi) >> 1;
     if (count(mid) <= slots) hi = mid;
@@ -121,6 +159,8 @@ ATTN_DEV WorkItem balanced_item(const int32_t* seq_lens, const int32_t* ring_hea
   it.b = 0;
   it.first = 0;
   it.k = 1;
+  it.len = 0;
+  it.head = 0;
   int base = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -134,10 +174,12 @@ ATTN_DEV WorkItem balanced_item(const int32_t* seq_lens, const int32_t* ring_hea
         const int src = __ffsll((long long)bal) - 1;
         it.valid = true;
         it.b = 64 * i + src;
-        it.first = __shfl((int)p0, src);
-        it.k = __shfl(k, src);
+        it.first = __builtin_amdgcn_readlane((int)p0, src);
+        it.k = __builtin_amdgcn_readlane(k, src);
+        it.len = __builtin_amdgcn_readlane(len[i], src);
+        it.head = __builtin_amdgcn_readlane(head[i], src);
       }
-      base += __shfl(incl, 63);
+      base += __builtin_amdgcn_readlane(incl, 63);
     }
   }
   it.r = it.valid ? w - it.first : 0;

@@ -101,7 +101,9 @@ struct MfmaCfg {
   static_assert(DV % 32 == 0 && DV == DK, "value columns");
 };
 
-template <int DK, int DV, int NH, int MODE>
+// BAL: work items from the balanced list (GqaArgs::balanced); a template
+// parameter so that the fixed-split kernels carry none of its setup.
+template <int DK, int DV, int NH, int MODE, bool BAL>
 __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   using C = MfmaCfg<DK, DV, NH>;
   constexpr int KS = C::KS, HB = C::HB, DB = C::DB, CPR = C::CPR;
@@ -122,7 +124,8 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   }
   const int item = bid;
   int hc, s, g, b, n_split = a.S, chunk = a.chunk;
-  if (a.balanced) {
+  int len_b = 0, head_b = 0;  // balanced: the item's stored length and ring head
+  if constexpr (BAL) {
     // item r of sequence b: ((g * k + s) * head_chunks + hc), so the head
     // chunks of one piece, which read the same rows, are neighbours
     const WorkItem wi = balanced_item(
@@ -132,6 +135,8 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
         kNW * kTT, 2 * kNW * kTT, item);
     if (!wi.valid) return;  // uniform over the work group
     b = wi.b;
+    len_b = wi.len;
+    head_b = wi.head;
     n_split = wi.k;
     chunk = wi.chunk;
     int r = wi.r;
@@ -152,12 +157,16 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
     b = bid / a.H_kv;
   }
 
-  const VisibleRange vr =
-      MODE == kAddrGlobal
+  const bool ring = MODE == kAddrDense && a.ring_head != nullptr;
+  VisibleRange vr =
+      BAL ? visible_range_of(len_b, ring, head_b, a.T_cap, a.window,
+                             MODE == kAddrGlobal ? a.gpos : nullptr,
+                             MODE == kAddrGlobal ? a.n_global : 0)
+      : MODE == kAddrGlobal
           ? visible_range(a.seq_lens, nullptr, b, a.T_cap, a.window, a.gpos, a.n_global)
           : visible_range(a.seq_lens, MODE == kAddrDense ? a.ring_head : nullptr, b,
                           a.T_cap, a.window);
-  const bool ring = MODE == kAddrDense && a.ring_head != nullptr;
+  ring_slot_order(vr, ring, a.L, a.T_cap);
   int p0, p1;  // this split's virtual rows
   split_range(vr, s, n_split, chunk, p0, p1);
   const int c0 = hc * NH;                // first column (head, token) served
@@ -437,7 +446,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
       a.out[row * DV + e] = ov;
       if (e == 0 && a.lse) a.lse[row] = lse;
     } else {
-      const size_t prow = a.balanced ? (size_t)item * NH + h : row * a.S + s;
+      const size_t prow = BAL ? (size_t)item * NH + h : row * a.S + s;
       a.o_part[prow * DV + e] = ov;
       if (e == 0) a.lse_part[prow] = lse;
     }
@@ -446,8 +455,12 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
 
 template <int DK, int DV, int NH, int MODE>
 hipError_t launch_one(const GqaArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((gqa_decode_mfma<DK, DV, NH, MODE>), dim3(grid), dim3(kNW * 64),
-                     0, st, a);
+  if (a.balanced)
+    hipLaunchKernelGGL((gqa_decode_mfma<DK, DV, NH, MODE, true>), dim3(grid),
+                       dim3(kNW * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((gqa_decode_mfma<DK, DV, NH, MODE, false>), dim3(grid),
+                       dim3(kNW * 64), 0, st, a);
   return hipGetLastError();
 }
 

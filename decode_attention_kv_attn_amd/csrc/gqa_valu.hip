@@ -194,12 +194,13 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
   const int g = bid % a.H_kv;
   const int b = bid / a.H_kv;
 
-  const VisibleRange vr =
+  VisibleRange vr =
       MODE == kAddrGlobal
           ? visible_range(a.seq_lens, nullptr, b, a.T_cap, a.window, a.gpos, a.n_global)
           : visible_range(a.seq_lens, MODE == kAddrDense ? a.ring_head : nullptr, b,
                           a.T_cap, a.window);
   const bool ring = MODE == kAddrDense && a.ring_head != nullptr;
+  ring_slot_order(vr, ring, a.L, a.T_cap);
   int p0, p1;  // this split's virtual rows
   split_range(vr, s, a.S, a.chunk, p0, p1);
   const int c0 = hc * N;                   // first column (head, token) served

