@@ -95,7 +95,7 @@ struct MfmaCfg {
   static constexpr int CPR = DV / 8;                      // 16-byte chunks per V row
   static constexpr int RPI = CPR >= 64 ? 1 : 64 / CPR;    // rows per load instruction
   static constexpr int VLD = kTT / RPI;                   // V loads per lane per tile
-  static constexpr int MERGE_BYTES = kNW * NH * (DV + 2) * 4;
+  static constexpr int MERGE_BYTES = kNW * NH * (DV + 3) * 4;
   static constexpr int LOOP_BYTES = kNW * VT_BYTES;
   static constexpr int SMEM = MERGE_BYTES > LOOP_BYTES ? MERGE_BYTES : LOOP_BYTES;
   static_assert(DV % 32 == 0 && DV == DK, "value columns");
@@ -409,6 +409,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   float* sm_o = (float*)smem;                       // [NW][NH][DV]
   float* sm_m = sm_o + kNW * NH * DV;               // [NW][NH]
   float* sm_l = sm_m + kNW * NH;                    // [NW][NH]
+  float* sm_w = sm_l + kNW * NH;                    // [NW][NH] weight / L
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int h = hb * 16 + li;
@@ -422,34 +423,50 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   }
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < nh * DV; idx += kNW * 64) {
-    const int h = idx / DV;
-    const int e = idx - h * DV;
+  // One lane per column merges the waves' (m, l) by the log-sum-exp rule
+  // and leaves each wave's weight divided by the total, so the value pass
+  // below is four multiply-adds per element with no exponentials.
+  const bool direct = n_split == 1;
+  if (threadIdx.x < nh) {
+    const int h = threadIdx.x;
     float M = neg_inf();
 #pragma unroll
     for (int w = 0; w < kNW; ++w) M = fmaxf(M, sm_m[w * NH + h]);
-    float L = 0.f, O = 0.f;
-    if (M != neg_inf()) {
+    float wt[kNW], L = 0.f;
 #pragma unroll
-      for (int w = 0; w < kNW; ++w) {
-        const float mw = sm_m[w * NH + h];
-        const float wt = (mw == neg_inf()) ? 0.f : fast_exp2(mw - M);
-        L = fmaf(wt, sm_l[w * NH + h], L);
-        O = fmaf(wt, sm_o[((size_t)w * NH + h) * DV + e], O);
-      }
+    for (int w = 0; w < kNW; ++w) {
+      const float mw = sm_m[w * NH + h];
+      wt[w] = (M == neg_inf() || mw == neg_inf()) ? 0.f : fast_exp2(mw - M);
+      L = fmaf(wt[w], sm_l[w * NH + h], L);
     }
     const bool empty = !(L > 0.f);
-    const float ov = empty ? 0.f : O / L;
+    const float inv = empty ? 0.f : 1.f / L;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) sm_w[w * NH + h] = wt[w] * inv;
     const float lse = empty ? neg_inf() : (M + fast_log2(L)) * kLn2;
     const size_t row = query_row(b, g, c0 + h, a.n, a.L, a.H_q);
-    if (n_split == 1) {
-      a.out[row * DV + e] = ov;
-      if (e == 0 && a.lse) a.lse[row] = lse;
+    if (direct) {
+      if (a.lse) a.lse[row] = lse;
     } else {
-      const size_t prow = BAL ? (size_t)item * NH + h : row * a.S + s;
-      a.o_part[prow * DV + e] = ov;
-      if (e == 0) a.lse_part[prow] = lse;
+      a.lse_part[BAL ? (size_t)item * NH + h : row * a.S + s] = lse;
     }
+  }
+  __syncthreads();
+
+  // values: four adjacent columns per lane and step (16-byte LDS reads)
+  constexpr int DV4 = DV / 4;
+  for (int idx = threadIdx.x; idx < nh * DV4; idx += kNW * 64) {
+    const int h = idx / DV4;
+    const int e = 4 * (idx - h * DV4);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kNW; ++w)
+      acc += sm_w[w * NH + h] * *(const f32x4_t*)(sm_o + ((size_t)w * NH + h) * DV + e);
+    const size_t row = query_row(b, g, c0 + h, a.n, a.L, a.H_q);
+    float* dst = direct ? a.out + row * DV + e
+                        : a.o_part + (BAL ? (size_t)item * NH + h : row * a.S + s) * DV + e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = acc[i];
   }
 }
 

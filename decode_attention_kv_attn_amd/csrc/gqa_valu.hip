@@ -174,6 +174,7 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
   __shared__ float sm_acc[NW][N][D];
   __shared__ float sm_m[NW][N];
   __shared__ float sm_l[NW][N];
+  __shared__ float sm_w[NW][N];  // each wave's merge weight divided by the total
 
   const int lane = threadIdx.x & 63;
   // uniform across the wave: tile bases and page ids stay scalar
@@ -426,33 +427,43 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
   __syncthreads();
 
   // ---- merge the waves and write ------------------------------------------
-  for (int idx = threadIdx.x; idx < nh * D; idx += NW * 64) {
-    const int h = idx / D;
-    const int e = idx - h * D;
+  // One lane per head merges the waves' (m, l) by the log-sum-exp rule and
+  // leaves each wave's weight divided by the total; the value pass is then
+  // NW multiply-adds per element with no exponentials.
+  if (threadIdx.x < nh) {
+    const int h = threadIdx.x;
     float M = neg_inf();
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
-    float L = 0.f, O = 0.f;
-    if (M != neg_inf()) {
+    float wt[NW], L = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float mw = sm_m[w][h];
-        const float wt = (mw == neg_inf()) ? 0.f : fast_exp2(mw - M);
-        L = fmaf(wt, sm_l[w][h], L);
-        O = fmaf(wt, sm_acc[w][h][e], O);
-      }
+    for (int w = 0; w < NW; ++w) {
+      const float mw = sm_m[w][h];
+      wt[w] = (M == neg_inf() || mw == neg_inf()) ? 0.f : fast_exp2(mw - M);
+      L = fmaf(wt[w], sm_l[w][h], L);
     }
     const bool empty = !(L > 0.f);
-    const float o = empty ? 0.f : O / L;
+    const float inv = empty ? 0.f : 1.f / L;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sm_w[w][h] = wt[w] * inv;
     const float lse = empty ? neg_inf() : (M + fast_log2(L)) * kLn2;
     const size_t row = query_row(b, g, c0 + h, a.n, a.L, a.H_q);
     if (a.S == 1) {
-      a.out[row * D + e] = o;
-      if (e == 0 && a.lse) a.lse[row] = lse;
+      if (a.lse) a.lse[row] = lse;
     } else {
-      a.o_part[(row * a.S + s) * D + e] = o;
-      if (e == 0) a.lse_part[row * a.S + s] = lse;
+      a.lse_part[row * a.S + s] = lse;
     }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nh * D; idx += NW * 64) {
+    const int h = idx / D;
+    const int e = idx - h * D;
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) o = fmaf(sm_w[w][h], sm_acc[w][h][e], o);
+    const size_t row = query_row(b, g, c0 + h, a.n, a.L, a.H_q);
+    if (a.S == 1) a.out[row * D + e] = o;
+    else a.o_part[(row * a.S + s) * D + e] = o;
   }
 }
 
