@@ -125,8 +125,12 @@ struct BalancedMap {
 
 // CPL = d_v / 64 columns per lane, read as CPL / VW vectors of VW floats.
 // BAL: the parts come from a balanced work list (`bm`), else S parts per row
-// stored next to each other.
-template <int CPL, bool BAL>
+// stored next to each other.  WPR waves share a row (parts s = sub, sub +
+// WPR, ...) and add their sums in LDS: few rows with many parts (one long
+// sequence cut into many pieces) would otherwise leave most of the GPU idle
+// while one wave per row walks every part.  Eight parts are in flight per
+// wave.
+template <int CPL, bool BAL, int WPR>
 __global__ __launch_bounds__(kThreads) void lse_combine_rows(
     const float* __restrict__ o_part, const float* __restrict__ lse_part,
     float* __restrict__ out, float* __restrict__ lse_out, int rows, int S,
@@ -134,15 +138,22 @@ __global__ __launch_bounds__(kThreads) void lse_combine_rows(
   constexpr int VW = CPL >= 4 ? 4 : CPL;
   constexpr int NV = CPL / VW;
   constexpr int d_v = 64 * CPL;
+  constexpr int NWG = kThreads / 64;
+  constexpr int RPB = NWG / WPR;  // rows per work group
+  constexpr int DEPTH = 8;        // parts in flight per wave
+  static_assert(NWG % WPR == 0 && (!BAL || WPR == 1), "waves per row");
   typedef typename VecOf<VW>::type vec;
-  __shared__ float wts[kThreads / 64][kMaxS];
+  __shared__ float wts[NWG][kMaxS];
+  __shared__ float red[WPR > 1 ? NWG : 1][WPR > 1 ? d_v : 1];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const size_t row = (size_t)blockIdx.x * (kThreads / 64) + wave;
-  if (row >= (size_t)rows) return;
+  const int sub = wave % WPR;
+  const size_t row = (size_t)blockIdx.x * RPB + wave / WPR;
+  bool active = row < (size_t)rows;
   size_t base = row * S;  // part row of part 0
   int stride = 1;         // part rows between consecutive parts
   if constexpr (BAL) {
+    if (!active) return;
     const int per_b = bm.L * bm.H_q;
     const int b = (int)(row / per_b);
     const int rem = (int)(row - (size_t)b * per_b);
@@ -155,48 +166,66 @@ __global__ __launch_bounds__(kThreads) void lse_combine_rows(
     base = (size_t)(bm.meta[2 * b] + g * S * bm.hc + chunk) * bm.nh + (c - chunk * bm.nh);
     stride = bm.hc * bm.nh;
   }
-  const float* lp = lse_part + base;
-  float* w_s = wts[wave];
-
-  // weights of the parts (natural-log input, log2 inside); this wave's own
-  // LDS row, so no barrier is needed between writing and reading it
-  float M = neg_inf();
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[(size_t)s * stride] * kLog2e);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float tot = 0.f;
-  for (int s = lane; s < S; s += 64) {
-    const float x = lp[(size_t)s * stride];
-    const float w = (x == neg_inf() || M == neg_inf()) ? 0.f : fast_exp2(x * kLog2e - M);
-    w_s[s] = w;
-    tot += w;
+  if constexpr (WPR == 1) {
+    if (!active) return;
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
-  if (lane == 0 && lse_out)
-    lse_out[row] = (tot > 0.f) ? (M + fast_log2(tot)) * kLn2 : neg_inf();
-  const float inv = (tot > 0.f) ? 1.f / tot : 0.f;
-
-  // lane owns columns VW*(lane + 64 v) .. +VW-1 for v < NV
-  const vec* op = reinterpret_cast<const vec*>(o_part + base * d_v) + lane;
-  const size_t step = (size_t)stride * (d_v / VW);  // vectors between parts
   float acc[NV][VW] = {};
-  int s = 0;
-  for (; s + 4 <= S; s += 4) {
-    vec x[4][NV];
+  float M = neg_inf(), tot = 0.f;
+  if (active) {
+    const float* lp = lse_part + base;
+    float* w_s = wts[wave];
+    // weights of every part (natural-log input, log2 inside), in this wave's
+    // own LDS row, so no barrier is needed between writing and reading it
+    for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[(size_t)s * stride] * kLog2e);
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    for (int s = lane; s < S; s += 64) {
+      const float x = lp[(size_t)s * stride];
+      const float w = (x == neg_inf() || M == neg_inf()) ? 0.f : fast_exp2(x * kLog2e - M);
+      w_s[s] = w;
+      tot += w;
+    }
 #pragma unroll
-      for (int v = 0; v < NV; ++v) x[k][v] = op[(size_t)(s + k) * step + 64 * v];
+    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
+    if (sub == 0 && lane == 0 && lse_out)
+      lse_out[row] = (tot > 0.f) ? (M + fast_log2(tot)) * kLn2 : neg_inf();
+
+    // lane owns columns VW*(lane + 64 v) .. +VW-1 for v < NV
+    const vec* op = reinterpret_cast<const vec*>(o_part + base * d_v) + lane;
+    const size_t step = (size_t)stride * (d_v / VW);  // vectors between parts
+    int s = sub;
+    for (; s + (DEPTH - 1) * WPR < S; s += DEPTH * WPR) {
+      vec x[DEPTH][NV];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < DEPTH; ++k)
 #pragma unroll
-      for (int v = 0; v < NV; ++v) fma_vec<VW>(acc[v], w_s[s + k], x[k][v]);
+        for (int v = 0; v < NV; ++v) x[k][v] = op[(size_t)(s + k * WPR) * step + 64 * v];
+#pragma unroll
+      for (int k = 0; k < DEPTH; ++k)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) fma_vec<VW>(acc[v], w_s[s + k * WPR], x[k][v]);
+    }
+    for (; s < S; s += WPR) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) fma_vec<VW>(acc[v], w_s[s], op[(size_t)s * step + 64 * v]);
+    }
   }
-  for (; s < S; ++s) {
+  if constexpr (WPR > 1) {
+    // the row's waves meet in LDS (element (v, i) of lane l at (v*VW+i)*64+l)
 #pragma unroll
-    for (int v = 0; v < NV; ++v) fma_vec<VW>(acc[v], w_s[s], op[(size_t)s * step + 64 * v]);
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int i = 0; i < VW; ++i) red[wave][(v * VW + i) * 64 + lane] = acc[v][i];
+    __syncthreads();
+    if (!active || sub != 0) return;
+#pragma unroll
+    for (int j = 1; j < WPR; ++j)
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int i = 0; i < VW; ++i) acc[v][i] += red[wave + j][(v * VW + i) * 64 + lane];
   }
+  const float inv = (tot > 0.f) ? 1.f / tot : 0.f;
   vec* dst = reinterpret_cast<vec*>(out + row * d_v) + lane;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
@@ -208,27 +237,28 @@ __global__ __launch_bounds__(kThreads) void lse_combine_rows(
   }
 }
 
-template <bool BAL>
+template <bool BAL, int WPR>
 hipError_t launch_rows(int cpl, const float* o_part, const float* lse_part, float* out,
                        float* lse, int rows, int S, const BalancedMap& bm,
                        hipStream_t stream) {
-  const dim3 g((unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64))), blk(kThreads);
+  constexpr int RPB = kThreads / 64 / WPR;
+  const dim3 g((unsigned)((rows + RPB - 1) / RPB)), blk(kThreads);
   switch (cpl) {
     case 1:
-      hipLaunchKernelGGL((lse_combine_rows<1, BAL>), g, blk, 0, stream, o_part, lse_part,
-                         out, lse, rows, S, bm);
+      hipLaunchKernelGGL((lse_combine_rows<1, BAL, WPR>), g, blk, 0, stream, o_part,
+                         lse_part, out, lse, rows, S, bm);
       break;
     case 2:
-      hipLaunchKernelGGL((lse_combine_rows<2, BAL>), g, blk, 0, stream, o_part, lse_part,
-                         out, lse, rows, S, bm);
+      hipLaunchKernelGGL((lse_combine_rows<2, BAL, WPR>), g, blk, 0, stream, o_part,
+                         lse_part, out, lse, rows, S, bm);
       break;
     case 4:
-      hipLaunchKernelGGL((lse_combine_rows<4, BAL>), g, blk, 0, stream, o_part, lse_part,
-                         out, lse, rows, S, bm);
+      hipLaunchKernelGGL((lse_combine_rows<4, BAL, WPR>), g, blk, 0, stream, o_part,
+                         lse_part, out, lse, rows, S, bm);
       break;
     case 8:
-      hipLaunchKernelGGL((lse_combine_rows<8, BAL>), g, blk, 0, stream, o_part, lse_part,
-                         out, lse, rows, S, bm);
+      hipLaunchKernelGGL((lse_combine_rows<8, BAL, WPR>), g, blk, 0, stream, o_part,
+                         lse_part, out, lse, rows, S, bm);
       break;
     default: return hipErrorInvalidValue;
   }
@@ -244,9 +274,16 @@ hipError_t launch_combine(const float* o_part, const float* lse_part,
   const int rows = B * H;
   const bool vec_ok = ((uintptr_t)o_part % 16 == 0) && ((uintptr_t)out % 16 == 0);
   const int cpl = d_v % 64 == 0 ? d_v / 64 : 0;  // columns per lane, one wave per row
-  if (vec_ok && (cpl == 1 || cpl == 2 || cpl == 4 || cpl == 8))
-    return launch_rows<false>(cpl, o_part, lse_part, out, lse, rows, S, BalancedMap{},
-                              stream);
+  if (vec_ok && (cpl == 1 || cpl == 2 || cpl == 4 || cpl == 8)) {
+    // waves per row: enough waves for the GPU when rows are few and parts
+    // many (about four per CU), else one
+    const BalancedMap none{};
+    if (S >= 32 && rows <= 256)
+      return launch_rows<false, 4>(cpl, o_part, lse_part, out, lse, rows, S, none, stream);
+    if (S >= 16 && rows <= 512)
+      return launch_rows<false, 2>(cpl, o_part, lse_part, out, lse, rows, S, none, stream);
+    return launch_rows<false, 1>(cpl, o_part, lse_part, out, lse, rows, S, none, stream);
+  }
   const int cl = d_v >= 256 ? 256 : (d_v > 128 ? 256 : (d_v > 64 ? 128 : 64));
   hipLaunchKernelGGL(lse_combine, dim3((unsigned)rows), dim3(kThreads), 0, stream,
                      o_part, lse_part, out, lse, S, d_v, cl);
@@ -261,8 +298,8 @@ hipError_t launch_combine_balanced(const float* o_part, const float* lse_part,
       d_v > 256)
     return hipErrorInvalidValue;
   const BalancedMap bm{meta, L, H_q, n, head_chunks, heads_per_item};
-  return launch_rows<true>(d_v / 64, o_part, lse_part, out, lse, B * L * H_q, 0, bm,
-                           stream);
+  return launch_rows<true, 1>(d_v / 64, o_part, lse_part, out, lse, B * L * H_q, 0, bm,
+                              stream);
 }
 
 }  // namespace attn

@@ -132,18 +132,21 @@ def test_split_invariance(num_splits):
 
 
 @pytest.mark.parametrize("d_v", [64, 128, 256, 512])
-@pytest.mark.parametrize("S", [1, 3, 6, 9])
+@pytest.mark.parametrize("S", [1, 3, 6, 9, 17, 40, 129])
 def test_combine_widths(d_v, S):
-    """The one-wave-per-row merge at every width the decode kernels emit:
-    7 rows (not a multiple of the 4 rows per group), part counts around the
-    4-part unroll, empty parts and an all-empty row."""
+    """The row merge at every width the decode kernels emit: 7 rows (not a
+    multiple of the rows per group), part counts around the 8-part unroll and
+    past the thresholds where two and four waves share a row (17, 40, 129),
+    empty parts (their values poisoned: never read) and an all-empty row."""
     B, H = 1, 7
     g = torch.Generator(device="cpu").manual_seed(6520 + d_v + S)
     o = torch.randn(B, H, S, d_v, generator=g)
     l = torch.randn(B, H, S, generator=g) * 4
     l[0, 2, S - 1] = -math.inf
     l[0, 5, :] = -math.inf
-    out, lse = L.attn_combine(o.to(DEV), l.to(DEV))
+    o_dev = o.clone()
+    o_dev[0, 2, S - 1] = float("nan")
+    out, lse = L.attn_combine(o_dev.to(DEV), l.to(DEV))
     ro, rl = oracle.combine_ref(o.double().numpy(), l.double().numpy())
     assert_parity(out, ro, f"combine d_v={d_v} S={S}")
     assert_lse(lse, rl, f"combine d_v={d_v} S={S}")
