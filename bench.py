@@ -374,7 +374,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": w["name"], "B": B, "H_q": H_q, "H_kv": H_kv,
                    "d": d, "T": T, "window": inp["window"], "ring": ring,
-                   "splits": S, "cache_copies": R, "settle_steps": settle,
+                   "splits": S,
+                   "balanced_list": bool(plan["balanced_groups"] and inp["seq_lens"] is not None
+                                         and args.num_splits == 0),
+                   "cache_copies": R, "settle_steps": settle,
                    "kv_bytes_per_step": alg_bytes},
         "roofline": {
             "bound": "hbm",
