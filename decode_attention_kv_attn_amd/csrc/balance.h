@@ -115,14 +115,16 @@ ATTN_DEV WorkItem balanced_item(const int32_t* seq_lens, const int32_t* ring_hea
       head[i] = ring_head ? ring_head[b] : 0;
       const int n = visible_range_of(len[i], ring_head != nullptr, head[i], T_cap,
                                      window, gpos, n_global).n;
-      nt[i] = (n + tile - 1) / tile;
+      nt[i] = (int)(((unsigned)n + tile - 1) / (unsigned)tile);
       sum_t += nt[i];
       max_t = max(max_t, nt[i]);
     }
   }
-  sum_t = wave_sum_i(sum_t);
+  // sums as unsigned: at most 256 sequences of 2^23 tiles (2^30 rows) each,
+  // plus one piece per sequence, stay below 2^32
+  const unsigned sum_all = (unsigned)wave_sum_i(sum_t);
   max_t = wave_max_i(max_t);
-  const int slots = cap / U;  // pieces the list may hold per unit
+  const unsigned slots = (unsigned)(cap / U);  // pieces the list may hold per unit
 
   // pieces per unit of every sequence at C = m tiles; ceil(n / (m * tile))
   // equals ceil(ceil(n / tile) / m)
@@ -131,17 +133,19 @@ ATTN_DEV WorkItem balanced_item(const int32_t* seq_lens, const int32_t* ring_hea
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
       if (nt[i] >= 0) c += nt[i] <= m ? 1 : (nt[i] + m - 1) / m;
-    return wave_sum_i(c);
+    return (unsigned)wave_sum_i(c);
   };
-  // Bounds of the search: the list needs at least sum_t / m pieces, and
-  // ceil(x / m) <= x / m + 1 bounds it by sum_t / m + B, so m =
-  // ceil(sum_t / (slots - B)) fits whenever slots > B; one piece per
+  // Bounds of the search: the list needs at least sum_all / m pieces, and
+  // ceil(x / m) <= x / m + 1 bounds it by sum_all / m + B, so m =
+  // ceil(sum_all / (slots - B)) fits whenever slots > B; one piece per
   // sequence (m = max_t) always fits.
-  int lo = max((c_min + tile - 1) / tile,
-               (int)(((long long)sum_t + slots - 1) / slots));
+  int lo = max((c_min + tile - 1) / tile, (int)((sum_all + slots - 1) / slots));
   lo = max(lo, 1);
   int hi = max(max_t, 1);
-  if (slots > B) hi = min(hi, (sum_t + (slots - B) - 1) / (slots - B));
+  if (slots > (unsigned)B) {
+    const unsigned room = slots - (unsigned)B;
+    hi = min(hi, (int)((sum_all + room - 1) / room));
+  }
   hi = max(hi, lo);
   if (count(lo) <= slots) hi = lo;  // the common case: the lower bound fits
   while (lo < hi) {  // smallest m in [lo, hi] whose list fits
