@@ -95,7 +95,11 @@ struct MfmaCfg {
   static constexpr int CPR = DV / 8;                      // 16-byte chunks per V row
   static constexpr int RPI = CPR >= 64 ? 1 : 64 / CPR;    // rows per load instruction
   static constexpr int VLD = kTT / RPI;                   // V loads per lane per tile
-  static constexpr int MERGE_BYTES = kNW * NH * (DV + 3) * 4;
+  // merge rows of DV + 4 floats: the 16 lanes of a group write 16 heads'
+  // rows with one 16-byte store each, so an unpadded stride (a multiple of
+  // the bank width) would put all of them on the same banks
+  static constexpr int ORS = DV + 4;
+  static constexpr int MERGE_BYTES = kNW * NH * (ORS + 3) * 4;
   static constexpr int LOOP_BYTES = kNW * VT_BYTES;
   static constexpr int SMEM = MERGE_BYTES > LOOP_BYTES ? MERGE_BYTES : LOOP_BYTES;
   static_assert(DV % 32 == 0 && DV == DK, "value columns");
@@ -406,8 +410,9 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
   }
 
   __syncthreads();  // the V tiles are dead; reuse LDS for the merge
-  float* sm_o = (float*)smem;                       // [NW][NH][DV]
-  float* sm_m = sm_o + kNW * NH * DV;               // [NW][NH]
+  constexpr int ORS = C::ORS;
+  float* sm_o = (float*)smem;                       // [NW][NH][ORS]
+  float* sm_m = sm_o + kNW * NH * ORS;              // [NW][NH]
   float* sm_l = sm_m + kNW * NH;                    // [NW][NH]
   float* sm_w = sm_l + kNW * NH;                    // [NW][NH] weight / L
 #pragma unroll
@@ -415,7 +420,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
     const int h = hb * 16 + li;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      *(f32x4_t*)(sm_o + ((size_t)wave * NH + h) * DV + 16 * db + 4 * lg) = o[db][hb];
+      *(f32x4_t*)(sm_o + ((size_t)wave * NH + h) * ORS + 16 * db + 4 * lg) = o[db][hb];
     if (lg == 0) {
       sm_m[wave * NH + h] = m[hb];
       sm_l[wave * NH + h] = l[hb];
@@ -461,7 +466,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kNW; ++w)
-      acc += sm_w[w * NH + h] * *(const f32x4_t*)(sm_o + ((size_t)w * NH + h) * DV + e);
+      acc += sm_w[w * NH + h] * *(const f32x4_t*)(sm_o + ((size_t)w * NH + h) * ORS + e);
     const size_t row = query_row(b, g, c0 + h, a.n, a.L, a.H_q);
     float* dst = direct ? a.out + row * DV + e
                         : a.o_part + (BAL ? (size_t)item * NH + h : row * a.S + s) * DV + e;
