@@ -174,13 +174,28 @@ __global__ __launch_bounds__(kThreads) void lse_combine_rows(
   if (active) {
     const float* lp = lse_part + base;
     float* w_s = wts[wave];
+    // lane owns columns VW*(lane + 64 v) .. +VW-1 for v < NV
+    const vec* op = reinterpret_cast<const vec*>(o_part + base * d_v) + lane;
+    const size_t step = (size_t)stride * (d_v / VW);  // vectors between parts
+    // The first DEPTH parts' values go out with the log-sum-exps (they do not
+    // depend on the weights), so a row of up to DEPTH parts costs one memory
+    // round trip instead of two.
+    vec x0[DEPTH][NV];
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k)
+      if (sub + k * WPR < S)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) x0[k][v] = op[(size_t)(sub + k * WPR) * step + 64 * v];
+    const float l_first = lane < S ? lp[(size_t)lane * stride] : neg_inf();
+
     // weights of every part (natural-log input, log2 inside), in this wave's
     // own LDS row, so no barrier is needed between writing and reading it
-    for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[(size_t)s * stride] * kLog2e);
+    M = l_first * kLog2e;
+    for (int s = lane + 64; s < S; s += 64) M = fmaxf(M, lp[(size_t)s * stride] * kLog2e);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     for (int s = lane; s < S; s += 64) {
-      const float x = lp[(size_t)s * stride];
+      const float x = s == lane ? l_first : lp[(size_t)s * stride];
       const float w = (x == neg_inf() || M == neg_inf()) ? 0.f : fast_exp2(x * kLog2e - M);
       w_s[s] = w;
       tot += w;
@@ -190,10 +205,12 @@ __global__ __launch_bounds__(kThreads) void lse_combine_rows(
     if (sub == 0 && lane == 0 && lse_out)
       lse_out[row] = (tot > 0.f) ? (M + fast_log2(tot)) * kLn2 : neg_inf();
 
-    // lane owns columns VW*(lane + 64 v) .. +VW-1 for v < NV
-    const vec* op = reinterpret_cast<const vec*>(o_part + base * d_v) + lane;
-    const size_t step = (size_t)stride * (d_v / VW);  // vectors between parts
-    int s = sub;
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k)
+      if (sub + k * WPR < S)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) fma_vec<VW>(acc[v], w_s[sub + k * WPR], x0[k][v]);
+    int s = sub + DEPTH * WPR;
     for (; s + (DEPTH - 1) * WPR < S; s += DEPTH * WPR) {
       vec x[DEPTH][NV];
 #pragma unroll
