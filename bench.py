@@ -398,6 +398,14 @@ def main():
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+        # the same oracle on one BLAS thread, over a shorter sample
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                one = cpu_baseline(w, inp, args.cpu_seconds / 2)
+            res["cpu_baseline_1thread"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
+        except ImportError:  # pragma: no cover
+            pass
     print(json.dumps(res), flush=True)
 
 
