@@ -121,19 +121,22 @@ def test_poison_past_lengths():
     assert_lse(lse, rl, "balanced poison")
 
 
-def test_most_sequences():
-    """200 sequences (four rounds of 64 lanes), lengths uniform on 0..1024;
-    257 sequences fall back to the fixed splits."""
-    B, T = 200, 1024
+@pytest.mark.parametrize("B", [1, 200, 255])
+def test_batch_sizes(B):
+    """One sequence (its pieces follow its own length, not T_cap), 200 and 255
+    sequences (four rounds of 64 lanes, the last partial); 256 units fill
+    the grid and 257 sequences exceed the list: both keep the fixed splits."""
+    T = 1024
     assert _balanced(B, 32, 1, T, 64)
+    assert not _balanced(256, 32, 1, T, 64)
     assert not _balanced(257, 32, 1, T, 64)
-    lens = synth.draw_ints(B, 0, T, 12300).tolist()
+    lens = [700] if B == 1 else synth.draw_ints(B, 0, T, 12300 + B).tolist()
     q, k, v, sl = _inputs(lens, 32, 1, T, 64, 12301)
     out, lse = L.attn_decode_gqa(q, k, v, sl)
     torch.cuda.synchronize()
     ro, rl = oracle.gqa_decode_ref(q, k, v, sl)
-    assert_parity(out, ro, "balanced B=200")
-    assert_lse(lse, rl, "balanced B=200")
+    assert_parity(out, ro, f"balanced B={B}")
+    assert_lse(lse, rl, f"balanced B={B}")
 
 
 @pytest.mark.parametrize("window", [0, 700, 1023])
