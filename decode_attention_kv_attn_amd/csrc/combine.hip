@@ -8,13 +8,14 @@
 // weight 0; if every part is empty the output is 0 and lse is -inf.
 //
 // Value widths that are a multiple of 64 up to 512 (every width the decode
-// kernels produce): one wave per (b, h), each lane owning d_v / 64 adjacent
-// columns, read as one vector per part; the loads of four parts are in
-// flight at once, and the weights come from the same wave, so one row costs
-// about two memory round trips.  Other widths: one work group of 256 lanes
-// per (b, h): lanes cover the columns (up to 256 at a time) and, when the
-// value is narrower than 256, the remaining lanes split the parts between
-// them and meet in LDS.
+// kernels produce): one wave per (b, h) -- two or four when rows are few and
+// parts many -- each lane owning d_v / 64 adjacent columns, read as vectors;
+// eight parts are in flight per wave, the first eight together with the
+// log-sum-exps, and the weights come from the same wave, so a row of up to
+// eight parts costs one memory round trip.  Other widths: one work group of
+// 256 lanes per (b, h): lanes cover the columns (up to 256 at a time) and,
+// when the value is narrower than 256, the remaining lanes split the parts
+// between them and meet in LDS.
 
 #include "device_common.h"
 #include "internal.h"
