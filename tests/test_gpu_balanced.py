@@ -242,3 +242,38 @@ def test_fallbacks_to_fixed_splits():
     assert_parity(o1, ro, "unaligned out")
     assert_lse(l1, rl, "unaligned out")
     assert torch.equal(o2, fixed_o) and torch.equal(l2, fixed_l)
+
+
+def test_graph_replays_follow_new_lengths():
+    """The list is built on the device from seq_lens, so a captured call
+    replays correctly after the lengths change (no host read of the lengths;
+    only kernels are captured).  Eager work runs between the replays, and
+    every replay is checked against the oracle."""
+    T, d = 2048, 128
+    lens0 = [2048, 1, 0, 1500, 129, 640, 2047, 300]
+    B = len(lens0)
+    q, k, v, sl = _inputs(lens0, 32, 1, T, d, 12900)
+    assert _balanced(B, 32, 1, T, d)
+    out = torch.empty(B, 32, d, dtype=torch.float32, device=DEV)
+    lse = torch.empty(B, 32, dtype=torch.float32, device=DEV)
+    ws = torch.empty(L.attn_decode_gqa_workspace_bytes(B, 32, 1, T, d, 1), dtype=torch.uint8,
+                     device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up off the default stream, as capture requires
+        L.attn_decode_gqa(q, k, v, sl, out=out, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        L.attn_decode_gqa(q, k, v, sl, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    for trial, lens in enumerate([lens0, [5, 2048, 2048, 0, 0, 17, 1000, 1],
+                                  [0] * B, [2048] * B]):
+        sl.copy_(torch.tensor(lens, dtype=torch.int32))
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        ro, rl = oracle.gqa_decode_ref(q, k, v, sl)
+        assert_parity(out, ro, f"replay {trial}")
+        assert_lse(lse, rl, f"replay {trial}")
