@@ -141,8 +141,8 @@ int plan_gqa(int B, int H_q, int H_kv, int T_cap, int d, int dtype, int window,
   // whole ring (or its window), the same for every sequence, and the list's
   // setup (about a microsecond per group) would buy nothing.
   p->cap = 0;
-  if (p->mfma && num_splits == 0 && p->S > 1 && !ring && B >= 1 &&
-      B <= kBalanceMaxB && target_groups() <= ATTN_MAX_SPLITS) {
+  if (num_splits == 0 && p->S > 1 && !ring && B >= 1 && B <= kBalanceMaxB &&
+      target_groups() <= ATTN_MAX_SPLITS) {
     p->cap = target_groups();
     const size_t bb = balanced_bytes(p->cap, p->N, d, B);
     if (bb > p->ws_bytes) p->ws_bytes = bb;

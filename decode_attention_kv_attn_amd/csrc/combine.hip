@@ -115,7 +115,7 @@ ATTN_DEV void fma_vec(float (&acc)[N], float w, const typename VecOf<N>::type& x
   for (int i = 0; i < N; ++i) acc[i] = add_part(acc[i], w, xs[i]);
 }
 
-// Balanced work list (the GQA matrix-core kernel's): output row
+// Balanced work list (both GQA kernels): output row
 // (b * L + token) * H_q + head belongs to column c = (head % n) * L + token of
 // KV head head / n, i.e. column c % nh of head chunk c / nh; piece s of it is
 // item meta[2b] + (g * k + s) * hc + c / nh with k = meta[2b + 1].

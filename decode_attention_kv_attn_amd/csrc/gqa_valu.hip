@@ -34,6 +34,7 @@
 
 #include <limits.h>
 
+#include "balance.h"
 #include "device_common.h"
 #include "internal.h"
 #include "visible.h"
@@ -163,7 +164,9 @@ ATTN_DEV void merge_fn(float (&m)[N], float (&l)[N], float (&acc)[N][E], F mv) {
   }
 }
 
-template <typename T, int D, int N, int MODE>
+// BAL: work items from the balanced list (GqaArgs::balanced, balance.h); a
+// template parameter so that the fixed-split kernels carry none of it.
+template <typename T, int D, int N, int MODE, bool BAL>
 __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
     GqaArgs a) {
   using C = Cfg<T, D, N>;
@@ -188,22 +191,50 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
     const int per = gridDim.x / kNumXCDs;
     bid = (bid % kNumXCDs) * per + bid / kNumXCDs;
   }
-  const int hc = bid % a.head_chunks;
-  bid /= a.head_chunks;
-  const int s = bid % a.S;
-  bid /= a.S;
-  const int g = bid % a.H_kv;
-  const int b = bid / a.H_kv;
+  const int item = bid;
+  int hc, s, g, b, n_split = a.S, chunk = a.chunk;
+  int len_b = 0;  // balanced: the item's stored length
+  if constexpr (BAL) {
+    // item r of sequence b: ((g * k + s) * head_chunks + hc)
+    const WorkItem wi = balanced_item(
+        a.seq_lens, nullptr, a.B, a.T_cap, a.window, MODE == kAddrGlobal ? a.gpos : nullptr,
+        MODE == kAddrGlobal ? a.n_global : 0, a.H_kv * a.head_chunks, a.cap, NW * TR,
+        2 * NW * TR, item);
+    if (!wi.valid) return;  // uniform over the work group
+    b = wi.b;
+    len_b = wi.len;
+    n_split = wi.k;
+    chunk = wi.chunk;
+    int r = wi.r;
+    hc = r % a.head_chunks;
+    r /= a.head_chunks;
+    s = r % wi.k;
+    g = r / wi.k;
+    if (wi.r == 0 && threadIdx.x == 0) {
+      a.meta[2 * b] = wi.first;
+      a.meta[2 * b + 1] = wi.k;
+    }
+  } else {
+    hc = bid % a.head_chunks;
+    bid /= a.head_chunks;
+    s = bid % a.S;
+    bid /= a.S;
+    g = bid % a.H_kv;
+    b = bid / a.H_kv;
+  }
 
   VisibleRange vr =
-      MODE == kAddrGlobal
+      BAL ? visible_range_of(len_b, false, 0, a.T_cap, a.window,
+                             MODE == kAddrGlobal ? a.gpos : nullptr,
+                             MODE == kAddrGlobal ? a.n_global : 0)
+      : MODE == kAddrGlobal
           ? visible_range(a.seq_lens, nullptr, b, a.T_cap, a.window, a.gpos, a.n_global)
           : visible_range(a.seq_lens, MODE == kAddrDense ? a.ring_head : nullptr, b,
                           a.T_cap, a.window);
   const bool ring = MODE == kAddrDense && a.ring_head != nullptr;
   ring_slot_order(vr, ring, a.L, a.T_cap);
   int p0, p1;  // this split's virtual rows
-  split_range(vr, s, a.S, a.chunk, p0, p1);
+  split_range(vr, s, n_split, chunk, p0, p1);
   const int c0 = hc * N;                   // first column (head, token) served
   const int nh = min(N, a.ncol - c0);      // columns actually present
 
@@ -448,10 +479,10 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
     for (int w = 0; w < NW; ++w) sm_w[w][h] = wt[w] * inv;
     const float lse = empty ? neg_inf() : (M + fast_log2(L)) * kLn2;
     const size_t row = query_row(b, g, c0 + h, a.n, a.L, a.H_q);
-    if (a.S == 1) {
+    if (n_split == 1) {
       if (a.lse) a.lse[row] = lse;
     } else {
-      a.lse_part[row * a.S + s] = lse;
+      a.lse_part[BAL ? (size_t)item * N + h : row * a.S + s] = lse;
     }
   }
   __syncthreads();
@@ -462,14 +493,19 @@ __global__ __launch_bounds__((Cfg<T, D, N>::NW * 64)) void gqa_decode_valu(
 #pragma unroll
     for (int w = 0; w < NW; ++w) o = fmaf(sm_w[w][h], sm_acc[w][h][e], o);
     const size_t row = query_row(b, g, c0 + h, a.n, a.L, a.H_q);
-    if (a.S == 1) a.out[row * D + e] = o;
-    else a.o_part[(row * a.S + s) * D + e] = o;
+    if (n_split == 1) a.out[row * D + e] = o;
+    else a.o_part[(BAL ? (size_t)item * N + h : row * a.S + s) * D + e] = o;
   }
 }
 
 template <typename T, int D, int N>
 hipError_t launch_one(const GqaArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((gqa_decode_valu<T, D, N, ATTN_VALU_MODE>), dim3(grid),
+  if (a.balanced) {
+    hipLaunchKernelGGL((gqa_decode_valu<T, D, N, ATTN_VALU_MODE, true>), dim3(grid),
+                       dim3(Cfg<T, D, N>::NW * 64), 0, st, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((gqa_decode_valu<T, D, N, ATTN_VALU_MODE, false>), dim3(grid),
                      dim3(Cfg<T, D, N>::NW * 64), 0, st, a);
   return hipGetLastError();
 }

@@ -39,7 +39,7 @@ struct GqaArgs {
   int chunk;        // positions per split
   int xcd_remap;    // 1: map consecutive work items onto one XCD
   float scale_log2; // softmax scale * log2(e)
-  // Balanced work list (matrix-core kernel only): work item w is item w of
+  // Balanced work list (both kernels): work item w is item w of
   // the list by visible rows (balance.h) instead of a fixed split; pieces of
   // a sequence's units go to o_part / lse_part row w * heads_per_item + column,
   // and meta[2b], meta[2b+1] receive the sequence's first item and its pieces

@@ -114,11 +114,11 @@ def test_planner(lib):
         B, H_q, H_kv, _, d, dt, w, ring = args
         plan = L.attn_decode_gqa_plan(B, H_q, H_kv, T, d, dt, w, ring)
         cap = plan["balanced_groups"]
-        # the balanced list is planned only where the fixed plan splits, for
-        # the matrix-core kernel, and keeps one round of work groups
-        assert cap == 0 or (S > 1 and plan["kernel"] == "mfma" and not ring and
+        # the balanced list is planned only where the fixed plan splits (no
+        # rings), for either kernel, and keeps one round of work groups
+        assert cap == 0 or (S > 1 and not ring and
                             B * H_kv * -(-H_q // H_kv // plan["heads_per_item"]) < cap)
-        if S > 1 and plan["kernel"] == "mfma" and not ring and B <= 256:
+        if S > 1 and not ring and B <= 256:
             assert cap > 0
         up = lambda x: -(-x // 256) * 256
         rows = cap * plan["heads_per_item"]

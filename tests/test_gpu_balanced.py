@@ -48,9 +48,11 @@ MIXES = {
     "uniform": [2048] * 8,
     "all_one_piece": [1, 2, 3, 100, 127, 255, 256, 200],
 }
-# (d, H_q, H_kv): MQA-sized groups, two KV heads of 16, d = 256, and 48 heads
-# per KV head (two head chunks of 32 columns)
-KERNELS = [(128, 32, 1), (64, 32, 2), (256, 16, 2), (128, 96, 2)]
+# (d, H_q, H_kv): matrix-core kernel -- MQA-sized groups, two KV heads of 16,
+# d = 256, and 48 heads per KV head (two head chunks of 32 columns); vector
+# kernel -- MHA at d = 64 and groups of 2 at d = 256
+KERNELS = [(128, 32, 1), (64, 32, 2), (256, 16, 2), (128, 96, 2), (64, 8, 8),
+           (256, 8, 4)]
 
 
 @pytest.mark.parametrize("d,H_q,H_kv", KERNELS, ids=[f"d{a}-{b}x{c}" for a, b, c in KERNELS])
@@ -72,6 +74,25 @@ def test_length_mixes(d, H_q, H_kv, mix):
     out2, _ = L.attn_decode_gqa(q, k, v, sl, num_splits=S)
     torch.cuda.synchronize()
     assert_parity(out2, ro, f"fixed {mix}")
+
+
+def test_fp32_vector_kernel():
+    """float32 data always takes the vector kernel: the same list, MQA-sized
+    group of 8 columns per item (four items per KV head)."""
+    lens = [0, 1, 2048, 1500, 129, 2047]
+    T, d = 2048, 64
+    B = len(lens)
+    p = L.attn_decode_gqa_plan(B, 32, 1, T, d, 0)
+    assert p["kernel"] == "valu" and p["balanced_groups"] > 0
+    q = synth.draw((B, 32, d), 12950, "fp32", DEV)
+    k = synth.draw((B, 1, T, d), 12951, "fp32", DEV)
+    v = synth.draw((B, 1, T, d), 12952, "fp32", DEV)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out, lse = L.attn_decode_gqa(q, k, v, sl)
+    torch.cuda.synchronize()
+    ro, rl = oracle.gqa_decode_ref(q, k, v, sl)
+    assert_parity(out, ro, "balanced fp32")
+    assert_lse(lse, rl, "balanced fp32")
 
 
 def test_integer_recovery_balanced():
