@@ -313,7 +313,7 @@ hipError_t launch_combine_balanced(const float* o_part, const float* lse_part,
                                    int L, int H_q, int n, int head_chunks,
                                    int heads_per_item, int d_v, hipStream_t stream) {
   if ((uintptr_t)o_part % 16 != 0 || (uintptr_t)out % 16 != 0 || d_v % 64 != 0 ||
-      d_v > 256)
+      d_v > 512)
     return hipErrorInvalidValue;
   const BalancedMap bm{meta, L, H_q, n, head_chunks, heads_per_item};
   return launch_rows<true, 1>(d_v / 64, o_part, lse_part, out, lse, B * L * H_q, 0, bm,

@@ -90,7 +90,8 @@ hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
                            const int32_t* seq_lens, const int32_t* block_table,
                            int max_pages, int page_shift, int num_pages, int B,
                            int L, int H, int T_cap, int d_c, int S, int chunk,
-                           int head_chunks, float scale_log2, hipStream_t stream);
+                           int head_chunks, int balanced, int cap, int* meta,
+                           float scale_log2, hipStream_t stream);
 
 }  // namespace attn
 
@@ -109,7 +110,7 @@ hipError_t launch_combine(const float* o_part, const float* lse_part,
 // (b * L + token) * H_q + head, for heads_per_item columns per item and
 // head_chunks items per KV head; rows whose sequence has one piece per unit
 // are left as the decode kernel wrote them.  o_part and out 16-byte aligned,
-// d_v in {64, 128, 256}.
+// d_v in {64, 128, 256, 512}.
 hipError_t launch_combine_balanced(const float* o_part, const float* lse_part,
                                    const int* meta, float* out, float* lse, int B,
                                    int L, int H_q, int n, int head_chunks,

@@ -21,8 +21,20 @@ int check_mla(int B, int H, int T_cap, int d_c, int d_rope) {
 
 struct MlaPlan {
   int head_chunks, S, chunk;
-  size_t ws_bytes;
+  size_t ws_bytes;  // the larger of the two workspaces below
+  size_t ws_fixed;  // fixed splits
+  int cap;          // > 0: groups of the balanced list (calls with lengths)
 };
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Balanced list over `cap` groups of hg columns: o_part, lse_part and the
+// per-sequence (first item, pieces) pairs.
+size_t mla_balanced_bytes(int cap, int hg, int d_c, int B) {
+  const size_t rows = (size_t)cap * hg;
+  return round_up(rows * d_c * sizeof(float), 256) + round_up(rows * sizeof(float), 256) +
+         round_up((size_t)B * 2 * sizeof(int), 256);
+}
 
 int plan_mla(int B, int H, int T_cap, int d_c, int d_rope, int num_splits,
              MlaPlan* p) {
@@ -52,11 +64,20 @@ int plan_mla(int B, int H, int T_cap, int d_c, int d_rope, int num_splits,
   p->chunk = (int)((T_cap + S - 1) / S);
   p->chunk = (p->chunk + tr - 1) / tr * tr;
   p->S = (T_cap + p->chunk - 1) / p->chunk;
-  p->ws_bytes = attn_decode_workspace_bytes(B, H, d_c, p->S);
+  p->ws_fixed = attn_decode_workspace_bytes(B, H, d_c, p->S);
+  p->ws_bytes = p->ws_fixed;
+  // balanced list: when the fixed plan splits, a call with lengths cuts each
+  // sequence by its own length into pieces of one common size (balance.h)
+  p->cap = 0;
+  const int cap = attn::kNumCUs * attn::mla_groups_per_cu(d_c);
+  if (num_splits == 0 && p->S > 1 && B >= 1 && B <= attn::kBalanceMaxB &&
+      (long long)B * p->head_chunks < cap && cap <= ATTN_MAX_SPLITS) {
+    p->cap = cap;
+    const size_t bb = mla_balanced_bytes(cap, hg, d_c, B);
+    if (bb > p->ws_bytes) p->ws_bytes = bb;
+  }
   return ATTN_OK;
 }
-
-inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
@@ -99,8 +120,18 @@ int decode_mla(const void* q, const void* latent, float* out, float* lse_out,
     return ATTN_ERR_ALIGN;
   float* o_part = nullptr;
   float* lse_part = nullptr;
-  if (p.S > 1) {
-    if (!workspace || workspace_bytes < p.ws_bytes) return ATTN_ERR_WORKSPACE;
+  int* meta = nullptr;
+  const int hg = attn::mla_heads_per_group(d_c);
+  // balanced list: lengths given and room for its parts; else fixed splits
+  const bool bal = p.cap > 0 && seq_lens && workspace && aligned(workspace, 16) &&
+                   workspace_bytes >= mla_balanced_bytes(p.cap, hg, d_c, B);
+  if (bal) {
+    const size_t rows = (size_t)p.cap * hg;
+    o_part = (float*)workspace;
+    lse_part = (float*)((char*)workspace + round_up(rows * d_c * sizeof(float), 256));
+    meta = (int*)((char*)lse_part + round_up(rows * sizeof(float), 256));
+  } else if (p.S > 1) {
+    if (!workspace || workspace_bytes < p.ws_fixed) return ATTN_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
     const size_t rows = (size_t)B * L * H * p.S;
     o_part = (float*)workspace;
@@ -110,12 +141,19 @@ int decode_mla(const void* q, const void* latent, float* out, float* lse_out,
   hipStream_t s = (hipStream_t)stream;
   if (attn::launch_mla_mfma(q, latent, out, lse_out, o_part, lse_part, seq_lens,
                             block_table, max_pages, page_shift, num_pages, B, L, H,
-                            T_cap, d_c, p.S, p.chunk, p.head_chunks,
-                            scale * 1.4426950408889634f, s) != hipSuccess)
+                            T_cap, d_c, p.S, p.chunk, p.head_chunks, bal ? 1 : 0,
+                            bal ? p.cap : 0, meta, scale * 1.4426950408889634f,
+                            s) != hipSuccess)
     return ATTN_ERR_HIP;
-  if (p.S > 1 && attn::launch_combine(o_part, lse_part, out, lse_out, B, H * L,
-                                      p.S, d_c, s) != hipSuccess)
+  if (bal) {
+    // columns are (head, token) pairs of one latent: n = H heads share it
+    if (attn::launch_combine_balanced(o_part, lse_part, meta, out, lse_out, B, L, H, H,
+                                      p.head_chunks, hg, d_c, s) != hipSuccess)
+      return ATTN_ERR_HIP;
+  } else if (p.S > 1 && attn::launch_combine(o_part, lse_part, out, lse_out, B, H * L,
+                                             p.S, d_c, s) != hipSuccess) {
     return ATTN_ERR_HIP;
+  }
   return ATTN_OK;
 }
 

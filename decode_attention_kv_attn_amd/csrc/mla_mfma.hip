@@ -28,6 +28,7 @@
 
 #include <type_traits>
 
+#include "balance.h"
 #include "device_common.h"
 #include "internal.h"
 #include "visible.h"
@@ -176,11 +177,17 @@ struct MlaArgs {
   int L;     // query tokens per sequence (the last L positions)
   int ncol;  // (head, token) columns: H * L
   float scale_log2;
+  // Balanced work list (balance.h): group w is item w of the list by
+  // visible length; a sequence cut into several pieces leaves partial rows
+  // w * kHG + column and meta[2b], meta[2b + 1] = (first item, pieces).
+  int balanced, cap, B;
+  int* meta;
 };
 
 // MULTI: several query tokens per sequence (per-column causal limits); a
-// separate instantiation so the single-token path carries none of it.
-template <class G, int MODE, bool MULTI>
+// separate instantiation so the single-token path carries none of it.  BAL:
+// the balanced work list, likewise.
+template <class G, int MODE, bool MULTI, bool BAL>
 __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(MlaArgs a) {
   constexpr int kDK = G::kDK, kDV = G::kDV, kNW = G::kNW, kHW = G::kHW, kHB = G::kHB;
   constexpr int kHG = G::kHG, kRowBytes = G::kRowBytes, kCPR = G::kCPR;
@@ -197,15 +204,38 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
   const int li = lane & 15;
   const int lg = lane >> 4;
 
-  int bid = blockIdx.x;
-  const int hc = bid % a.head_chunks;
-  bid /= a.head_chunks;
-  const int s = bid % a.S;
-  const int b = bid / a.S;
+  const int item = blockIdx.x;
+  int hc, s, b, n_split = a.S, chunk = a.chunk, len_b = 0;
+  if constexpr (BAL) {
+    // item r of sequence b: s * head_chunks + hc; pieces are whole tiles
+    const WorkItem wi = balanced_item(a.seq_lens, nullptr, a.B, a.T_cap, 0, nullptr, 0,
+                                      a.head_chunks, a.cap, kTT, 2 * kTT, item);
+    if (!wi.valid) return;  // uniform over the work group
+    // uniform values, kept in scalar registers (the tile loads' descriptors
+    // are built from them)
+    b = __builtin_amdgcn_readfirstlane(wi.b);
+    len_b = __builtin_amdgcn_readfirstlane(wi.len);
+    n_split = __builtin_amdgcn_readfirstlane(wi.k);
+    chunk = __builtin_amdgcn_readfirstlane(wi.chunk);
+    const int r = __builtin_amdgcn_readfirstlane(wi.r);
+    hc = r % a.head_chunks;
+    s = r / a.head_chunks;
+    if (wi.r == 0 && threadIdx.x == 0) {
+      a.meta[2 * b] = wi.first;
+      a.meta[2 * b + 1] = wi.k;
+    }
+  } else {
+    int bid = item;
+    hc = bid % a.head_chunks;
+    bid /= a.head_chunks;
+    s = bid % a.S;
+    b = bid / a.S;
+  }
 
-  const VisibleRange vr = visible_range(a.seq_lens, nullptr, b, a.T_cap, 0);
+  const VisibleRange vr = BAL ? visible_range_of(len_b, false, 0, a.T_cap, 0)
+                              : visible_range(a.seq_lens, nullptr, b, a.T_cap, 0);
   int p0, p1;
-  split_range(vr, s, a.S, a.chunk, p0, p1);  // no window: rows = positions
+  split_range(vr, s, n_split, chunk, p0, p1);  // no window: rows = positions
   const int hw0 = hc * kHG + wave * kHW;  // first head of this wave
   const int span = p1 - p0;
   const int ntiles = span > 0 ? (span + kTT - 1) / kTT : 0;
@@ -542,15 +572,16 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
     const float inv = empty ? 0.f : 1.f / l[hb];
     const float lse = empty ? neg_inf() : (m[hb] + fast_log2(l[hb])) * kLn2;
     const size_t row = query_row(b, 0, c, a.H, a.L, a.H);
-    float* dst = (a.S == 1) ? a.out + row * kDV : a.o_part + (row * a.S + s) * kDV;
+    const size_t prow = BAL ? (size_t)item * kHG + (c - hc * kHG) : row * a.S + s;
+    float* dst = (n_split == 1) ? a.out + row * kDV : a.o_part + prow * kDV;
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
       *(f32x4_t*)(dst + 16 * db + 4 * lg) = o[db][hb] * inv;
     if (lg == 0) {
-      if (a.S == 1) {
+      if (n_split == 1) {
         if (a.lse) a.lse[row] = lse;
       } else {
-        a.lse_part[row * a.S + s] = lse;
+        a.lse_part[prow] = lse;
       }
     }
   }
@@ -565,16 +596,25 @@ int mla_groups_per_cu(int d_c) {
 int mla_tile_rows() { return kTT; }
 
 namespace {
-template <class G>
-void launch_geo(const MlaArgs& a, dim3 g, bool paged, hipStream_t stream) {
+template <class G, bool BAL>
+void launch_bal(const MlaArgs& a, dim3 g, bool paged, hipStream_t stream) {
   const dim3 blk(G::kNW * 64);
   if (paged) {
-    if (a.L > 1) hipLaunchKernelGGL((mla_decode_mfma<G, kAddrPaged, true>), g, blk, 0, stream, a);
-    else hipLaunchKernelGGL((mla_decode_mfma<G, kAddrPaged, false>), g, blk, 0, stream, a);
+    if (a.L > 1)
+      hipLaunchKernelGGL((mla_decode_mfma<G, kAddrPaged, true, BAL>), g, blk, 0, stream, a);
+    else
+      hipLaunchKernelGGL((mla_decode_mfma<G, kAddrPaged, false, BAL>), g, blk, 0, stream, a);
   } else {
-    if (a.L > 1) hipLaunchKernelGGL((mla_decode_mfma<G, kAddrDense, true>), g, blk, 0, stream, a);
-    else hipLaunchKernelGGL((mla_decode_mfma<G, kAddrDense, false>), g, blk, 0, stream, a);
+    if (a.L > 1)
+      hipLaunchKernelGGL((mla_decode_mfma<G, kAddrDense, true, BAL>), g, blk, 0, stream, a);
+    else
+      hipLaunchKernelGGL((mla_decode_mfma<G, kAddrDense, false, BAL>), g, blk, 0, stream, a);
   }
+}
+template <class G>
+void launch_geo(const MlaArgs& a, dim3 g, bool paged, hipStream_t stream) {
+  if (a.balanced) launch_bal<G, true>(a, g, paged, stream);
+  else launch_bal<G, false>(a, g, paged, stream);
 }
 }  // namespace
 
@@ -583,7 +623,8 @@ hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
                            const int32_t* seq_lens, const int32_t* block_table,
                            int max_pages, int page_shift, int num_pages, int B,
                            int L, int H, int T_cap, int d_c, int S, int chunk,
-                           int head_chunks, float scale_log2, hipStream_t stream) {
+                           int head_chunks, int balanced, int cap, int* meta,
+                           float scale_log2, hipStream_t stream) {
   MlaArgs a;
   a.q = (const uint16_t*)q;
   a.latent = (const uint16_t*)latent;
@@ -604,7 +645,11 @@ hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
   a.chunk = chunk;
   a.head_chunks = head_chunks;
   a.scale_log2 = scale_log2;
-  const dim3 g((unsigned)((long long)B * S * head_chunks));
+  a.balanced = balanced;
+  a.cap = cap;
+  a.B = B;
+  a.meta = meta;
+  const dim3 g((unsigned)(balanced ? (long long)cap : (long long)B * S * head_chunks));
   if (d_c == 512) launch_geo<GeoWide>(a, g, block_table != nullptr, stream);
   else launch_geo<GeoNarrow>(a, g, block_table != nullptr, stream);
   return hipGetLastError();

@@ -298,3 +298,51 @@ def test_graph_replays_follow_new_lengths():
         ro, rl = oracle.gqa_decode_ref(q, k, v, sl)
         assert_parity(out, ro, f"replay {trial}")
         assert_lse(lse, rl, f"replay {trial}")
+
+
+# ------------------------------------------------------------ absorbed MLA
+MLA_GEOMS = [(512, 128), (256, 32)]  # (d_c, heads); d_rope = 64
+
+
+@pytest.mark.parametrize("d_c,H", MLA_GEOMS, ids=[f"dc{a}-H{b}" for a, b in MLA_GEOMS])
+@pytest.mark.parametrize("mix", ["extreme", "one_long", "all_empty", "all_one_piece"])
+def test_mla_length_mixes(d_c, H, mix):
+    """The MLA kernel takes the same list (pieces of whole 32-row tiles);
+    against the oracle and against the fixed splits."""
+    lens = MIXES[mix]
+    B, T, dk = len(lens), 2048, d_c + 64
+    q = synth.draw((B, H, dk), 13000 + d_c + len(mix), "bf16", DEV, dk ** -0.5)
+    lat = synth.draw((B, T, dk), 13001 + d_c + len(mix), "bf16", DEV, dk ** -0.5)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    scale = 192 ** -0.5
+    z, lse = L.attn_decode_mla(q, lat, d_c, scale, sl)
+    torch.cuda.synchronize()
+    rz, rl = oracle.mla_decode_ref(q, lat, d_c, scale, sl)
+    assert_parity(z, rz, f"mla balanced {mix} d_c={d_c}")
+    assert_lse(lse, rl, f"mla balanced {mix}")
+    S = L.attn_decode_mla_splits(B, H, T, d_c, 64)
+    assert S > 1
+    zf, _ = L.attn_decode_mla(q, lat, d_c, scale, sl, S)
+    torch.cuda.synchronize()
+    assert_parity(zf, rz, f"mla fixed {mix}")
+
+
+def test_mla_paged_and_multi_token():
+    """Paged latent pool (16-position pages): the same bits as the dense
+    cache; three query tokens per sequence (three head chunks at 128 heads)
+    against the oracle."""
+    from test_gpu_paged import _latent_pool
+    lens = [2048, 1, 0, 1500, 17, 385, 2047, 640]
+    B, T, H = len(lens), 2048, 128
+    q = synth.draw((B, 3, H, 576), 13100, "bf16", DEV, 576 ** -0.5)
+    lat = synth.draw((B, T, 576), 13101, "bf16", DEV, 576 ** -0.5)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    scale = 192 ** -0.5
+    pool, table = _latent_pool(lat, 16, 13102, poison=True)
+    zp, lp = L.attn_decode_mla_paged(q, pool, table, 512, scale, sl)
+    zd, ld = L.attn_decode_mla_multi(q, lat, 512, scale, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(zp, zd) and torch.equal(lp, ld)
+    rz, rl = oracle.mla_decode_multi_ref(q, lat, 512, scale, sl)
+    assert_parity(zd, rz, "mla balanced multi")
+    assert_lse(ld, rl, "mla balanced multi")
