@@ -63,6 +63,12 @@ WORKLOADS = {
                           d_c=512, d_rope=64, dtype="bf16",
                           scale=1.0 / math.sqrt(192),
                           value_scale=1.0 / math.sqrt(576)),
+    # the same with lengths uniform on 1024..8192 (the ragged variant)
+    "mla_b64_t8192_ragged": dict(kind="mla", index=4, B=64, H=128, T_cap=8192,
+                                 d_c=512, d_rope=64, dtype="bf16",
+                                 scale=1.0 / math.sqrt(192),
+                                 value_scale=1.0 / math.sqrt(576),
+                                 ragged=(1024, 8192)),
     # second latent geometry: 32 query heads, latent 256 + RoPE 64
     "mla256_b64_t8192": dict(kind="mla", index=5, B=64, H=32, T_cap=8192,
                              d_c=256, d_rope=64, dtype="bf16",

@@ -110,10 +110,13 @@ def test_poison_past_length():
     assert_lse(lse, rl, "poison")
 
 
-def test_full_size_sampled():
+@pytest.mark.parametrize("name", ["mla_b64_t8192", "mla_b64_t8192_ragged"])
+def test_full_size_sampled(name):
     """B=64, 128 heads, latent [64, 8192, 576], N(0,1)/sqrt(576), scale
-    1/sqrt(192), library-chosen splits; sampled sequences against the oracle."""
-    w = synth.workload("mla_b64_t8192")
+    1/sqrt(192), in its default launch configuration (uniform lengths: fixed
+    splits; lengths on 1024..8192: the balanced list); sampled sequences
+    against the oracle."""
+    w = synth.workload(name)
     inp = synth.mla_inputs(w, DEV)
     z, lse = L.attn_decode_mla(inp["q"], inp["latent"], inp["d_c"], inp["scale"],
                                inp["seq_lens"])
