@@ -54,7 +54,8 @@ def parse():
                          "--pmc FETCH_SIZE / WRITE_SIZE runs of this workload "
                          "(PMC_DIR/{FETCH_SIZE,WRITE_SIZE}/run_counter_collection.csv) "
                          "and of the --probe copy (--copy-dir)")
-    ap.add_argument("--copy-dir", default="gpurun_out/pmc/copy")
+    ap.add_argument("--copy-dir", metavar="PMC_DIR",
+                    help="the --pmc runs of `bench.py --probe` (the 1 GiB plain copy)")
     ap.add_argument("--probe", action="store_true",
                     help="only run the HBM read probe and a 1 GiB plain copy")
     return ap.parse_args()
@@ -206,6 +207,8 @@ def record_traffic(args):
     kind = "mla" if w["kind"] == "mla" else "gqa"
     kern = "mla_decode_mfma" if kind == "mla" else "gqa_decode_"
     d = args.record_traffic
+    if not args.copy_dir:
+        sys.exit("--record-traffic needs --copy-dir: the --pmc runs of the plain copy")
     fk, _, nf = _counter_kib_per_dispatch(os.path.join(d, "FETCH_SIZE", "run_counter_collection.csv"), kern)
     wk, _, nw = _counter_kib_per_dispatch(os.path.join(d, "WRITE_SIZE", "run_counter_collection.csv"), kern)
     cf, _, _ = _counter_kib_per_dispatch(os.path.join(args.copy_dir, "FETCH_SIZE", "run_counter_collection.csv"), "plain_copy")
