@@ -258,7 +258,7 @@ def test_large_scores_stay_finite():
 # ------------------------------------------------ full-size workloads, sampled
 FULL = ["llama3_8b_gqa_t4096", "mha_t32k_b1", "mqa_t32k_b1",
         "swa_ring_w4096_t32k", "wide_d256_t128k", "mqa_t32k_b64_ragged",
-        "mha_t32k_b64_ragged", "mha_t32k_b64"]
+        "mha_t32k_b64_ragged", "mha_t32k_b64", "mqa_t32k_b64"]
 
 
 @pytest.mark.parametrize("name", FULL)
