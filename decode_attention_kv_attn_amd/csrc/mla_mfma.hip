@@ -463,9 +463,12 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
       float p[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        // m is finite once any row of this head was visible; masked rows
-        // (only in a partial tile) get weight 0
-        p[j] = ((!full || multi) && x[j] == neg_inf())
+        // One token: every computed tile has a visible row (the split's
+        // rows start at its first tile), so m is finite here and a masked
+        // row's -inf gives exp2(-inf) = 0 without a test.  Several tokens:
+        // a column may have seen no visible row yet (m = -inf), and
+        // -inf - (-inf) would be NaN, so masked rows are set to 0.
+        p[j] = (multi && x[j] == neg_inf())
                    ? 0.f
                    : fast_exp2(fmaf(x[j], a.scale_log2, -m[hb]));
         l[hb] += p[j];
