@@ -34,8 +34,9 @@ METRIC = "decode-attention KV-read GB/s (% of HBM peak) and µs/step per layer"
 DEFAULT_WORKLOAD = "llama3_8b_gqa_t4096"
 SETTLE_S = 0.3  # seconds of untimed calls before the warmup (clock ramp-up)
 KERNEL_SOURCES = {"gqa": ["gqa_valu.hip", "gqa_mfma.hip", "balance.h", "visible.h",
-                          "device_common.h"],
-                  "mla": ["mla_mfma.hip", "balance.h", "visible.h", "device_common.h"]}
+                          "device_common.h", "internal.h"],
+                  "mla": ["mla_mfma.hip", "balance.h", "visible.h", "device_common.h",
+                          "internal.h"]}
 
 
 def parse():
