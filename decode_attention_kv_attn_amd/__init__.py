@@ -127,6 +127,47 @@ def _need_dev(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _dims(t, name, n):
+    """t.shape, checked to have n dimensions (n an int or a tuple of ints)."""
+    ok = (n,) if isinstance(n, int) else n
+    if t.dim() not in ok:
+        raise ValueError(f"{name} must have {' or '.join(map(str, ok))} dimensions, "
+                         f"got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _expect(t, name, shape=None, dtype=None, min_rows=None):
+    """Shape / dtype check of an optional tensor argument (None passes)."""
+    if t is None:
+        return
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if min_rows is not None and (t.dim() != 2 or t.shape[0] < min_rows):
+        raise ValueError(f"{name} must be 2-D with at least {min_rows} rows, "
+                         f"got shape {tuple(t.shape)}")
+
+
+def _same_dtype(ref, *named):
+    for name, t in named:
+        if t is not None and t.dtype != ref.dtype:
+            raise ValueError(f"{name} must have the dtype of q ({ref.dtype}), got {t.dtype}")
+
+
+def _on_device(ref, *ts):
+    """Every tensor on the GPU, contiguous, on ref's device (checked after
+    the shapes, so the shape checks run without a GPU)."""
+    _need_dev(ref, *ts)
+    for t in ts:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"tensors must share one device: {t.device} vs {ref.device}")
+
+
+_I32 = torch.int32
+_F32 = torch.float32
+
+
 def attn_decode_gqa_splits(B, H_q, H_kv, T_cap, d, dtype, window=0, ring=False,
                            num_splits=0):
     return library().attn_decode_gqa_splits(B, H_q, H_kv, T_cap, d, dtype,
@@ -180,6 +221,26 @@ def _workspace(nbytes, device, workspace):
     return workspace
 
 
+def _gqa_shapes(q, k, v, out, lse, seq_lens, ring_head, q_dims=3):
+    """B, L, H_q, d, H_kv, T_cap of a GQA call, after checking every tensor's
+    shape and dtype against them: q [B, H_q, d] (or [B, L, H_q, d]), k and v
+    [B, H_kv, T_cap, d] of q's dtype, out / lse float32 shaped like q,
+    seq_lens / ring_head int32 [B]."""
+    shp = _dims(q, "q", q_dims)
+    B, H_q, d = shp[0], shp[-2], shp[-1]
+    L = shp[1] if len(shp) == 4 else 1
+    _dtype_code(q)
+    _, H_kv, T_cap, dk = _dims(k, "k", 4)
+    _expect(k, "k", (B, H_kv, T_cap, d))
+    _expect(v, "v", tuple(k.shape))
+    _same_dtype(q, ("k", k), ("v", v))
+    _expect(out, "out", shp, _F32)
+    _expect(lse, "lse", shp[:-1], _F32)
+    _expect(seq_lens, "seq_lens", (B,), _I32)
+    _expect(ring_head, "ring_head", (B,), _I32)
+    return B, L, H_q, d, H_kv, T_cap
+
+
 def attn_decode_gqa(q, k, v, seq_lens=None, ring_head=None, window=0,
                     scale=None, num_splits=0, out=None, lse=None,
                     workspace=None, want_lse=True, stream=None):
@@ -189,9 +250,8 @@ def attn_decode_gqa(q, k, v, seq_lens=None, ring_head=None, window=0,
     seq_lens / ring_head int32 [B] or None.  Returns ``(out, lse)`` float32
     tensors ([B, H_q, d], [B, H_q] or None).  See include/attn_decode.h.
     """
-    _need_dev(q, k, v, seq_lens, ring_head, out, lse)
-    B, H_q, d = q.shape
-    _, H_kv, T_cap, _ = k.shape
+    B, _, H_q, d, H_kv, T_cap = _gqa_shapes(q, k, v, out, lse, seq_lens, ring_head)
+    _on_device(q, k, v, seq_lens, ring_head, out, lse, workspace)
     dt = _dtype_code(q)
     if out is None:
         out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
@@ -233,9 +293,11 @@ def attn_decode_gqa_global(q, k, v, global_pos, window, seq_lens=None,
     ``global_pos``: sorted int32 [n_global] device tensor (or None for none);
     other arguments as for :func:`attn_decode_gqa` without ``ring_head``.
     """
-    _need_dev(q, k, v, seq_lens, global_pos, out, lse)
-    B, H_q, d = q.shape
-    _, H_kv, T_cap, _ = k.shape
+    B, _, H_q, d, H_kv, T_cap = _gqa_shapes(q, k, v, out, lse, seq_lens, None)
+    if global_pos is not None:
+        _dims(global_pos, "global_pos", 1)
+        _expect(global_pos, "global_pos", dtype=_I32)
+    _on_device(q, k, v, seq_lens, global_pos, out, lse, workspace)
     dt = _dtype_code(q)
     n_global = 0 if global_pos is None else global_pos.numel()
     if out is None:
@@ -266,14 +328,35 @@ def attn_decode_mla_workspace_bytes(B, H, T_cap, d_c, d_rope, num_splits=0):
                                                      num_splits)
 
 
+def _mla_shapes(q, latent, d_c, out, lse, seq_lens, q_dims=3, paged=False):
+    """B, L, H, dk of an MLA call after checking q [B, H, dk] (or [B, L, H,
+    dk]) and the latent (or its page pool) bfloat16 with rows of dk, out /
+    lse float32 shaped like q with d_c values, seq_lens int32 [B]."""
+    shp = _dims(q, "q", q_dims)
+    B, H, dk = shp[0], shp[-2], shp[-1]
+    L = shp[1] if len(shp) == 4 else 1
+    _expect(q, "q", dtype=torch.bfloat16)
+    lshp = _dims(latent, "latent_pages" if paged else "latent", 3)
+    if lshp[2] != dk or (not paged and lshp[0] != B):
+        raise ValueError(f"latent rows must be [{'num_pages, P' if paged else f'{B}, T_cap'}, {dk}], "
+                         f"got shape {lshp}")
+    _expect(latent, "latent", dtype=torch.bfloat16)
+    if not 0 < d_c < dk:
+        raise ValueError(f"d_c must be in (0, {dk}), got {d_c}")
+    _expect(out, "out", shp[:-1] + (d_c,), _F32)
+    _expect(lse, "lse", shp[:-1], _F32)
+    _expect(seq_lens, "seq_lens", (B,), _I32)
+    return B, L, H, dk
+
+
 def attn_decode_mla(q, latent, d_c, scale, seq_lens=None, num_splits=0,
                     out=None, lse=None, workspace=None, want_lse=True,
                     stream=None):
     """Absorbed MLA decode: q [B, H, d_c+d_rope], latent [B, T_cap, d_c+d_rope]
     (bfloat16).  Returns ``(z [B, H, d_c], lse [B, H])`` float32."""
-    _need_dev(q, latent, seq_lens, out, lse)
-    B, H, dk = q.shape
-    _, T_cap, _ = latent.shape
+    B, _, H, dk = _mla_shapes(q, latent, d_c, out, lse, seq_lens)
+    _on_device(q, latent, seq_lens, out, lse, workspace)
+    T_cap = latent.shape[1]
     d_rope = dk - d_c
     if out is None:
         out = torch.empty((B, H, d_c), dtype=torch.float32, device=q.device)
@@ -295,8 +378,12 @@ def attn_decode_mla(q, latent, d_c, scale, seq_lens=None, num_splits=0,
 def attn_combine(o_part, lse_part, out=None, lse=None, want_lse=True,
                  stream=None):
     """Merge split results: o_part [B, H, S, d_v], lse_part [B, H, S]."""
-    _need_dev(o_part, lse_part, out, lse)
-    B, H, S, d_v = o_part.shape
+    B, H, S, d_v = _dims(o_part, "o_part", 4)
+    _expect(o_part, "o_part", dtype=_F32)
+    _expect(lse_part, "lse_part", (B, H, S), _F32)
+    _expect(out, "out", (B, H, d_v), _F32)
+    _expect(lse, "lse", (B, H), _F32)
+    _on_device(o_part, lse_part, out, lse)
     if out is None:
         out = torch.empty((B, H, d_v), dtype=torch.float32, device=o_part.device)
     if lse is None and want_lse:
@@ -318,11 +405,26 @@ def _cache_dims(cache):
     return B, H, T_cap, d
 
 
+def _append_shapes(k_cache, k_new, v_cache, v_new, B, H, d, index, index_name):
+    """New rows [B, H, d] ([B, d] for a three-dimensional cache) of the
+    cache's dtype, v given with both or neither of its tensors and shaped
+    like k, the index tensor int32 [B]."""
+    _dtype_code(k_cache)
+    row = (B, H, d) if k_cache.dim() == 4 else (B, d)
+    _expect(k_new, "k_new", row, k_cache.dtype)
+    if (v_cache is None) != (v_new is None):
+        raise ValueError("v_cache and v_new go together (both or neither)")
+    _expect(v_cache, "v_cache", tuple(k_cache.shape), k_cache.dtype)
+    _expect(v_new, "v_new", row, k_cache.dtype)
+    _expect(index, index_name, (B,), _I32)
+
+
 def attn_kv_append(k_cache, k_new, positions, v_cache=None, v_new=None,
                    stream=None):
     """Write k_new (and v_new) [B, H, d] at row positions[b] of the cache."""
-    _need_dev(k_cache, k_new, positions, v_cache, v_new)
     B, H, T_cap, d = _cache_dims(k_cache)
+    _append_shapes(k_cache, k_new, v_cache, v_new, B, H, d, positions, "positions")
+    _on_device(k_cache, k_new, positions, v_cache, v_new)
     st = library().attn_kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(k_new),
                                   _ptr(v_new), _ptr(positions), B, H, T_cap, d,
                                   _dtype_code(k_cache), _stream(stream, k_cache.device))
@@ -332,8 +434,9 @@ def attn_kv_append(k_cache, k_new, positions, v_cache=None, v_new=None,
 def attn_kv_append_ring(k_cache, k_new, ring_head, v_cache=None, v_new=None,
                         stream=None):
     """Advance ring_head[b] (in place) and write the rows at the new slot."""
-    _need_dev(k_cache, k_new, ring_head, v_cache, v_new)
     B, H, T_cap, d = _cache_dims(k_cache)
+    _append_shapes(k_cache, k_new, v_cache, v_new, B, H, d, ring_head, "ring_head")
+    _on_device(k_cache, k_new, ring_head, v_cache, v_new)
     st = library().attn_kv_append_ring(_ptr(k_cache), _ptr(v_cache), _ptr(k_new),
                                        _ptr(v_new), _ptr(ring_head), B, H, T_cap, d,
                                        _dtype_code(k_cache),
@@ -356,11 +459,20 @@ def attn_decode_gqa_paged(q, k_pages, v_pages, block_table, seq_lens=None,
     d], block_table int32 [B, max_pages]; q [B, H_q, d] (one token) or
     [B, L, H_q, d] (L tokens per sequence).  Returns ``(out, lse)`` shaped
     like q (float32) and q without its last dim."""
-    _need_dev(q, k_pages, v_pages, block_table, seq_lens, out, lse)
-    lead = q.shape[:-2]
-    B, L = (q.shape[0], 1) if q.dim() == 3 else (q.shape[0], q.shape[1])
-    H_q, d = q.shape[-2], q.shape[-1]
-    num_pages, H_kv, P, _ = k_pages.shape
+    shp = _dims(q, "q", (3, 4))
+    B, H_q, d = shp[0], shp[-2], shp[-1]
+    L = shp[1] if len(shp) == 4 else 1
+    lead = shp[:-2]
+    _dtype_code(q)
+    num_pages, H_kv, P, _ = _dims(k_pages, "k_pages", 4)
+    _expect(k_pages, "k_pages", (num_pages, H_kv, P, d))
+    _expect(v_pages, "v_pages", tuple(k_pages.shape))
+    _same_dtype(q, ("k_pages", k_pages), ("v_pages", v_pages))
+    _expect(block_table, "block_table", dtype=_I32, min_rows=B)
+    _expect(out, "out", shp, _F32)
+    _expect(lse, "lse", shp[:-1], _F32)
+    _expect(seq_lens, "seq_lens", (B,), _I32)
+    _on_device(q, k_pages, v_pages, block_table, seq_lens, out, lse, workspace)
     max_pages = block_table.shape[1]
     dt = _dtype_code(q)
     if out is None:
@@ -386,9 +498,9 @@ def attn_decode_gqa_multi(q, k, v, seq_lens=None, ring_head=None, window=0,
     """L query tokens per sequence: q [B, L, H_q, d] (the last L positions of
     each cache), k / v [B, H_kv, T_cap, d].  Returns ``(out [B, L, H_q, d],
     lse [B, L, H_q])`` float32."""
-    _need_dev(q, k, v, seq_lens, ring_head, out, lse)
-    B, L, H_q, d = q.shape
-    _, H_kv, T_cap, _ = k.shape
+    B, L, H_q, d, H_kv, T_cap = _gqa_shapes(q, k, v, out, lse, seq_lens, ring_head,
+                                            q_dims=4)
+    _on_device(q, k, v, seq_lens, ring_head, out, lse, workspace)
     dt = _dtype_code(q)
     if out is None:
         out = torch.empty((B, L, H_q, d), dtype=torch.float32, device=q.device)
@@ -413,10 +525,11 @@ def attn_decode_mla_paged(q, latent_pages, block_table, d_c, scale,
     """Absorbed MLA over a paged latent pool [num_pages, P, d_c+d_rope]
     (bfloat16) with block_table int32 [B, max_pages]; q [B, H, d_c+d_rope]
     or [B, L, H, d_c+d_rope] (L tokens per sequence)."""
-    _need_dev(q, latent_pages, block_table, seq_lens, out, lse)
-    lead = q.shape[:-2]
-    B, L = (q.shape[0], 1) if q.dim() == 3 else (q.shape[0], q.shape[1])
-    H, dk = q.shape[-2], q.shape[-1]
+    B, L, H, dk = _mla_shapes(q, latent_pages, d_c, out, lse, seq_lens, (3, 4),
+                              paged=True)
+    _expect(block_table, "block_table", dtype=_I32, min_rows=B)
+    _on_device(q, latent_pages, block_table, seq_lens, out, lse, workspace)
+    lead = tuple(q.shape[:-2])
     num_pages, P, _ = latent_pages.shape
     max_pages = block_table.shape[1]
     d_rope = dk - d_c
@@ -445,9 +558,9 @@ def attn_decode_mla_multi(q, latent, d_c, scale, seq_lens=None, num_splits=0,
     """Absorbed MLA with L query tokens per sequence: q [B, L, H,
     d_c+d_rope], latent [B, T_cap, d_c+d_rope] (bfloat16).  Returns
     ``(z [B, L, H, d_c], lse [B, L, H])`` float32."""
-    _need_dev(q, latent, seq_lens, out, lse)
-    B, L, H, dk = q.shape
-    _, T_cap, _ = latent.shape
+    B, L, H, dk = _mla_shapes(q, latent, d_c, out, lse, seq_lens, 4)
+    _on_device(q, latent, seq_lens, out, lse, workspace)
+    T_cap = latent.shape[1]
     d_rope = dk - d_c
     if out is None:
         out = torch.empty((B, L, H, d_c), dtype=torch.float32, device=q.device)
@@ -471,13 +584,17 @@ def attn_kv_append_paged(k_pages, k_new, positions, block_table, v_pages=None,
     """Write k_new (and v_new) [B, H, d] at position positions[b] of each
     sequence's pages ([num_pages, H, P, d]; a latent pool [num_pages, P, d]
     with [B, d] rows is taken as H = 1)."""
-    _need_dev(k_pages, k_new, positions, block_table, v_pages, v_new)
     if k_pages.dim() == 3:
         num_pages, P, d = k_pages.shape
         H = 1
-    else:
+    elif k_pages.dim() == 4:
         num_pages, H, P, d = k_pages.shape
-    B = positions.shape[0]
+    else:
+        raise ValueError("k_pages must be [num_pages, H, P, d] or [num_pages, P, d]")
+    B = _dims(positions, "positions", 1)[0]
+    _append_shapes(k_pages, k_new, v_pages, v_new, B, H, d, positions, "positions")
+    _expect(block_table, "block_table", dtype=_I32, min_rows=B)
+    _on_device(k_pages, k_new, positions, block_table, v_pages, v_new)
     st = library().attn_kv_append_paged(
         _ptr(k_pages), _ptr(v_pages), _ptr(k_new), _ptr(v_new), _ptr(positions),
         _ptr(block_table), block_table.shape[1], B, H, num_pages, P, d,
@@ -487,6 +604,10 @@ def attn_kv_append_paged(k_pages, k_new, positions, block_table, v_pages=None,
 
 def attn_probe_read(src, sink, blocks=0, stream=None):
     """Stream-read every byte of ``src`` once (HBM read-rate probe)."""
+    _expect(sink, "sink", dtype=_I32)
+    if sink.numel() < 1:
+        raise ValueError("sink must hold at least one int32")
+    _on_device(src, sink)
     st = library().attn_probe_read(_ptr(src), src.numel() * src.element_size(),
                                    _ptr(sink), blocks, _stream(stream, src.device))
     _check("attn_probe_read", st)
@@ -494,6 +615,9 @@ def attn_probe_read(src, sink, blocks=0, stream=None):
 
 def attn_probe_copy(dst, src, stream=None):
     """dst <- src byte for byte (a copy of known size)."""
+    if dst.numel() * dst.element_size() < src.numel() * src.element_size():
+        raise ValueError("dst is smaller than src")
+    _on_device(src, dst)
     st = library().attn_probe_copy(_ptr(dst), _ptr(src),
                                    src.numel() * src.element_size(),
                                    _stream(stream, src.device))

@@ -55,6 +55,12 @@ WORKLOADS = {
     "swa_ring_w4096_t32k": dict(kind="gqa", index=3, B=16, H_q=32, H_kv=8,
                                 d=128, T_cap=4096, dtype="bf16", window=4096,
                                 ring=True, logical_len=32768),
+    # The same window over a linear 32768-row cache: only the last 4096 rows
+    # of each sequence are visible, so a kernel that skips masked rows reads
+    # an eighth of the cache.
+    "swa_linear_w4096_t32k": dict(kind="gqa", index=3, B=16, H_q=32, H_kv=8,
+                                  d=128, T_cap=32768, dtype="bf16",
+                                  window=4096),
     # Wide head (d=256), 24 query heads over 4 KV heads, T=131072.
     "wide_d256_t128k": dict(kind="gqa", index=3, B=4, H_q=24, H_kv=4, d=256,
                             T_cap=131072, dtype="bf16"),

@@ -1,5 +1,7 @@
 """Shared helpers of the GPU parity tests: tolerances and comparisons."""
 
+import os
+
 import numpy as np
 import torch
 
@@ -34,10 +36,65 @@ def assert_parity(got, want, what="", atol=MAX_ABS, rtol_l2=REL_L2):
 
 
 def assert_lse(got, want, what="", atol=2e-3):
-    g = to64(got)
+    g = to64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
     w = np.asarray(want, np.float64)
     assert np.array_equal(np.isneginf(g), np.isneginf(w)), f"{what}: empty-set pattern"
     fin = np.isfinite(w)
     if fin.any():
         err = float(np.max(np.abs(g[fin] - w[fin])))
         assert err <= atol, f"{what}: lse max_abs={err:.3e}"
+
+
+def host_workers():
+    """Host threads for the per-unit oracle: the cores this process may use,
+    at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def map_units(fn, units, workers=None):
+    """fn(u) for every u of `units` on a pool of host threads, each numpy
+    call on one BLAS thread (numpy releases the GIL inside its kernels, and
+    one thread per small product is far faster than many); results in the
+    order of `units`."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        with ThreadPoolExecutor(max_workers=workers or host_workers()) as ex:
+            return list(ex.map(fn, units))
+
+
+def assert_parity_each(got, want, what="", atol=MAX_ABS, rtol_l2=REL_L2):
+    """assert_parity over the whole tensor and over each leading index on its
+    own (one sequence), so an error confined to one sequence cannot hide in
+    the norm of the rest."""
+    got64 = to64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert_parity(got64, want, what, atol, rtol_l2)
+    for b in range(want.shape[0]):
+        assert_parity(got64[b], want[b], f"{what} [{b}]", atol, rtol_l2)
+
+
+def assert_lse_each(got, want, what="", atol=2e-3):
+    g = to64(got)
+    for b in range(g.shape[0]):
+        assert_lse(g[b], np.asarray(want)[b], f"{what} [{b}]", atol)
+
+
+def mla_oracle_every_sequence(inp, w):
+    """The float64 MLA oracle for every sequence of a workload, one sequence
+    per host thread task (each copies its own latent rows from the device)."""
+    import oracle
+    q = inp["q"].cpu()
+    sl = None if inp["seq_lens"] is None else inp["seq_lens"].cpu()
+
+    def seq(b):
+        return oracle.mla_decode_ref(q[b:b + 1], inp["latent"][b:b + 1], inp["d_c"],
+                                     inp["scale"], None if sl is None else sl[b:b + 1])
+
+    res = map_units(seq, list(range(w["B"])))
+    return (np.concatenate([z for z, _ in res]), np.concatenate([l for _, l in res]))

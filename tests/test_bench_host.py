@@ -6,7 +6,8 @@ import re
 import bench
 
 CSRC = os.path.join(bench.ROOT, "decode_attention_kv_attn_amd", "csrc")
-KERNELS = {"gqa": ["gqa_valu.hip", "gqa_mfma.hip"], "mla": ["mla_mfma.hip"]}
+KERNELS = {"gqa": ["gqa_valu.hip", "gqa_mfma.hip", "combine.hip"],
+           "mla": ["mla_mfma.hip", "combine.hip"]}
 
 
 def local_includes(name, seen=None):
@@ -33,10 +34,11 @@ def test_traffic_hash_covers_kernel_sources():
 
 
 def test_traffic_records_are_consistent():
-    """Each committed traffic record is the counters scaled by its own copy
-    calibration, and names the commands and workload it came from.  (Whether
-    it still matches the sources is bench.py's business: it reports null
-    traffic once the hash differs.)"""
+    """Each committed traffic record is the counters of each kernel of a step
+    (decode, and the merge of a split plan) scaled by its own copy
+    calibration, summed per step, and names the commands and workload it came
+    from.  (Whether it still matches the sources is bench.py's business: it
+    reports null traffic once the hash differs.)"""
     import json
     prof = os.path.join(bench.ROOT, "profiles")
     recs = [f for f in sorted(os.listdir(prof))
@@ -49,12 +51,39 @@ def test_traffic_records_are_consistent():
         c = t["copy_calibration"]
         assert abs(c["fetch_scale"] - c["bytes"] / (c["fetch_kib_raw"] * 1024)) < 1e-3
         assert abs(c["write_scale"] - c["bytes"] / (c["write_kib_raw"] * 1024)) < 1e-3
-        rd = t["fetch_kib_per_dispatch_raw"] * 1024 * c["fetch_scale"]
-        wr = t["write_kib_per_dispatch_raw"] * 1024 * c["write_scale"]
-        assert abs(t["read_bytes_per_launch"] - rd) <= 1e-4 * rd + 1024
-        assert abs(t["write_bytes_per_launch"] - wr) <= 1e-4 * wr + 1024
-        assert abs(t["bytes_per_launch"] - t["read_bytes_per_launch"]
-                   - t["write_bytes_per_launch"]) <= 1  # each rounded down on its own
-        # HBM traffic of a decode launch is at least its algorithmic bytes
-        assert t["read_bytes_per_launch"] >= t["algorithmic_bytes_per_launch"]
+        assert any(k.startswith(("gqa_decode_", "mla_decode_")) for k in t["kernels"])
+        rd_sum = wr_sum = 0
+        for k in t["kernels"].values():
+            rd = k["fetch_kib_per_dispatch_raw"] * 1024 * c["fetch_scale"]
+            wr = k["write_kib_per_dispatch_raw"] * 1024 * c["write_scale"]
+            assert abs(k["read_bytes"] - rd) <= 1e-4 * rd + 1024
+            assert abs(k["write_bytes"] - wr) <= 1e-4 * wr + 1024
+            rd_sum += k["read_bytes"]
+            wr_sum += k["write_bytes"]
+        assert t["read_bytes_per_step"] == rd_sum
+        assert t["write_bytes_per_step"] == wr_sum
+        assert t["bytes_per_step"] == rd_sum + wr_sum
+        # HBM traffic of a decode step is at least its algorithmic bytes
+        assert t["read_bytes_per_step"] >= t["algorithmic_bytes_per_step"]
         assert all(f"--workload {w} " in cmd for cmd in t["commands"][:2])
+
+
+def test_algorithmic_bytes_of_the_workloads():
+    """The byte count the bench divides by: the attention-head note's
+    512 MiB per layer for MHA at B=1, T=32768 (section 1), 64 times that at
+    B=64; a window of 4096 over a 32768-row linear cache counts only the
+    window; the MLA latent (section 5.4) counts (512 + 64) * 2 bytes a row."""
+    import synth
+    alg = lambda name: bench.algorithmic_bytes(synth.workload(name))
+    assert alg("mha_t32k_b1") == 512 * 2**20
+    assert alg("mha_t32k_b64") == 64 * 512 * 2**20
+    assert alg("mqa_t32k_b1") == 16 * 2**20
+    assert alg("llama3_8b_gqa_t4096") == 512 * 2**20
+    assert alg("swa_linear_w4096_t32k") == alg("swa_ring_w4096_t32k") == 256 * 2**20
+    assert alg("mla_b64_t8192") == 64 * 8192 * 576 * 2
+
+
+def test_sample_stride_bounds_the_host_copy():
+    assert bench.sample_stride(2048, 16 << 20) == 16      # 128 units of 16 MiB
+    assert bench.sample_stride(256, 4 << 20) == 1         # 1 GiB: all of it
+    assert bench.sample_stride(1, 64 << 30) == 1

@@ -9,7 +9,8 @@ import torch
 import decode_attention_kv_attn_amd as L
 import oracle
 import synth
-from helpers import assert_lse, assert_parity, to64
+from helpers import (assert_lse, assert_lse_each, assert_parity,
+                     assert_parity_each, mla_oracle_every_sequence, to64)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -111,18 +112,16 @@ def test_poison_past_length():
 
 
 @pytest.mark.parametrize("name", ["mla_b64_t8192", "mla_b64_t8192_ragged"])
-def test_full_size_sampled(name):
+def test_full_size_every_output(name):
     """B=64, 128 heads, latent [64, 8192, 576], N(0,1)/sqrt(576), scale
     1/sqrt(192), in its default launch configuration (uniform lengths: fixed
-    splits; lengths on 1024..8192: the balanced list); sampled sequences
-    against the oracle."""
+    splits; lengths on 1024..8192: the balanced list); every sequence against
+    the oracle, one sequence per host thread task."""
     w = synth.workload(name)
     inp = synth.mla_inputs(w, DEV)
     z, lse = L.attn_decode_mla(inp["q"], inp["latent"], inp["d_c"], inp["scale"],
                                inp["seq_lens"])
     torch.cuda.synchronize()
-    for b in (0, 17, 63):
-        rz, rl = oracle.mla_decode_ref(inp["q"], inp["latent"], inp["d_c"],
-                                       inp["scale"], inp["seq_lens"], batches=[b])
-        assert_parity(z[b], rz[b], f"mla b={b}")
-        assert_lse(lse[b], rl[b], f"mla b={b}")
+    rz, rl = mla_oracle_every_sequence(inp, w)
+    assert_parity_each(z, rz, name)
+    assert_lse_each(lse, rl, name)
