@@ -24,10 +24,12 @@ __all__ = [
     "attn_decode_gqa_global_workspace_bytes",
     "attn_decode_gqa_paged", "attn_decode_mla_paged", "attn_kv_append_paged",
     "attn_decode_gqa_plan", "attn_decode_gqa_multi", "attn_decode_mla_multi",
+    "attn_decode_gqa_noalloc", "ATTN_NOALLOC_SCRATCH_BYTES",
 ]
 
 ATTN_F32 = 0
 ATTN_BF16 = 1
+ATTN_NOALLOC_SCRATCH_BYTES = 16 << 20  # attn_decode_gqa_noalloc's device array
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libattn_decode.so")
@@ -37,6 +39,8 @@ _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_
 _SIGS = {
     "attn_decode_gqa": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                              _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "attn_decode_gqa_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                                     _i, _i, _i, _i, _f, _i, _vp]),
     "attn_decode_gqa_global": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
                                     _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz,
                                     _vp]),
@@ -270,6 +274,27 @@ def attn_decode_gqa(q, k, v, seq_lens=None, ring_head=None, window=0,
         0.0 if scale is None else float(scale), num_splits, _ptr(workspace),
         ws_bytes, _stream(stream, q.device))
     _check("attn_decode_gqa", st)
+    return out, lse
+
+
+def attn_decode_gqa_noalloc(q, k, v, out, lse=None, seq_lens=None,
+                            ring_head=None, window=0, scale=None, num_splits=0,
+                            stream=None):
+    """attn_decode_gqa with its split results in the library's per-GPU
+    device array (no workspace, nothing allocated by the call): ``out``
+    [B, H_q, d] float32 and the optional ``lse`` [B, H_q] float32 are
+    supplied by the caller.  Calls that overlap on one GPU race (they share
+    the array)."""
+    if out is None:
+        raise ValueError("out is required: the no-allocation form allocates nothing")
+    B, _, H_q, d, H_kv, T_cap = _gqa_shapes(q, k, v, out, lse, seq_lens, ring_head)
+    _on_device(q, k, v, seq_lens, ring_head, out, lse)
+    st = library().attn_decode_gqa_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(seq_lens),
+        _ptr(ring_head), B, H_q, H_kv, T_cap, d, _dtype_code(q), window,
+        0.0 if scale is None else float(scale), num_splits,
+        _stream(stream, q.device))
+    _check("attn_decode_gqa_noalloc", st)
     return out, lse
 
 

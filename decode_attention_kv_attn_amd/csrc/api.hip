@@ -4,6 +4,9 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/attn_decode.h"
 #include "internal.h"
 
@@ -227,8 +230,43 @@ size_t attn_decode_gqa_global_workspace_bytes(int B, int H_q, int H_kv,
 
 }  // extern "C"
 
+// ----------------------------------------------------------------------------
+// attn_decode_gqa_noalloc: attn_decode_gqa with its split / balanced-list
+// buffers in a file-scope device array instead of a caller's workspace.
+// Each device holds its own copy of `scratch` until the process ends.  Host
+// code never passes the array's name to a kernel or a copy (on the host it is
+// only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current,
+// and is the only form of the buffer host code uses.
 namespace attn {
 namespace {
+
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch (nullptr on failure).
+void* scratch_addr(int* status) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = ATTN_ERR_HIP;
+    return nullptr;
+  }
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      *status = ATTN_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 
 // Paged caches: (block_table, max_pages, page_shift, num_pages), with
 // T_cap = max_pages << page_shift; block_table == nullptr otherwise.
@@ -246,7 +284,7 @@ int decode_gqa(const void* q, const void* k, const void* v, float* out,
                const int32_t* gpos, int n_global, PagedArgs pg, int B, int L,
                int H_q, int H_kv, int T_cap, int d, int dtype, int window,
                float scale, int num_splits, void* workspace,
-               size_t workspace_bytes, void* stream) {
+               size_t workspace_bytes, void* stream, bool use_scratch = false) {
   const int ring = ring_head != nullptr;
   if (L < 1 || L > ATTN_MAX_QLEN) return ATTN_ERR_ARG;
   if (L > 1 && n_global > 0) return ATTN_ERR_UNSUPPORTED;
@@ -267,6 +305,20 @@ int decode_gqa(const void* q, const void* k, const void* v, float* out,
       (lse_out && !aligned(lse_out, 4)) || (seq_lens && !aligned(seq_lens, 4)) ||
       (ring_head && !aligned(ring_head, 4)))
     return ATTN_ERR_ALIGN;
+  if (use_scratch) {
+    // the device array stands in for the workspace (after every host check,
+    // since finding its address is a HIP call): the fixed splits must fit in
+    // it, the balanced list is taken when it fits too
+    if (p.S > 1 && p.ws_fixed > (size_t)ATTN_NOALLOC_SCRATCH_BYTES)
+      return ATTN_ERR_WORKSPACE;
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (p.S > 1) {
+      workspace = scratch_addr(&st);
+      if (!workspace) return st;
+      workspace_bytes = ATTN_NOALLOC_SCRATCH_BYTES;
+    }
+  }
   // balanced work list: lengths given, out 16-byte aligned (the merge writes
   // whole vectors) and room for its parts; else the fixed splits
   const bool bal = p.cap > 0 && seq_lens && aligned(out, 16) && workspace &&
@@ -354,6 +406,16 @@ int attn_decode_gqa(const void* q, const void* k, const void* v, float* out,
                     window, scale, num_splits, workspace, workspace_bytes, stream);
 }
 
+int attn_decode_gqa_noalloc(const void* q, const void* k, const void* v, float* out,
+                            float* lse_out, const int32_t* seq_lens,
+                            const int32_t* ring_head, int B, int H_q, int H_kv,
+                            int T_cap, int d, int dtype, int window, float scale,
+                            int num_splits, void* stream) {
+  return decode_gqa(q, k, v, out, lse_out, seq_lens, ring_head, nullptr, 0,
+                    PagedArgs{nullptr, 0, 0, 0}, B, 1, H_q, H_kv, T_cap, d, dtype,
+                    window, scale, num_splits, nullptr, 0, stream, true);
+}
+
 int attn_decode_gqa_multi(const void* q, const void* k, const void* v,
                           float* out, float* lse_out, const int32_t* seq_lens,
                           const int32_t* ring_head, int B, int q_len, int H_q,
@@ -396,6 +458,7 @@ int attn_decode_gqa_paged(const void* q, const void* k_pages,
                     H_q, H_kv, max_pages * page_size, d, dtype, window, scale,
                     num_splits, workspace, workspace_bytes, stream);
 }
+
 
 int attn_combine(const float* o_part, const float* lse_part, float* out,
                  float* lse_out, int B, int H, int S, int d_v, void* stream) {

@@ -22,7 +22,8 @@
  *    The library never allocates, frees or synchronises; every call only
  *    enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
  *    returns.  The caller keeps inputs alive and unmodified until the stream
- *    reaches the work.  Calls are thread-safe; there is no global state.
+ *    reaches the work.  Calls are thread-safe; the only global state is the
+ *    per-GPU device array of attn_decode_gqa_noalloc (see there).
  *  - Tensors are dense, row-major, in exactly the shapes given.  q, k, v,
  *    latent and workspace must be 16-byte aligned; out, lse_out and the
  *    partial buffers 4-byte aligned.
@@ -119,6 +120,37 @@ int attn_decode_gqa(const void* q, const void* k, const void* v, float* out,
                     int T_cap, int d, int dtype, int window, float scale,
                     int num_splits, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* Bytes of the device array attn_decode_gqa_noalloc keeps its split results
+ * in (16 MiB per GPU). */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * attn_decode_gqa_noalloc -- attn_decode_gqa for callers that cannot
+ * allocate device memory or manage a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments, meaning and result as attn_decode_gqa without workspace /
+ * workspace_bytes: the split partials (and the balanced list's parts) go to
+ * a device array of ATTN_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends.  The call allocates nothing
+ * (no hipMalloc or hipFree, no allocating library routine); its first call
+ * on a device looks up that device's array address once.  The caller still
+ * passes inputs and outputs.
+ *   - A plan whose fixed splits need more than ATTN_NOALLOC_SCRATCH_BYTES
+ *     (attn_decode_gqa_workspace_bytes with ring and num_splits as given,
+ *     for the fixed part) returns ATTN_ERR_WORKSPACE before any HIP call;
+ *     the balanced list is used only when it fits.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on
+ *     one GPU (two streams, or two threads each with its own stream) race
+ *     and give unspecified results.  Calls ordered on one stream are safe.
+ *     The array's contents on entry are never read before they are written.
+ */
+int attn_decode_gqa_noalloc(const void* q, const void* k, const void* v,
+                            float* out, float* lse_out, const int32_t* seq_lens,
+                            const int32_t* ring_head, int B, int H_q, int H_kv,
+                            int T_cap, int d, int dtype, int window, float scale,
+                            int num_splits, void* stream);
 
 /* Split count attn_decode_gqa would use for these arguments (>= 1), or a
  * negative status if the shape arguments are invalid. */

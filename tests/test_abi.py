@@ -79,6 +79,44 @@ def test_gqa_host_errors(lib):
     assert gqa(lib, B=0, q=None, k=None, v=None, out=None) == 0
 
 
+def noalloc(lib, q=P16, k=P16, v=P16, out=P16, lse=None, sl=None, rh=None, B=1,
+            H_q=8, H_kv=2, T=512, d=64, dt=1, window=0, scale=0.0, S=0):
+    return lib.attn_decode_gqa_noalloc(q, k, v, out, lse, sl, rh, B, H_q, H_kv, T,
+                                       d, dt, window, scale, S, None)
+
+
+def test_gqa_noalloc_host_errors(lib):
+    """The no-allocation form checks like attn_decode_gqa, and rejects a plan
+    whose fixed splits exceed its device array before any HIP call."""
+    assert noalloc(lib, q=None) == -1
+    assert noalloc(lib, out=None) == -1
+    assert noalloc(lib, H_kv=3) == -2
+    assert noalloc(lib, dt=7) == -3
+    assert noalloc(lib, d=96) == -4
+    assert noalloc(lib, rh=P16, window=513) == -5
+    assert noalloc(lib, out=ctypes.c_void_p(4098)) == -7
+    assert noalloc(lib, scale=float("inf")) == -9
+    assert noalloc(lib, S=2000) == -9
+    assert noalloc(lib, B=0, q=None, k=None, v=None, out=None) == 0
+    # 64 x 32 heads x 16 splits x 128 floats: 16 MiB of partials plus their
+    # log-sum-exps -- past the array; 8 splits fit
+    big = dict(B=64, H_q=32, H_kv=32, T=32768, d=128)
+    assert lib.attn_decode_gqa_workspace_bytes(64, 32, 32, 32768, 128, 1, 0, 0, 16) \
+        > L.ATTN_NOALLOC_SCRATCH_BYTES
+    assert lib.attn_decode_gqa_workspace_bytes(64, 32, 32, 32768, 128, 1, 0, 0, 8) \
+        <= L.ATTN_NOALLOC_SCRATCH_BYTES
+    assert noalloc(lib, S=16, **big) == -6
+    assert noalloc(lib, S=1000, B=1, H_q=32, H_kv=1, T=32768, d=256) == -6
+
+
+def test_noalloc_binding_needs_out():
+    import torch
+    q = torch.zeros(1, 8, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out is required"):
+        L.attn_decode_gqa_noalloc(q, k, k, None)
+
+
 def test_combine_and_mla_host_errors(lib):
     assert lib.attn_combine(None, P16, P16, None, 1, 1, 2, 8, None) == -1
     assert lib.attn_combine(P16, P16, P16, None, 1, 1, 0, 8, None) == -9
