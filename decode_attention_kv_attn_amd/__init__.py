@@ -32,7 +32,9 @@ ATTN_BF16 = 1
 ATTN_NOALLOC_SCRATCH_BYTES = 16 << 20  # attn_decode_gqa_noalloc's device array
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libattn_decode.so")
+# ATTN_DECODE_LIBRARY names another build of the same library (the host-side
+# sanitizer build of the tests); by default the in-tree one.
+library_path = os.environ.get("ATTN_DECODE_LIBRARY") or os.path.join(_HERE, "libattn_decode.so")
 _LIB = None
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -217,11 +219,17 @@ def attn_status_string(status):
     return library().attn_status_string(status).decode()
 
 
+def _empty(shape, dtype, device):
+    """Every output and workspace the binding allocates comes from here (one
+    place a test can wrap, e.g. with guard bands around each buffer)."""
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
 def _workspace(nbytes, device, workspace):
     if nbytes == 0:
         return workspace
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        workspace = _empty((nbytes,), torch.uint8, device)
     return workspace
 
 
@@ -258,9 +266,9 @@ def attn_decode_gqa(q, k, v, seq_lens=None, ring_head=None, window=0,
     _on_device(q, k, v, seq_lens, ring_head, out, lse, workspace)
     dt = _dtype_code(q)
     if out is None:
-        out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
+        out = _empty((B, H_q, d), torch.float32, q.device)
     if lse is None and want_lse:
-        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+        lse = _empty((B, H_q), torch.float32, q.device)
     ring = ring_head is not None
     nbytes = attn_decode_gqa_workspace_bytes(B, H_q, H_kv, T_cap, d, dt,
                                              window, ring, num_splits)
@@ -326,9 +334,9 @@ def attn_decode_gqa_global(q, k, v, global_pos, window, seq_lens=None,
     dt = _dtype_code(q)
     n_global = 0 if global_pos is None else global_pos.numel()
     if out is None:
-        out = torch.empty((B, H_q, d), dtype=torch.float32, device=q.device)
+        out = _empty((B, H_q, d), torch.float32, q.device)
     if lse is None and want_lse:
-        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+        lse = _empty((B, H_q), torch.float32, q.device)
     nbytes = attn_decode_gqa_global_workspace_bytes(
         B, H_q, H_kv, T_cap, d, dt, window, n_global, num_splits)
     if nbytes == 2**64 - 1:
@@ -384,9 +392,9 @@ def attn_decode_mla(q, latent, d_c, scale, seq_lens=None, num_splits=0,
     T_cap = latent.shape[1]
     d_rope = dk - d_c
     if out is None:
-        out = torch.empty((B, H, d_c), dtype=torch.float32, device=q.device)
+        out = _empty((B, H, d_c), torch.float32, q.device)
     if lse is None and want_lse:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+        lse = _empty((B, H), torch.float32, q.device)
     nbytes = attn_decode_mla_workspace_bytes(B, H, T_cap, d_c, d_rope, num_splits)
     if nbytes == 2**64 - 1:
         nbytes = 0
@@ -410,9 +418,9 @@ def attn_combine(o_part, lse_part, out=None, lse=None, want_lse=True,
     _expect(lse, "lse", (B, H), _F32)
     _on_device(o_part, lse_part, out, lse)
     if out is None:
-        out = torch.empty((B, H, d_v), dtype=torch.float32, device=o_part.device)
+        out = _empty((B, H, d_v), torch.float32, o_part.device)
     if lse is None and want_lse:
-        lse = torch.empty((B, H), dtype=torch.float32, device=o_part.device)
+        lse = _empty((B, H), torch.float32, o_part.device)
     st = library().attn_combine(_ptr(o_part), _ptr(lse_part), _ptr(out),
                                 _ptr(lse), B, H, S, d_v,
                                 _stream(stream, o_part.device))
@@ -501,9 +509,9 @@ def attn_decode_gqa_paged(q, k_pages, v_pages, block_table, seq_lens=None,
     max_pages = block_table.shape[1]
     dt = _dtype_code(q)
     if out is None:
-        out = torch.empty((*lead, H_q, d), dtype=torch.float32, device=q.device)
+        out = _empty((*lead, H_q, d), torch.float32, q.device)
     if lse is None and want_lse:
-        lse = torch.empty((*lead, H_q), dtype=torch.float32, device=q.device)
+        lse = _empty((*lead, H_q), torch.float32, q.device)
     nbytes = _gqa_plan_bytes(B, L, H_q, H_kv, max_pages * P, d, dt, window, False,
                              num_splits)
     workspace = _workspace(nbytes, q.device, workspace)
@@ -528,9 +536,9 @@ def attn_decode_gqa_multi(q, k, v, seq_lens=None, ring_head=None, window=0,
     _on_device(q, k, v, seq_lens, ring_head, out, lse, workspace)
     dt = _dtype_code(q)
     if out is None:
-        out = torch.empty((B, L, H_q, d), dtype=torch.float32, device=q.device)
+        out = _empty((B, L, H_q, d), torch.float32, q.device)
     if lse is None and want_lse:
-        lse = torch.empty((B, L, H_q), dtype=torch.float32, device=q.device)
+        lse = _empty((B, L, H_q), torch.float32, q.device)
     nbytes = _gqa_plan_bytes(B, L, H_q, H_kv, T_cap, d, dt, window,
                              ring_head is not None, num_splits)
     workspace = _workspace(nbytes, q.device, workspace)
@@ -559,9 +567,9 @@ def attn_decode_mla_paged(q, latent_pages, block_table, d_c, scale,
     max_pages = block_table.shape[1]
     d_rope = dk - d_c
     if out is None:
-        out = torch.empty((*lead, H, d_c), dtype=torch.float32, device=q.device)
+        out = _empty((*lead, H, d_c), torch.float32, q.device)
     if lse is None and want_lse:
-        lse = torch.empty((*lead, H), dtype=torch.float32, device=q.device)
+        lse = _empty((*lead, H), torch.float32, q.device)
     nbytes = attn_decode_mla_workspace_bytes(B, H * L, max_pages * P, d_c, d_rope,
                                              num_splits)
     if nbytes == 2**64 - 1:
@@ -588,9 +596,9 @@ def attn_decode_mla_multi(q, latent, d_c, scale, seq_lens=None, num_splits=0,
     T_cap = latent.shape[1]
     d_rope = dk - d_c
     if out is None:
-        out = torch.empty((B, L, H, d_c), dtype=torch.float32, device=q.device)
+        out = _empty((B, L, H, d_c), torch.float32, q.device)
     if lse is None and want_lse:
-        lse = torch.empty((B, L, H), dtype=torch.float32, device=q.device)
+        lse = _empty((B, L, H), torch.float32, q.device)
     nbytes = attn_decode_mla_workspace_bytes(B, H * L, T_cap, d_c, d_rope, num_splits)
     if nbytes == 2**64 - 1:
         nbytes = 0

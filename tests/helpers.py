@@ -98,3 +98,43 @@ def mla_oracle_every_sequence(inp, w):
 
     res = map_units(seq, list(range(w["B"])))
     return (np.concatenate([z for z, _ in res]), np.concatenate([l for _, l in res]))
+
+
+class GuardBands:
+    """Allocator that surrounds every buffer with sentinel-filled margins.
+
+    Each allocation is one larger device buffer: MARGIN bytes of FILL, the
+    tensor itself, MARGIN bytes of FILL (MARGIN keeps the tensor's 256-byte
+    alignment).  check() waits for the GPU and asserts that no margin byte
+    changed, so a kernel that writes past either end of an output, a
+    log-sum-exp or a workspace region fails the test that ran it."""
+
+    MARGIN = 64 << 10
+    FILL = 0x5A
+
+    def __init__(self):
+        self.buffers = []
+
+    def empty(self, shape, dtype, device):
+        n = 1
+        for x in shape:
+            n *= int(x)
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        buf = torch.full((nbytes + 2 * self.MARGIN,), self.FILL, dtype=torch.uint8,
+                         device=device)
+        self.buffers.append((buf, nbytes, tuple(shape), dtype))
+        return buf[self.MARGIN:self.MARGIN + nbytes].view(dtype).view(shape)
+
+    def check(self):
+        if not self.buffers:
+            return
+        if any(b.is_cuda for b, *_ in self.buffers):
+            torch.cuda.synchronize()
+        for buf, nbytes, shape, dtype in self.buffers:
+            head = buf[:self.MARGIN]
+            tail = buf[self.MARGIN + nbytes:]
+            bad_head = int((head != self.FILL).sum())
+            bad_tail = int((tail != self.FILL).sum())
+            assert bad_head == 0 and bad_tail == 0, (
+                f"guard band of a {dtype} {shape} buffer overwritten: "
+                f"{bad_head} bytes before it, {bad_tail} after it")
