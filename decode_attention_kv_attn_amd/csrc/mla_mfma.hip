@@ -3,7 +3,7 @@
 // Every query head of a sequence reads the same latent rows [c_j | k^R_j]
 // (xuesongtap "attention-head" note, sections 5.2-5.3: keys absorbed into
 // the query, the RoPE key shared by all heads, values projected after the
-// weighted sum), so both products are dense and run on MFMA 16x16x32 bf16:
+// weighted sum), so both products are dense and run on MFMA 16x16x32:
 //
 //   S^T[tokens, heads] = L[tokens, 0:576] . Q^T[576, heads]
 //   Z^T[0:512, heads] += L[tokens, 0:512]^T . P^T[tokens, heads]
@@ -17,8 +17,16 @@
 // operands come transposed through ds_read_b64_tr_b16.  Rows are swizzled
 // in 16-byte chunks so both read patterns are free of bank conflicts.
 //
-// The weights keep ~16 significant bits as P_hi + P_lo in bf16 (two MFMAs
-// per value block); the value columns stay exactly bf16.
+// Precision, per geometry.  fp16 (the 512 + 64 latent, where the matrix
+// cores bound the kernel): each tile is converted from bf16 to fp16 in place,
+// once, by all waves together while the tile before it is computed (a bf16
+// value converts exactly when 2^-14 <= |x| <= 65504, smaller ones with an
+// absolute error below 2^-25; larger ones overflow), and the queries once at
+// the start; the softmax weights enter the value product as fp16 (11
+// significant bits, rounded to nearest), one MFMA per value block.  bf16
+// (the 256 + 64 latent, bound by memory): the data stays bf16 and the weights
+// keep about 16 significant bits as a bf16 high part plus a bf16 remainder,
+// two MFMAs per value block.
 //
 // Paged latent caches ([num_pages, P, 576], P a power of two >= 16; the
 // paging the baidu article, section 四.3, names for MLA): splits and tiles
@@ -36,6 +44,9 @@
 // Tuning knobs (compile-time; defaults are the measured best).
 #ifndef ATTN_MLA_QK_AHEAD  // k-steps the score operand reads run ahead
 #define ATTN_MLA_QK_AHEAD 2
+#endif
+#ifndef ATTN_MLA_V_AHEAD  // value blocks the transposed operand reads run ahead
+#define ATTN_MLA_V_AHEAD 2
 #endif
 
 namespace attn {
@@ -57,9 +68,10 @@ constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor flags (gfx9)
 // Latent geometry and group shape: rows of DK = d_c + d_rope bf16, the first
 // DV columns are the values; NW waves of HW (head, token) columns each;
 // STAGES tiles in LDS (STAGES - 1 loading while one is computed).
-template <int DK, int DV, int NW, int HW, int STAGES>
+template <int DK, int DV, int NW, int HW, int STAGES, bool F16>
 struct MlaGeo {
   static constexpr int kDK = DK, kDV = DV, kNW = NW, kHW = HW, kStages = STAGES;
+  static constexpr bool kF16 = F16;  // fp16 products (else bf16, split weights)
   static constexpr int kHB = HW / 16;                     // 16-column blocks per wave
   static constexpr int kHG = NW * HW;                     // columns per group
   static constexpr int kRowBytes = DK * 2;
@@ -75,7 +87,7 @@ struct MlaGeo {
   static_assert((16 * kRowBytes) % 1024 == 0, "tile halves are whole loads");
   static_assert(16 * kRowBytes <= 65536, "per-lane offsets in a half fit 16 bits");
   static_assert(HW % 16 == 0 && (HW / 16 == 1 || HW / 16 == 2), "column blocks");
-  static_assert(STAGES >= 2 && STAGES * kTileBytes <= kLdsPerCU, "stages");
+  static_assert(STAGES >= (F16 ? 3 : 2) && STAGES * kTileBytes <= kLdsPerCU, "stages");
   static constexpr int kGroupsPerCU = kLdsPerCU / (STAGES * kTileBytes);
 };
 // (512, 64): four waves of 32 heads, four stages (144 KiB, one group per
@@ -83,8 +95,11 @@ struct MlaGeo {
 #ifndef ATTN_MLA_NARROW_STAGES
 #define ATTN_MLA_NARROW_STAGES 4
 #endif
-using GeoWide = MlaGeo<576, 512, 4, 32, 4>;
-using GeoNarrow = MlaGeo<320, 256, 2, 16, ATTN_MLA_NARROW_STAGES>;
+#ifndef ATTN_MLA_WIDE_WAVES  // waves sharing the 128 heads of a group
+#define ATTN_MLA_WIDE_WAVES 4
+#endif
+using GeoWide = MlaGeo<576, 512, ATTN_MLA_WIDE_WAVES, 128 / ATTN_MLA_WIDE_WAVES, 4, true>;
+using GeoNarrow = MlaGeo<320, 256, 2, 16, ATTN_MLA_NARROW_STAGES, false>;
 
 // Chunk swizzle: logical 16-byte chunk c of row t sits at chunk c ^ swz(t);
 // the xor stays inside an aligned group of 8 chunks.  Chosen by measured LDS
@@ -93,10 +108,25 @@ using GeoNarrow = MlaGeo<320, 256, 2, 16, ATTN_MLA_NARROW_STAGES>;
 // swz(t + 16) = swz(t): the two 16-row halves of a tile share their layout.
 ATTN_DEV int swz(int t) { return t & 7; }
 
-ATTN_DEV bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+typedef _Float16 f16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+
+// (a, b) -> packed fp16, rounded to nearest even (v_cvt_pk_f16_f32).
+ATTN_DEV uint32_t pack_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{a, b}, f16x2_v));
+}
+
+// Two bf16 (one dword) -> two fp16 (exact in fp16's normal range).
+ATTN_DEV uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack_f16(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+
+ATTN_DEV uint4 bf16x8_to_f16x8(uint4 u) {
+  return make_uint4(bf16x2_to_f16x2(u.x), bf16x2_to_f16x2(u.y), bf16x2_to_f16x2(u.z),
+                    bf16x2_to_f16x2(u.w));
+}
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
-typedef float f32x2_v __attribute__((ext_vector_type(2)));
 
 // (a, b) -> packed bf16 high parts (round to nearest even, v_cvt_pk_bf16_f32)
 // and packed bf16 remainders a - hi(a), b - hi(b): hi + lo carries about 16
@@ -108,8 +138,8 @@ ATTN_DEV void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{ra, rb}, bf16x2_v));
 }
 
-// The MFMAs are written out (v_mfma_f32_16x16x32_bf16, accumulating in
-// place).  The compiler's own form keeps no accumulator in place once the
+// The MFMAs are written out (v_mfma_f32_16x16x32_f16 or _bf16, accumulating
+// in place).  The compiler's own form keeps no accumulator in place once the
 // 256 AGPRs are all taken by o: it routes each result through a scratch
 // register and shuttles accumulators between the register files, and an
 // MFMA that overwrites a register an earlier one still reads stalls the
@@ -117,18 +147,33 @@ ATTN_DEV void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
 // score accumulators are VGPRs, the value accumulators AGPRs.  Since the
 // compiler does not see these as MFMAs, the hazards it would cover are
 // covered here: VALU reads of an MFMA result wait out its latency
-// (mfma_drain_*), and operands written by VALU instructions get wait states
-// before their first MFMA (the s_nop in the value product's prologue).
-ATTN_DEV void mfma_first_v(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+// (ATTN_MFMA_DRAIN), and operands written by VALU instructions get wait
+// states before their first MFMA (the s_nop in the value product's prologue).
+// Operands are 8 fp16 or 8 bf16 in four dwords.
+template <bool F16>
+ATTN_DEV void mfma_first_v(f32x4_t& acc, const u32x4& a, const u32x4& b) {
+  if constexpr (F16)
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
-ATTN_DEV void mfma_v(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+template <bool F16>
+ATTN_DEV void mfma_v(f32x4_t& acc, const u32x4& a, const u32x4& b) {
+  if constexpr (F16)
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
-ATTN_DEV void mfma_a(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+template <bool F16>
+ATTN_DEV void mfma_a(f32x4_t& acc, const u32x4& a, const u32x4& b) {
+  if constexpr (F16)
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 #define ATTN_MFMA_DRAIN "s_nop 15\n\ts_nop 15"
+
+ATTN_DEV u32x4 as_u32x4(const uint4& u) { return __builtin_bit_cast(u32x4, u); }
 
 // One direct-to-LDS buffer load: lane l copies the 16 bytes at `base` + voff
 // (the descriptor covers `bytes`) to LDS address lds + 16 l.  Written out so
@@ -194,6 +239,7 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
   constexpr int kTileBytes = G::kTileBytes, kPieces = G::kPieces;
   constexpr int kDmaPerWave = G::kDmaPerWave, kKS = G::kKS, kDB = G::kDB;
   constexpr int kStages = G::kStages;
+  constexpr bool kF16 = G::kF16;
   __shared__ __attribute__((aligned(1024))) unsigned char stages[kStages * kTileBytes];
   // LDS of the stage that holds tile `it`
   auto stage_of = [&](int it) { return stages + (it % kStages) * kTileBytes; };
@@ -357,13 +403,22 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
       if (j < my_pieces) issue_piece(pid, src, dst, j);
   };
 
+  // fp16 conversion of this wave's own loads of a tile: its 1 KiB pieces
+  // wave, wave + kNW, ... (chunk `lane` of each), converted in place once
+  // they have landed -- no other wave's loads are involved, so no barrier
+  // separates a wave's wait from its conversion.
+  auto own_chunk = [&](int t, int j) -> uint4* {
+    return (uint4*)(stage_of(t) + (wave + j * kNW) * 1024 + 16 * lane);
+  };
+
   // Computes tile `it` from its stage.  The loads of tile it+3 (into the
   // stage of tile it-1, which every wave finished before the barrier) are
   // issued piece by piece between the score MFMAs, so their issue stalls
-  // overlap matrix work.  Past the last tile they load a copy of the last
-  // tile into that free stage (an L2 hit, never used): every step issues the
-  // same loads, so the score loop has no branch and the vmcnt waits are the
-  // same for all steps.
+  // overlap matrix work; fp16: this wave's pieces of tile it+1, landed, are
+  // converted between them as well.  Past the last tile the loads fetch a
+  // copy of the last tile into that free stage (an L2 hit, never used, and
+  // converted like any other): every step issues the same loads and
+  // conversions, so the vmcnt waits are the same for all steps.
   auto compute_tile = [&](int it) {
     const unsigned char* tile = stage_of(it);
     const int base = p0 + it * kTT;
@@ -390,13 +445,24 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
         af[k0][tb] = *(const uint4*)(abase[tb][k0 & 1] + 128 * (k0 >> 1));
+    // chunk j of this wave's pieces of tile it+1 is read at k-step
+    // (j * kKS) / kDmaPerWave and written back converted at the next one's
+    uint4 cv[2];
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      // this wave's loads spread evenly over the k-steps
+      // this wave's loads, spread evenly over the k-steps
 #pragma unroll
       for (int j = 0; j < kDmaPerWave; ++j)
         if ((j * kKS) / kDmaPerWave == ks && j < my_pieces)
           issue_piece(pid_cur, next, it + kStages - 1, j);
+      if constexpr (kF16) {
+#pragma unroll
+        for (int j = 0; j < kDmaPerWave; ++j)
+          if ((j * kKS) / kDmaPerWave == ks && j < my_pieces) {
+            if (j > 0) *own_chunk(it + 1, j - 1) = bf16x8_to_f16x8(cv[(j - 1) & 1]);
+            cv[j & 1] = *own_chunk(it + 1, j);
+          }
+      }
       const int cur = ks % (kAhead + 1);
       const int kn = ks + kAhead;
       if (kn < kKS) {
@@ -408,9 +474,14 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int hb = 0; hb < kHB; ++hb) {
-          if (ks == 0) mfma_first_v(sc[tb][hb], as_bf16x8(af[cur][tb]), as_bf16x8(qf[hb][ks]));
-          else mfma_v(sc[tb][hb], as_bf16x8(af[cur][tb]), as_bf16x8(qf[hb][ks]));
+          if (ks == 0) mfma_first_v<kF16>(sc[tb][hb], as_u32x4(af[cur][tb]), as_u32x4(qf[hb][ks]));
+          else mfma_v<kF16>(sc[tb][hb], as_u32x4(af[cur][tb]), as_u32x4(qf[hb][ks]));
         }
+    }
+    if constexpr (kF16) {
+#pragma unroll
+      for (int j = 0; j < kDmaPerWave; ++j)
+        if (j == my_pieces - 1) *own_chunk(it + 1, j) = bf16x8_to_f16x8(cv[j & 1]);
     }
     // the softmax reads the scores with VALU instructions
     if constexpr (kHB == 2)
@@ -419,9 +490,10 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
     else
       asm volatile(ATTN_MFMA_DRAIN : "+v"(sc[0][0]), "+v"(sc[1][0]));
 
-    // online softmax per head (lazy maximum); weights split into bf16 hi+lo
+    // online softmax per head (lazy maximum); weights rounded to fp16, or
+    // split into bf16 high parts and remainders
     const bool full = base + kTT <= p1;  // uniform: no masked row in the tile
-    uint32_t phi[kHB][4], plo[kHB][4];
+    uint32_t ph[kHB][4], pl[kHB][4];
 #pragma unroll
     for (int hb = 0; hb < kHB; ++hb) {
       // raw scores; the scale (> 0) is applied once to the maximum and fused
@@ -436,7 +508,7 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
         for (int j = 0; j < 8; ++j)
           if (base + 16 * (j >> 2) + 4 * lg + (j & 3) >= p1) x[j] = neg_inf();
       }
-      if constexpr (multi) {  // each column's token sees positions <= tl
+      if constexpr (MULTI) {  // each column's token sees positions <= tl
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           if (base + 16 * (j >> 2) + 4 * lg + (j & 3) > tl[hb]) x[j] = neg_inf();
@@ -468,13 +540,16 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
         // row's -inf gives exp2(-inf) = 0 without a test.  Several tokens:
         // a column may have seen no visible row yet (m = -inf), and
         // -inf - (-inf) would be NaN, so masked rows are set to 0.
-        p[j] = (multi && x[j] == neg_inf())
+        p[j] = (MULTI && x[j] == neg_inf())
                    ? 0.f
                    : fast_exp2(fmaf(x[j], a.scale_log2, -m[hb]));
         l[hb] += p[j];
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) split_bf16(p[2 * j], p[2 * j + 1], phi[hb][j], plo[hb][j]);
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (kF16) ph[hb][j] = pack_f16(p[2 * j], p[2 * j + 1]);
+        else split_bf16(p[2 * j], p[2 * j + 1], ph[hb][j], pl[hb][j]);
+      }
     }
 
     // values: transposed 4x16 reads of rows 4*lg + li/4 (and +16), columns
@@ -500,40 +575,53 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
       return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     typedef short s16x8_t __attribute__((ext_vector_type(8)));
-    bf16x8_t bh[kHB], bl[kHB];
+    u32x4 bh[kHB], bl[kHB];
 #pragma unroll
     for (int hb = 0; hb < kHB; ++hb) {
-      bh[hb] = as_bf16x8(make_uint4(phi[hb][0], phi[hb][1], phi[hb][2], phi[hb][3]));
-      bl[hb] = as_bf16x8(make_uint4(plo[hb][0], plo[hb][1], plo[hb][2], plo[hb][3]));
+      bh[hb] = u32x4{ph[hb][0], ph[hb][1], ph[hb][2], ph[hb][3]};
+      if constexpr (!kF16) bl[hb] = u32x4{pl[hb][0], pl[hb][1], pl[hb][2], pl[hb][3]};
     }
     // wait states between the VALU writes of the weights and their MFMAs
-    if constexpr (kHB == 2)
-      asm volatile("s_nop 4" ::"v"(bh[0]), "v"(bl[0]), "v"(bh[kHB - 1]), "v"(bl[kHB - 1]));
+    if constexpr (kF16)
+      asm volatile("s_nop 4" ::"v"(bh[0]), "v"(bh[kHB - 1]));
     else
-      asm volatile("s_nop 4" ::"v"(bh[0]), "v"(bl[0]));
-    // transposed value reads run one block ahead of their MFMAs
-    s16x8_t vf[2];
-    vf[0] = read_v(0);
+      asm volatile("s_nop 4" ::"v"(bh[0]), "v"(bl[0]), "v"(bh[kHB - 1]), "v"(bl[kHB - 1]));
+    // transposed value reads run kVAhead blocks ahead of their MFMAs
+    constexpr int kVAhead = ATTN_MLA_V_AHEAD < kDB ? ATTN_MLA_V_AHEAD : kDB - 1;
+    s16x8_t vf[kVAhead + 1];
+#pragma unroll
+    for (int db = 0; db < kVAhead; ++db) vf[db] = read_v(db);
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
-      const int cur = db & 1;
-      if (db + 1 < kDB) vf[cur ^ 1] = read_v(db + 1);
-      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, vf[cur]);
+      if (db + kVAhead < kDB) vf[(db + kVAhead) % (kVAhead + 1)] = read_v(db + kVAhead);
+      const u32x4 av = __builtin_bit_cast(u32x4, vf[db % (kVAhead + 1)]);
 #pragma unroll
       for (int hb = 0; hb < kHB; ++hb) {
-        mfma_a(o[db][hb], av, bh[hb]);
-        mfma_a(o[db][hb], av, bl[hb]);
+        mfma_a<kF16>(o[db][hb], av, bh[hb]);
+        if constexpr (!kF16) mfma_a<kF16>(o[db][hb], av, bl[hb]);
       }
     }
+    // The compiler does not see these MFMAs, and where steps join it may
+    // move an accumulator to other registers: their latency is waited out
+    // before any such copy can read them.
+    asm volatile(ATTN_MFMA_DRAIN ::: "memory");
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int hb = 0; hb < kHB; ++hb) asm volatile("" : "+a"(o[db][hb]));
   };
 
-  // One pipeline step: tile `it` is computed while tiles it+1 and it+2 land
-  // and tile it+3 is issued.
+  // One pipeline step: tile `it` is computed (and, fp16, tile it+1 converted)
+  // while the later tiles land and tile it+3 is issued.
+  constexpr int kLanding = kF16 ? kStages - 3 : kStages - 2;  // tiles still landing
   auto step = [&](int it) {
     if (it >= ntiles) return;
-    // the next tile's loads (this wave's share) may still be in flight
-    if (my_pieces == kDmaPerWave) wait_vmcnt<(kStages - 2) * kDmaPerWave>();
-    else wait_vmcnt<(kStages - 2) * (kDmaPerWave - 1)>();
+    // fp16: this wave's loads of tile it+1 (converted during this step) must
+    // have landed, those of later tiles may still be in flight, and the
+    // barrier publishes tile it (converted by every wave during the step
+    // before).  bf16: tile it must have landed.
+    if (my_pieces == kDmaPerWave) wait_vmcnt<kLanding * kDmaPerWave>();
+    else wait_vmcnt<kLanding * (kDmaPerWave - 1)>();
     lds_barrier();
     pages_ready();
     compute_tile(it);
@@ -550,9 +638,20 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
     // the query fragments (and the first tiles) land here, once: the loop
     // then carries no wait on the query loads
     wait_vmcnt<0>();
+    if constexpr (kF16) {
+      // the queries and this wave's pieces of tile 0 go to fp16 here (step
+      // 0's barrier publishes tile 0)
+#pragma unroll
+      for (int hb = 0; hb < kHB; ++hb)
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) qf[hb][ks] = bf16x8_to_f16x8(qf[hb][ks]);
+#pragma unroll
+      for (int j = 0; j < kDmaPerWave; ++j)
+        if (j < my_pieces) *own_chunk(0, j) = bf16x8_to_f16x8(*own_chunk(0, j));
+    }
     for (int it = 0; it < ntiles; ++it) step(it);
-    // the last two steps' loads (unused) must land before the group's LDS
-    // is released
+    // the last steps' loads (unused) must land before the group's LDS is
+    // released
     wait_vmcnt<0>();
   }
 

@@ -69,6 +69,32 @@ def test_large_scale_stays_finite():
     _check(q, lat, sl, scale=1.0, what="scale 1 on N(0,1)")
 
 
+def test_fp16_range_edges():
+    """Both products run in fp16, which holds every bf16 value with
+    2^-14 <= |x| <= 65504 exactly (smaller ones with an absolute error below
+    2^-25).  Latent rows carrying entries of +-6e4 next to many of +-1e-6,
+    and queries with entries down to 1e-7: the relative L2 error stays within
+    the bar and the largest error within 2e-3 of the largest output."""
+    B, H, T = 2, 128, 700
+    q, lat, sl = _case(B, H, T, 8450, lens=[700, 321], value_scale=1.0)
+    g = torch.Generator(device="cpu").manual_seed(8451)
+    big = torch.rand(lat.shape, generator=g) < 2e-4
+    tiny = torch.rand(lat.shape, generator=g) < 0.1
+    sign = torch.where(torch.rand(lat.shape, generator=g) < 0.5, -1.0, 1.0)
+    lat32 = lat.float().cpu()
+    lat32 = torch.where(big, sign * 6.0e4, torch.where(tiny, sign * 1.0e-6, lat32))
+    lat = lat32.to(torch.bfloat16).to(DEV)
+    q32 = q.float().cpu()
+    q32 = torch.where(torch.rand(q.shape, generator=g) < 0.1, 1.0e-7, q32)
+    q = q32.to(torch.bfloat16).to(DEV)
+    assert float(lat.abs().max()) <= 65504 and int(big.sum()) > 10
+    z, lse = L.attn_decode_mla(q, lat, D_C, 0.02, sl)
+    torch.cuda.synchronize()
+    rz, rl = oracle.mla_decode_ref(q, lat, D_C, 0.02, sl)
+    assert_parity(z, rz, "fp16 range", atol=2e-3 * max(1.0, float(np.abs(rz).max())))
+    assert_lse(lse, rl, "fp16 range", atol=2e-3 * max(1.0, float(np.abs(rl).max())))
+
+
 def test_integer_recovery():
     """q = 0 makes every visible weight exactly 1/T_b; latent value column i
     holds bit i of the position (column 511 = 1), the RoPE part is random.
