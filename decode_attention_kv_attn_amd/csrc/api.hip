@@ -379,8 +379,8 @@ int decode_gqa(const void* q, const void* k, const void* v, float* out,
                               : launch_gqa_valu(a, dtype, d, (int)grid, s);
   if (e != hipSuccess) return ATTN_ERR_HIP;
   if (bal) {
-    if (launch_combine_balanced(a.o_part, a.lse_part, a.meta, out, lse_out, B, L, H_q,
-                                a.n, p.head_chunks, p.N, d, s) != hipSuccess)
+    if (launch_combine_balanced(a.o_part, false, a.lse_part, a.meta, out, lse_out, B, L,
+                                H_q, a.n, p.head_chunks, p.N, d, s) != hipSuccess)
       return ATTN_ERR_HIP;
   } else if (p.S > 1) {
     if (launch_combine(a.o_part, a.lse_part, out, lse_out, B * L, H_q, p.S, d, s) !=

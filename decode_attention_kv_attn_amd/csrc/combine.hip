@@ -7,6 +7,10 @@
 // "attention-head" note, section 1).  Parts with lse = -inf are empty and get
 // weight 0; if every part is empty the output is 0 and lse is -inf.
 //
+// Partial values are float32, or fp16 where the producing kernel says so (the
+// fp16 MLA geometry, whose values already lie in fp16's range); weights,
+// sums and outputs are float32.
+//
 // Value widths that are a multiple of 64 up to 512 (every width the decode
 // kernels produce): one wave per (b, h) -- two or four when rows are few and
 // parts many -- each lane owning d_v / 64 adjacent columns, read as vectors;
@@ -102,17 +106,24 @@ __global__ __launch_bounds__(kThreads) void lse_combine(
   }
 }
 
-template <int N>
-struct VecOf;
-template <> struct VecOf<1> { typedef float type; };
-template <> struct VecOf<2> { typedef float2 type; };
-template <> struct VecOf<4> { typedef float4 type; };
+typedef _Float16 half2_v __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_v __attribute__((ext_vector_type(4)));
 
-template <int N>
-ATTN_DEV void fma_vec(float (&acc)[N], float w, const typename VecOf<N>::type& x) {
-  const float* xs = reinterpret_cast<const float*>(&x);
+// N elements of P loaded as one vector
+template <typename P, int N>
+struct VecOf;
+template <> struct VecOf<float, 1> { typedef float type; };
+template <> struct VecOf<float, 2> { typedef float2 type; };
+template <> struct VecOf<float, 4> { typedef float4 type; };
+template <> struct VecOf<_Float16, 1> { typedef _Float16 type; };
+template <> struct VecOf<_Float16, 2> { typedef half2_v type; };
+template <> struct VecOf<_Float16, 4> { typedef half4_v type; };
+
+template <typename P, int N>
+ATTN_DEV void fma_vec(float (&acc)[N], float w, const typename VecOf<P, N>::type& x) {
+  const P* xs = reinterpret_cast<const P*>(&x);
 #pragma unroll
-  for (int i = 0; i < N; ++i) acc[i] = add_part(acc[i], w, xs[i]);
+  for (int i = 0; i < N; ++i) acc[i] = add_part(acc[i], w, (float)xs[i]);
 }
 
 // Balanced work list (both GQA kernels): output row
@@ -124,16 +135,17 @@ struct BalancedMap {
   int L, H_q, n, hc, nh;
 };
 
-// CPL = d_v / 64 columns per lane, read as CPL / VW vectors of VW floats.
+// CPL = d_v / 64 columns per lane, read as CPL / VW vectors of VW elements of
+// P (float32 or fp16 partial values).
 // BAL: the parts come from a balanced work list (`bm`), else S parts per row
 // stored next to each other.  WPR waves share a row (parts s = sub, sub +
 // WPR, ...) and add their sums in LDS: few rows with many parts (one long
 // sequence cut into many pieces) would otherwise leave most of the GPU idle
 // while one wave per row walks every part.  Eight parts are in flight per
 // wave.
-template <int CPL, bool BAL, int WPR>
+template <typename P, int CPL, bool BAL, int WPR>
 __global__ __launch_bounds__(kThreads) void lse_combine_rows(
-    const float* __restrict__ o_part, const float* __restrict__ lse_part,
+    const P* __restrict__ o_part, const float* __restrict__ lse_part,
     float* __restrict__ out, float* __restrict__ lse_out, int rows, int S,
     BalancedMap bm) {
   constexpr int VW = CPL >= 4 ? 4 : CPL;
@@ -143,7 +155,8 @@ __global__ __launch_bounds__(kThreads) void lse_combine_rows(
   constexpr int RPB = NWG / WPR;  // rows per work group
   constexpr int DEPTH = 8;        // parts in flight per wave
   static_assert(NWG % WPR == 0 && (!BAL || WPR == 1), "waves per row");
-  typedef typename VecOf<VW>::type vec;
+  typedef typename VecOf<P, VW>::type vec;       // partial values
+  typedef typename VecOf<float, VW>::type ovec;  // outputs
   __shared__ float wts[NWG][kMaxS];
   __shared__ float red[WPR > 1 ? NWG : 1][WPR > 1 ? d_v : 1];
   const int wave = threadIdx.x >> 6;
@@ -210,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_rows(
     for (int k = 0; k < DEPTH; ++k)
       if (sub + k * WPR < S)
 #pragma unroll
-        for (int v = 0; v < NV; ++v) fma_vec<VW>(acc[v], w_s[sub + k * WPR], x0[k][v]);
+        for (int v = 0; v < NV; ++v) fma_vec<P, VW>(acc[v], w_s[sub + k * WPR], x0[k][v]);
     int s = sub + DEPTH * WPR;
     for (; s + (DEPTH - 1) * WPR < S; s += DEPTH * WPR) {
       vec x[DEPTH][NV];
@@ -221,11 +234,11 @@ __global__ __launch_bounds__(kThreads) void lse_combine_rows(
 #pragma unroll
       for (int k = 0; k < DEPTH; ++k)
 #pragma unroll
-        for (int v = 0; v < NV; ++v) fma_vec<VW>(acc[v], w_s[s + k * WPR], x[k][v]);
+        for (int v = 0; v < NV; ++v) fma_vec<P, VW>(acc[v], w_s[s + k * WPR], x[k][v]);
     }
     for (; s < S; s += WPR) {
 #pragma unroll
-      for (int v = 0; v < NV; ++v) fma_vec<VW>(acc[v], w_s[s], op[(size_t)s * step + 64 * v]);
+      for (int v = 0; v < NV; ++v) fma_vec<P, VW>(acc[v], w_s[s], op[(size_t)s * step + 64 * v]);
     }
   }
   if constexpr (WPR > 1) {
@@ -244,10 +257,10 @@ __global__ __launch_bounds__(kThreads) void lse_combine_rows(
         for (int i = 0; i < VW; ++i) acc[v][i] += red[wave + j][(v * VW + i) * 64 + lane];
   }
   const float inv = (tot > 0.f) ? 1.f / tot : 0.f;
-  vec* dst = reinterpret_cast<vec*>(out + row * d_v) + lane;
+  ovec* dst = reinterpret_cast<ovec*>(out + row * d_v) + lane;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    vec r;
+    ovec r;
     float* rs = reinterpret_cast<float*>(&r);
 #pragma unroll
     for (int i = 0; i < VW; ++i) rs[i] = acc[v][i] * inv;
@@ -255,27 +268,27 @@ __global__ __launch_bounds__(kThreads) void lse_combine_rows(
   }
 }
 
-template <bool BAL, int WPR>
-hipError_t launch_rows(int cpl, const float* o_part, const float* lse_part, float* out,
+template <typename P, bool BAL, int WPR>
+hipError_t launch_rows(int cpl, const P* o_part, const float* lse_part, float* out,
                        float* lse, int rows, int S, const BalancedMap& bm,
                        hipStream_t stream) {
   constexpr int RPB = kThreads / 64 / WPR;
   const dim3 g((unsigned)((rows + RPB - 1) / RPB)), blk(kThreads);
   switch (cpl) {
     case 1:
-      hipLaunchKernelGGL((lse_combine_rows<1, BAL, WPR>), g, blk, 0, stream, o_part,
+      hipLaunchKernelGGL((lse_combine_rows<P, 1, BAL, WPR>), g, blk, 0, stream, o_part,
                          lse_part, out, lse, rows, S, bm);
       break;
     case 2:
-      hipLaunchKernelGGL((lse_combine_rows<2, BAL, WPR>), g, blk, 0, stream, o_part,
+      hipLaunchKernelGGL((lse_combine_rows<P, 2, BAL, WPR>), g, blk, 0, stream, o_part,
                          lse_part, out, lse, rows, S, bm);
       break;
     case 4:
-      hipLaunchKernelGGL((lse_combine_rows<4, BAL, WPR>), g, blk, 0, stream, o_part,
+      hipLaunchKernelGGL((lse_combine_rows<P, 4, BAL, WPR>), g, blk, 0, stream, o_part,
                          lse_part, out, lse, rows, S, bm);
       break;
     case 8:
-      hipLaunchKernelGGL((lse_combine_rows<8, BAL, WPR>), g, blk, 0, stream, o_part,
+      hipLaunchKernelGGL((lse_combine_rows<P, 8, BAL, WPR>), g, blk, 0, stream, o_part,
                          lse_part, out, lse, rows, S, bm);
       break;
     default: return hipErrorInvalidValue;
@@ -297,10 +310,10 @@ hipError_t launch_combine(const float* o_part, const float* lse_part,
     // many (about four per CU), else one
     const BalancedMap none{};
     if (S >= 32 && rows <= 256)
-      return launch_rows<false, 4>(cpl, o_part, lse_part, out, lse, rows, S, none, stream);
+      return launch_rows<float, false, 4>(cpl, o_part, lse_part, out, lse, rows, S, none, stream);
     if (S >= 16 && rows <= 512)
-      return launch_rows<false, 2>(cpl, o_part, lse_part, out, lse, rows, S, none, stream);
-    return launch_rows<false, 1>(cpl, o_part, lse_part, out, lse, rows, S, none, stream);
+      return launch_rows<float, false, 2>(cpl, o_part, lse_part, out, lse, rows, S, none, stream);
+    return launch_rows<float, false, 1>(cpl, o_part, lse_part, out, lse, rows, S, none, stream);
   }
   const int cl = d_v >= 256 ? 256 : (d_v > 128 ? 256 : (d_v > 64 ? 128 : 64));
   hipLaunchKernelGGL(lse_combine, dim3((unsigned)rows), dim3(kThreads), 0, stream,
@@ -308,16 +321,36 @@ hipError_t launch_combine(const float* o_part, const float* lse_part,
   return hipGetLastError();
 }
 
-hipError_t launch_combine_balanced(const float* o_part, const float* lse_part,
-                                   const int* meta, float* out, float* lse, int B,
-                                   int L, int H_q, int n, int head_chunks,
-                                   int heads_per_item, int d_v, hipStream_t stream) {
+hipError_t launch_combine_half(const void* o_part, const float* lse_part, float* out,
+                               float* lse, int B, int H, int S, int d_v,
+                               hipStream_t stream) {
+  if (S > kMaxS || (uintptr_t)o_part % 16 != 0 || (uintptr_t)out % 16 != 0 ||
+      d_v % 64 != 0 || d_v > 512)
+    return hipErrorInvalidValue;
+  const BalancedMap none{};
+  const int rows = B * H, cpl = d_v / 64;
+  const _Float16* op = (const _Float16*)o_part;
+  if (S >= 32 && rows <= 256)
+    return launch_rows<_Float16, false, 4>(cpl, op, lse_part, out, lse, rows, S, none, stream);
+  if (S >= 16 && rows <= 512)
+    return launch_rows<_Float16, false, 2>(cpl, op, lse_part, out, lse, rows, S, none, stream);
+  return launch_rows<_Float16, false, 1>(cpl, op, lse_part, out, lse, rows, S, none, stream);
+}
+
+hipError_t launch_combine_balanced(const void* o_part, bool half_parts,
+                                   const float* lse_part, const int* meta, float* out,
+                                   float* lse, int B, int L, int H_q, int n,
+                                   int head_chunks, int heads_per_item, int d_v,
+                                   hipStream_t stream) {
   if ((uintptr_t)o_part % 16 != 0 || (uintptr_t)out % 16 != 0 || d_v % 64 != 0 ||
       d_v > 512)
     return hipErrorInvalidValue;
   const BalancedMap bm{meta, L, H_q, n, head_chunks, heads_per_item};
-  return launch_rows<true, 1>(d_v / 64, o_part, lse_part, out, lse, B * L * H_q, 0, bm,
-                              stream);
+  if (half_parts)
+    return launch_rows<_Float16, true, 1>(d_v / 64, (const _Float16*)o_part, lse_part, out,
+                                          lse, B * L * H_q, 0, bm, stream);
+  return launch_rows<float, true, 1>(d_v / 64, (const float*)o_part, lse_part, out, lse,
+                                     B * L * H_q, 0, bm, stream);
 }
 
 }  // namespace attn

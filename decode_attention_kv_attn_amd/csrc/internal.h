@@ -81,6 +81,9 @@ hipError_t launch_gqa_mfma(const GqaArgs& a, int d, int heads_per_item, int grid
 int mla_heads_per_group(int d_c);  // (head, token) columns per work group
 int mla_groups_per_cu(int d_c);    // work groups one CU holds at once (LDS)
 int mla_tile_rows();
+// true: the kernel writes its split partial values as fp16 (the o_part region
+// keeps its float32 size; the fp16 rows fill its first half)
+bool mla_half_parts(int d_c);
 // L query tokens per sequence (q [B, L, H, DK], outputs [B, L, H, ...]) with
 // DK = d_c + 64; block_table == nullptr: dense latent [B, T_cap, DK]; else a
 // page pool [num_pages, 2^page_shift, DK] with T_cap = max_pages <<
@@ -109,11 +112,18 @@ hipError_t launch_combine(const float* o_part, const float* lse_part,
 // Merge of a balanced work list's pieces (GqaArgs::balanced): output row
 // (b * L + token) * H_q + head, for heads_per_item columns per item and
 // head_chunks items per KV head; rows whose sequence has one piece per unit
-// are left as the decode kernel wrote them.  o_part and out 16-byte aligned,
-// d_v in {64, 128, 256, 512}.
-hipError_t launch_combine_balanced(const float* o_part, const float* lse_part,
-                                   const int* meta, float* out, float* lse, int B,
-                                   int L, int H_q, int n, int head_chunks,
-                                   int heads_per_item, int d_v, hipStream_t stream);
+// are left as the decode kernel wrote them.  o_part (float32, or fp16 when
+// half_parts) and out 16-byte aligned, d_v in {64, 128, 256, 512}.
+hipError_t launch_combine_balanced(const void* o_part, bool half_parts,
+                                   const float* lse_part, const int* meta, float* out,
+                                   float* lse, int B, int L, int H_q, int n,
+                                   int head_chunks, int heads_per_item, int d_v,
+                                   hipStream_t stream);
+
+// launch_combine with fp16 partial values (o_part [B, H, S, d_v] of _Float16,
+// 16-byte aligned; d_v a multiple of 64 up to 512).
+hipError_t launch_combine_half(const void* o_part, const float* lse_part, float* out,
+                               float* lse, int B, int H, int S, int d_v,
+                               hipStream_t stream);
 
 }  // namespace attn

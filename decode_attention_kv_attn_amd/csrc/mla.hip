@@ -145,14 +145,18 @@ int decode_mla(const void* q, const void* latent, float* out, float* lse_out,
                             bal ? p.cap : 0, meta, scale * 1.4426950408889634f,
                             s) != hipSuccess)
     return ATTN_ERR_HIP;
+  const bool half = attn::mla_half_parts(d_c);
   if (bal) {
     // columns are (head, token) pairs of one latent: n = H heads share it
-    if (attn::launch_combine_balanced(o_part, lse_part, meta, out, lse_out, B, L, H, H,
-                                      p.head_chunks, hg, d_c, s) != hipSuccess)
+    if (attn::launch_combine_balanced(o_part, half, lse_part, meta, out, lse_out, B, L,
+                                      H, H, p.head_chunks, hg, d_c, s) != hipSuccess)
       return ATTN_ERR_HIP;
-  } else if (p.S > 1 && attn::launch_combine(o_part, lse_part, out, lse_out, B, H * L,
-                                             p.S, d_c, s) != hipSuccess) {
-    return ATTN_ERR_HIP;
+  } else if (p.S > 1) {
+    const hipError_t e =
+        half ? attn::launch_combine_half(o_part, lse_part, out, lse_out, B, H * L, p.S,
+                                         d_c, s)
+             : attn::launch_combine(o_part, lse_part, out, lse_out, B, H * L, p.S, d_c, s);
+    if (e != hipSuccess) return ATTN_ERR_HIP;
   }
   return ATTN_OK;
 }

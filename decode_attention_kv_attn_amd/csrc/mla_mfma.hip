@@ -23,7 +23,9 @@
 // value converts exactly when 2^-14 <= |x| <= 65504, smaller ones with an
 // absolute error below 2^-25; larger ones overflow), and the queries once at
 // the start; the softmax weights enter the value product as fp16 (11
-// significant bits, rounded to nearest), one MFMA per value block.  bf16
+// significant bits, rounded to nearest), one MFMA per value block; a split's
+// partial values (weighted means of latent values, so inside the same range)
+// are stored as fp16 for the merge, halving that round trip.  bf16
 // (the 256 + 64 latent, bound by memory): the data stays bf16 and the weights
 // keep about 16 significant bits as a bf16 high part plus a bf16 remainder,
 // two MFMAs per value block.
@@ -215,7 +217,7 @@ struct MlaArgs {
   int max_pages, page_shift, num_pages;
   float* out;              // [B, H, DV] when S == 1
   float* lse;              // [B, H] (nullable) when S == 1
-  float* o_part;           // [B, H, S, DV]
+  float* o_part;           // [B, H, S, DV]; fp16 values when G::kF16
   float* lse_part;         // [B, H, S]
   const int32_t* seq_lens;
   int H, T_cap, S, chunk, head_chunks;
@@ -415,7 +417,9 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
   // stage of tile it-1, which every wave finished before the barrier) are
   // issued piece by piece between the score MFMAs, so their issue stalls
   // overlap matrix work; fp16: this wave's pieces of tile it+1, landed, are
-  // converted between them as well.  Past the last tile the loads fetch a
+  // read when the scores are done and written back converted between the
+  // heads' softmax updates (the LDS serves no operand reads then; in the
+  // score loop the same work competes with them).  Past the last tile the loads fetch a
   // copy of the last tile into that free stage (an L2 hit, never used, and
   // converted like any other): every step issues the same loads and
   // conversions, so the vmcnt waits are the same for all steps.
@@ -445,9 +449,6 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
         af[k0][tb] = *(const uint4*)(abase[tb][k0 & 1] + 128 * (k0 >> 1));
-    // chunk j of this wave's pieces of tile it+1 is read at k-step
-    // (j * kKS) / kDmaPerWave and written back converted at the next one's
-    uint4 cv[2];
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
       // this wave's loads, spread evenly over the k-steps
@@ -455,14 +456,6 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
       for (int j = 0; j < kDmaPerWave; ++j)
         if ((j * kKS) / kDmaPerWave == ks && j < my_pieces)
           issue_piece(pid_cur, next, it + kStages - 1, j);
-      if constexpr (kF16) {
-#pragma unroll
-        for (int j = 0; j < kDmaPerWave; ++j)
-          if ((j * kKS) / kDmaPerWave == ks && j < my_pieces) {
-            if (j > 0) *own_chunk(it + 1, j - 1) = bf16x8_to_f16x8(cv[(j - 1) & 1]);
-            cv[j & 1] = *own_chunk(it + 1, j);
-          }
-      }
       const int cur = ks % (kAhead + 1);
       const int kn = ks + kAhead;
       if (kn < kKS) {
@@ -478,11 +471,6 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
           else mfma_v<kF16>(sc[tb][hb], as_u32x4(af[cur][tb]), as_u32x4(qf[hb][ks]));
         }
     }
-    if constexpr (kF16) {
-#pragma unroll
-      for (int j = 0; j < kDmaPerWave; ++j)
-        if (j == my_pieces - 1) *own_chunk(it + 1, j) = bf16x8_to_f16x8(cv[j & 1]);
-    }
     // the softmax reads the scores with VALU instructions
     if constexpr (kHB == 2)
       asm volatile(ATTN_MFMA_DRAIN
@@ -494,6 +482,15 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
     // split into bf16 high parts and remainders
     const bool full = base + kTT <= p1;  // uniform: no masked row in the tile
     uint32_t ph[kHB][4], pl[kHB][4];
+    // fp16: this wave's pieces of tile it+1 are read now and converted
+    // between the heads' softmax updates, while the LDS is otherwise idle
+    uint4 cw[kDmaPerWave];
+    if constexpr (kF16) {
+#pragma unroll
+      for (int j = 0; j < kDmaPerWave; ++j)
+        if (j < my_pieces) cw[j] = *own_chunk(it + 1, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int hb = 0; hb < kHB; ++hb) {
       // raw scores; the scale (> 0) is applied once to the maximum and fused
@@ -550,6 +547,15 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
         if constexpr (kF16) ph[hb][j] = pack_f16(p[2 * j], p[2 * j + 1]);
         else split_bf16(p[2 * j], p[2 * j + 1], ph[hb][j], pl[hb][j]);
       }
+      if constexpr (kF16) {
+        // pieces [hb * D / kHB, (hb + 1) * D / kHB) after head block hb
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < kDmaPerWave; ++j)
+          if (j * kHB / kDmaPerWave == hb && j < my_pieces)
+            *own_chunk(it + 1, j) = bf16x8_to_f16x8(cw[j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 
     // values: transposed 4x16 reads of rows 4*lg + li/4 (and +16), columns
@@ -600,6 +606,7 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
         mfma_a<kF16>(o[db][hb], av, bh[hb]);
         if constexpr (!kF16) mfma_a<kF16>(o[db][hb], av, bl[hb]);
       }
+
     }
     // The compiler does not see these MFMAs, and where steps join it may
     // move an accumulator to other registers: their latency is waited out
@@ -675,10 +682,22 @@ __global__ __launch_bounds__(G::kNW * 64, G::kGroupsPerCU) void mla_decode_mfma(
     const float lse = empty ? neg_inf() : (m[hb] + fast_log2(l[hb])) * kLn2;
     const size_t row = query_row(b, 0, c, a.H, a.L, a.H);
     const size_t prow = BAL ? (size_t)item * kHG + (c - hc * kHG) : row * a.S + s;
-    float* dst = (n_split == 1) ? a.out + row * kDV : a.o_part + prow * kDV;
+    if (kF16 && n_split > 1) {
+      // fp16 partials: a weighted mean of latent values, inside fp16's range
+      // whenever the latent is
+      uint16_t* dst = (uint16_t*)a.o_part + prow * kDV;
 #pragma unroll
-    for (int db = 0; db < kDB; ++db)
-      *(f32x4_t*)(dst + 16 * db + 4 * lg) = o[db][hb] * inv;
+      for (int db = 0; db < kDB; ++db) {
+        const f32x4_t v = o[db][hb] * inv;
+        *(uint2*)(dst + 16 * db + 4 * lg) = make_uint2(pack_f16(v[0], v[1]),
+                                                        pack_f16(v[2], v[3]));
+      }
+    } else {
+      float* dst = (n_split == 1) ? a.out + row * kDV : a.o_part + prow * kDV;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+        *(f32x4_t*)(dst + 16 * db + 4 * lg) = o[db][hb] * inv;
+    }
     if (lg == 0) {
       if (n_split == 1) {
         if (a.lse) a.lse[row] = lse;
@@ -696,6 +715,7 @@ int mla_groups_per_cu(int d_c) {
   return d_c == 512 ? GeoWide::kGroupsPerCU : GeoNarrow::kGroupsPerCU;
 }
 int mla_tile_rows() { return kTT; }
+bool mla_half_parts(int d_c) { return d_c == 512 ? GeoWide::kF16 : GeoNarrow::kF16; }
 
 namespace {
 template <class G, bool BAL>
