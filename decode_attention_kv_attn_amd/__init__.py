@@ -191,14 +191,14 @@ class _GqaPlan(ctypes.Structure):
                 ("chunk", ctypes.c_int), ("heads_per_item", ctypes.c_int),
                 ("tile_rows", ctypes.c_int), ("waves", ctypes.c_int),
                 ("groups", ctypes.c_longlong), ("workspace_bytes", ctypes.c_size_t),
-                ("balanced_groups", ctypes.c_int)]
+                ("balanced_groups", ctypes.c_int), ("even_split", ctypes.c_int)]
 
 
 def attn_decode_gqa_plan(B, H_q, H_kv, T_cap, d, dtype, window=0, ring=False,
                          n_global=0, num_splits=0, q_len=1):
     """How a GQA decode call would run: dict with kernel ("valu" / "mfma"),
     splits, chunk, heads_per_item, tile_rows, waves, groups, workspace_bytes,
-    balanced_groups."""
+    balanced_groups, even_split."""
     p = _GqaPlan()
     st = library().attn_decode_gqa_plan(B, q_len, H_q, H_kv, T_cap, d, dtype,
                                         window, int(bool(ring)), n_global,
@@ -208,7 +208,7 @@ def attn_decode_gqa_plan(B, H_q, H_kv, T_cap, d, dtype, window=0, ring=False,
             "chunk": p.chunk, "heads_per_item": p.heads_per_item,
             "tile_rows": p.tile_rows, "waves": p.waves, "groups": p.groups,
             "workspace_bytes": p.workspace_bytes,
-            "balanced_groups": p.balanced_groups}
+            "balanced_groups": p.balanced_groups, "even_split": bool(p.even_split)}
 
 
 def attn_decode_workspace_bytes(B, H, d_v, num_splits):

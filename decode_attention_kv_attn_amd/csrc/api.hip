@@ -22,6 +22,22 @@ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Work groups the planner aims for before it cuts the visible range into
 // more splits: one per CU, each a full CU's worth of waves.  Overridable for
 // tuning sweeps through ATTN_DECODE_TARGET_GROUPS.
+// Lead tiles per unit of the even split: the start-up cost of a unit in a
+// work group -- mostly one HBM round trip under load before its first tile
+// can be computed, plus the waves' merge at its end -- in tiles of 32 rows.
+// Measured at d = 128 (MQA, lengths 1k..32k) the best lead is 12 tiles,
+// about 7 us; a tile of width d costs time in proportion to d, so the lead
+// is 1536 / d tiles (overridable for tuning sweeps through
+// ATTN_DECODE_EVEN_LEAD).
+int even_lead(int d) {
+  static const int v = [] {
+    const char* e = getenv("ATTN_DECODE_EVEN_LEAD");
+    const int x = e ? atoi(e) : -1;
+    return x >= 0 && x <= 256 ? x : -1;
+  }();
+  return v >= 0 ? v : max(1, 1536 / d);
+}
+
 int target_groups() {
   static const int v = [] {
     const char* e = getenv("ATTN_DECODE_TARGET_GROUPS");
@@ -41,15 +57,26 @@ struct GqaPlan {
   int tile_rows;    // positions per wave per tile
   size_t ws_bytes;  // workspace needed
   size_t ws_fixed;  // workspace of the fixed splits alone
-  int cap;          // > 0: items of the balanced work list (calls with lengths)
+  int cap;          // > 0: work groups of the balanced list (calls with lengths)
+  int even;         // 1: the list is the even split (matrix-core kernel)
+  int units;        // (KV head, head chunk) units per sequence
 };
 
-// Workspace of a balanced list of `cap` items of N columns: o_part, lse_part
-// and the per-sequence (first item, pieces) pairs.
-size_t balanced_bytes(int cap, int N, int d, int B) {
-  const size_t rows = (size_t)cap * N;
+// Partial slots of a balanced list: one per item of the per-sequence list;
+// the even split needs one per (group, unit) segment, at most groups plus
+// the units of the batch.
+size_t list_slots(const GqaPlan& p, int B) {
+  return p.even ? (size_t)p.cap + (size_t)B * p.units : (size_t)p.cap;
+}
+
+// Workspace of a balanced list: o_part and lse_part (N rows per slot), then
+// the (first slot, pieces) pairs, per sequence or, for the even split, per
+// unit.
+size_t balanced_bytes(const GqaPlan& p, int d, int B) {
+  const size_t rows = list_slots(p, B) * p.N;
+  const size_t pairs = p.even ? (size_t)B * p.units : (size_t)B;
   return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256) +
-         round_up((size_t)B * 2 * sizeof(int), 256);
+         round_up(pairs * 2 * sizeof(int), 256);
 }
 
 // Largest number of positions a non-global query can have visible (a query
@@ -144,10 +171,17 @@ int plan_gqa(int B, int H_q, int H_kv, int T_cap, int d, int dtype, int window,
   // whole ring (or its window), the same for every sequence, and the list's
   // setup (about a microsecond per group) would buy nothing.
   p->cap = 0;
+  p->units = H_kv * p->head_chunks;
+  // the even split numbers tiles of 32 rows with ints: B * units * line
+  // positions per unit (at most T_cap / 32 + 1 tiles plus the lead) must stay
+  // below 2^31
+  p->even = p->mfma && (long long)B * p->units *
+                               (T_cap / mfma_tile_rows() + 1 + even_lead(d)) <
+                           (1LL << 31);
   if (num_splits == 0 && p->S > 1 && !ring && B >= 1 && B <= kBalanceMaxB &&
       target_groups() <= ATTN_MAX_SPLITS) {
     p->cap = target_groups();
-    const size_t bb = balanced_bytes(p->cap, p->N, d, B);
+    const size_t bb = balanced_bytes(*p, d, B);
     if (bb > p->ws_bytes) p->ws_bytes = bb;
   }
   return ATTN_OK;
@@ -197,6 +231,7 @@ int attn_decode_gqa_plan(int B, int q_len, int H_q, int H_kv, int T_cap, int d,
   plan->groups = (long long)B * H_kv * p.head_chunks * p.S;
   plan->workspace_bytes = p.ws_bytes;
   plan->balanced_groups = p.cap;
+  plan->even_split = p.cap > 0 && p.even;
   return ATTN_OK;
 }
 
@@ -323,7 +358,7 @@ int decode_gqa(const void* q, const void* k, const void* v, float* out,
   // whole vectors) and room for its parts; else the fixed splits
   const bool bal = p.cap > 0 && seq_lens && aligned(out, 16) && workspace &&
                    aligned(workspace, 16) &&
-                   workspace_bytes >= balanced_bytes(p.cap, p.N, d, B);
+                   workspace_bytes >= balanced_bytes(p, d, B);
   if (p.S > 1 && !bal) {
     if (!workspace || workspace_bytes < p.ws_fixed) return ATTN_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
@@ -358,11 +393,12 @@ int decode_gqa(const void* q, const void* k, const void* v, float* out,
   a.scale_log2 = scale * 1.4426950408889634f;
   a.o_part = nullptr;
   a.lse_part = nullptr;
-  a.balanced = bal ? 1 : 0;
+  a.balanced = bal ? (p.even ? 2 : 1) : 0;
   a.cap = bal ? p.cap : 0;
+  a.even_lead = even_lead(d);
   a.meta = nullptr;
   if (bal) {
-    const size_t rows = (size_t)p.cap * p.N;
+    const size_t rows = list_slots(p, B) * p.N;
     a.o_part = (float*)workspace;
     a.lse_part = (float*)((char*)workspace + round_up(rows * d * sizeof(float), 256));
     a.meta = (int*)((char*)a.lse_part + round_up(rows * sizeof(float), 256));
@@ -380,7 +416,8 @@ int decode_gqa(const void* q, const void* k, const void* v, float* out,
   if (e != hipSuccess) return ATTN_ERR_HIP;
   if (bal) {
     if (launch_combine_balanced(a.o_part, false, a.lse_part, a.meta, out, lse_out, B, L,
-                                H_q, a.n, p.head_chunks, p.N, d, s) != hipSuccess)
+                                H_q, a.n, p.head_chunks, p.N, d, p.even != 0,
+                                s) != hipSuccess)
       return ATTN_ERR_HIP;
   } else if (p.S > 1) {
     if (launch_combine(a.o_part, a.lse_part, out, lse_out, B * L, H_q, p.S, d, s) !=

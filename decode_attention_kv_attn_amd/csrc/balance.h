@@ -190,4 +190,122 @@ ATTN_DEV WorkItem balanced_item(const int32_t* seq_lens, const int32_t* ring_hea
   return it;
 }
 
+// Even split (GqaArgs::balanced == 2, the matrix-core GQA kernel).  The
+// units' tiles are laid end to end -- sequence after sequence, the U units
+// of a sequence one after another, each unit max(1, ceil(n_b / tile))
+// tiles preceded by `lead` tiles that stand for the fixed cost of starting a
+// unit (loading its queries, refilling the load pipeline, merging the
+// waves) -- and that line is cut into `groups` ranges whose lengths differ
+// by at most one tile, so every work group gets about the same time of work:
+// a group that starts many short units gets fewer rows.  A range may end
+// inside a unit and carry on into the next ones: its group computes one
+// segment per unit whose rows it holds (a range that holds only part of a
+// unit's lead tiles computes nothing for it).  Segment (unit ui, group w)
+// keeps its partial result in slot w + ui.  Two segments never share a
+// slot: w + ui = w' + ui' with w < w' needs ui > ui', but a later group
+// never starts in an earlier unit.  A unit's slots are consecutive (its
+// groups are), and the list needs at most groups + B*U of them.  Every wave
+// derives the plan from seq_lens on its own, like balanced_item.
+struct EvenPlan {
+  int et[kBalanceMaxB / 64];   // tiles per unit of sequence 64 i + lane (-1: none)
+  int pre[kBalanceMaxB / 64];  // line position of that sequence's first unit
+  int len[kBalanceMaxB / 64];  // its stored length
+  int rounds;                  // 64-sequence rounds held
+  int lead;                    // lead tiles per unit
+  int total;                   // line length (>= 1)
+  int groups;                  // ranges, 1 .. cap
+};
+
+// Plan for B <= kBalanceMaxB sequences of U units; at least min_tiles line
+// positions per range (fewer ranges than cap when the work is small).  The
+// caller guarantees that B * U * (T_cap / tile + 1 + lead) fits an int.
+ATTN_DEV EvenPlan even_plan(const int32_t* seq_lens, int B, int T_cap, int window,
+                            const int32_t* gpos, int n_global, int U, int cap,
+                            int tile, int lead, int min_tiles) {
+  constexpr int kPer = kBalanceMaxB / 64;
+  const int lane = __lane_id();
+  EvenPlan p;
+  p.rounds = (B + 63) >> 6;
+  p.lead = lead;
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int b = 64 * i + lane;
+    p.et[i] = -1;
+    p.len[i] = 0;
+    p.pre[i] = 0;
+    if (i < p.rounds) {  // uniform
+      int e = 0;
+      if (b < B) {
+        p.len[i] = seq_lens[b];
+        const int n = visible_range_of(p.len[i], false, 0, T_cap, window, gpos,
+                                       n_global).n;
+        e = max(1, (n + tile - 1) / tile);
+        p.et[i] = e;
+      }
+      const int w = b < B ? (e + lead) * U : 0;
+      const int incl = wave_incl_scan_i(w);
+      p.pre[i] = base + incl - w;
+      base += __builtin_amdgcn_readlane(incl, 63);
+    }
+  }
+  p.total = base;
+  p.groups = max(1, min(cap, base / max(1, min_tiles)));
+  return p;
+}
+
+// Line position where range w starts (w = groups gives the end of the line).
+ATTN_DEV int even_start(const EvenPlan& p, int w) {
+  return (int)((long long)w * p.total / p.groups);
+}
+
+// The range holding line position x: the largest w with even_start(w) <= x.
+ATTN_DEV int even_group_of(const EvenPlan& p, int x) {
+  return (int)(((long long)(x + 1) * p.groups - 1) / p.total);
+}
+
+struct EvenSeg {
+  int b, len;      // sequence and its stored length
+  int u;           // unit of the sequence
+  int t0, t1;      // the unit's tiles [t0, t1) in this range (t0 == t1: none)
+  int next;        // line position after this segment
+  int first, last; // the ranges holding the unit's first and last tiles
+};
+
+// The segment that starts at line position x, inside a range ending at x1.
+ATTN_DEV EvenSeg even_segment(const EvenPlan& p, int U, int x, int x1) {
+  constexpr int kPer = kBalanceMaxB / 64;
+  EvenSeg sg;
+  sg.b = 0;
+  sg.len = 0;
+  int pre = 0, et = 1;
+  // the starts grow with b, so the sequences starting at or before x are a
+  // prefix: the last one holds x
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (i < p.rounds) {
+      const unsigned long long bal = __ballot(p.et[i] >= 0 && p.pre[i] <= x);
+      if (bal) {
+        const int src = 63 - __clzll((long long)bal);
+        sg.b = 64 * i + src;
+        pre = __builtin_amdgcn_readlane(p.pre[i], src);
+        et = __builtin_amdgcn_readlane(p.et[i], src);
+        sg.len = __builtin_amdgcn_readlane(p.len[i], src);
+      }
+    }
+  }
+  const int span = et + p.lead;  // line positions per unit
+  const int off = x - pre;
+  sg.u = off / span;
+  const int ustart = pre + sg.u * span;  // the unit's lead tiles start here
+  const int rstart = ustart + p.lead;    // its tiles start here
+  const int uend = ustart + span;
+  sg.next = min(x1, uend);
+  sg.t0 = max(x, rstart) - rstart;
+  sg.t1 = max(sg.next, rstart) - rstart;
+  sg.first = even_group_of(p, rstart);
+  sg.last = even_group_of(p, uend - 1);
+  return sg;
+}
+
 }  // namespace attn

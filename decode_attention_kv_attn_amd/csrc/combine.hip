@@ -126,13 +126,17 @@ ATTN_DEV void fma_vec(float (&acc)[N], float w, const typename VecOf<P, N>::type
   for (int i = 0; i < N; ++i) acc[i] = add_part(acc[i], w, (float)xs[i]);
 }
 
-// Balanced work list (both GQA kernels): output row
-// (b * L + token) * H_q + head belongs to column c = (head % n) * L + token of
-// KV head head / n, i.e. column c % nh of head chunk c / nh; piece s of it is
-// item meta[2b] + (g * k + s) * hc + c / nh with k = meta[2b + 1].
+// Balanced work lists: output row (b * L + token) * H_q + head belongs to
+// column c = (head % n) * L + token of KV head g = head / n, i.e. column
+// c % nh of head chunk c / nh.  Per-sequence list (both GQA kernels, MLA):
+// piece s of it is item meta[2b] + (g * k + s) * hc + c / nh with k =
+// meta[2b + 1].  Even split (per_unit, the matrix-core GQA kernel): unit
+// ui = (b * H_kv + g) * hc + c / nh has k = meta[2ui + 1] pieces in the
+// consecutive slots from meta[2ui].  Each slot holds nh rows.
 struct BalancedMap {
   const int* meta;
   int L, H_q, n, hc, nh;
+  int per_unit;
 };
 
 // CPL = d_v / 64 columns per lane, read as CPL / VW vectors of VW elements of
@@ -172,13 +176,21 @@ __global__ __launch_bounds__(kThreads) void lse_combine_rows(
     const int b = (int)(row / per_b);
     const int rem = (int)(row - (size_t)b * per_b);
     const int tok = rem / bm.H_q, head = rem - tok * bm.H_q;
-    S = bm.meta[2 * b + 1];
-    if (S == 1) return;  // one piece: the decode kernel wrote this row
     const int g = head / bm.n;
     const int c = (head - g * bm.n) * bm.L + tok;
     const int chunk = c / bm.nh;
-    base = (size_t)(bm.meta[2 * b] + g * S * bm.hc + chunk) * bm.nh + (c - chunk * bm.nh);
-    stride = bm.hc * bm.nh;
+    if (bm.per_unit) {
+      const int ui = (b * (bm.H_q / bm.n) + g) * bm.hc + chunk;
+      S = bm.meta[2 * ui + 1];
+      if (S == 1) return;  // one piece: the decode kernel wrote this row
+      base = (size_t)bm.meta[2 * ui] * bm.nh + (c - chunk * bm.nh);
+      stride = bm.nh;
+    } else {
+      S = bm.meta[2 * b + 1];
+      if (S == 1) return;
+      base = (size_t)(bm.meta[2 * b] + g * S * bm.hc + chunk) * bm.nh + (c - chunk * bm.nh);
+      stride = bm.hc * bm.nh;
+    }
   }
   if constexpr (WPR == 1) {
     if (!active) return;
@@ -341,11 +353,11 @@ hipError_t launch_combine_balanced(const void* o_part, bool half_parts,
                                    const float* lse_part, const int* meta, float* out,
                                    float* lse, int B, int L, int H_q, int n,
                                    int head_chunks, int heads_per_item, int d_v,
-                                   hipStream_t stream) {
+                                   bool per_unit, hipStream_t stream) {
   if ((uintptr_t)o_part % 16 != 0 || (uintptr_t)out % 16 != 0 || d_v % 64 != 0 ||
       d_v > 512)
     return hipErrorInvalidValue;
-  const BalancedMap bm{meta, L, H_q, n, head_chunks, heads_per_item};
+  const BalancedMap bm{meta, L, H_q, n, head_chunks, heads_per_item, per_unit ? 1 : 0};
   if (half_parts)
     return launch_rows<_Float16, true, 1>(d_v / 64, (const _Float16*)o_part, lse_part, out,
                                           lse, B * L * H_q, 0, bm, stream);

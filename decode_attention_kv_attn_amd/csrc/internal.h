@@ -39,15 +39,19 @@ struct GqaArgs {
   int chunk;        // positions per split
   int xcd_remap;    // 1: map consecutive work items onto one XCD
   float scale_log2; // softmax scale * log2(e)
-  // Balanced work list (both kernels): work item w is item w of
-  // the list by visible rows (balance.h) instead of a fixed split; pieces of
-  // a sequence's units go to o_part / lse_part row w * heads_per_item + column,
-  // and meta[2b], meta[2b+1] receive the sequence's first item and its pieces
-  // per unit.  A sequence cut into one piece per unit is written to out / lse
+  // Balanced work lists (balance.h).  1, both kernels: work item w is item w
+  // of the per-sequence list by visible rows instead of a fixed split; pieces
+  // of a sequence's units go to o_part / lse_part row w * heads_per_item +
+  // column, and meta[2b], meta[2b+1] receive the sequence's first item and
+  // its pieces per unit.  2, the matrix-core kernel: the even split; the
+  // segment of unit ui in work group w goes to slot w + ui (rows slot *
+  // heads_per_item + column), and meta[2ui], meta[2ui+1] receive the unit's
+  // first slot and its pieces.  A unit in one piece is written to out / lse
   // directly.
   int balanced;
   int cap;          // items the list may hold (the grid)
-  int* meta;        // [B, 2]
+  int even_lead;    // even split: lead tiles per unit (its start-up cost)
+  int* meta;        // [B, 2] (list 1) or [B * units per sequence, 2] (list 2)
 };
 
 // Per-instantiation geometry of the VALU kernel, reported to the planner.
@@ -111,14 +115,15 @@ hipError_t launch_combine(const float* o_part, const float* lse_part,
 
 // Merge of a balanced work list's pieces (GqaArgs::balanced): output row
 // (b * L + token) * H_q + head, for heads_per_item columns per item and
-// head_chunks items per KV head; rows whose sequence has one piece per unit
-// are left as the decode kernel wrote them.  o_part (float32, or fp16 when
+// head_chunks items per KV head; rows whose unit has one piece are left as
+// the decode kernel wrote them.  per_unit: the even split's meta (one pair
+// per unit), else the per-sequence list's.  o_part (float32, or fp16 when
 // half_parts) and out 16-byte aligned, d_v in {64, 128, 256, 512}.
 hipError_t launch_combine_balanced(const void* o_part, bool half_parts,
                                    const float* lse_part, const int* meta, float* out,
                                    float* lse, int B, int L, int H_q, int n,
                                    int head_chunks, int heads_per_item, int d_v,
-                                   hipStream_t stream);
+                                   bool per_unit, hipStream_t stream);
 
 // launch_combine with fp16 partial values (o_part [B, H, S, d_v] of _Float16,
 // 16-byte aligned; d_v a multiple of 64 up to 512).

@@ -149,7 +149,8 @@ int decode_mla(const void* q, const void* latent, float* out, float* lse_out,
   if (bal) {
     // columns are (head, token) pairs of one latent: n = H heads share it
     if (attn::launch_combine_balanced(o_part, half, lse_part, meta, out, lse_out, B, L,
-                                      H, H, p.head_chunks, hg, d_c, s) != hipSuccess)
+                                      H, H, p.head_chunks, hg, d_c, false,
+                                      s) != hipSuccess)
       return ATTN_ERR_HIP;
   } else if (p.S > 1) {
     const hipError_t e =

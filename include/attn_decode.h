@@ -109,9 +109,9 @@ enum {
  *             Contents on entry are ignored.  When the library picks the
  *             splits and the batch has fewer (sequence, KV head) units than
  *             work groups, a call with seq_lens assigns pieces by visible
- *             length instead (attn_gqa_plan.balanced_groups); a workspace
- *             smaller than that size but large enough for the fixed splits
- *             runs the fixed splits.
+ *             length instead (attn_gqa_plan.balanced_groups, and
+ *             .even_split for how); a workspace smaller than that size but
+ *             large enough for the fixed splits runs the fixed splits.
  *   stream    hipStream_t.
  */
 int attn_decode_gqa(const void* q, const void* k, const void* v, float* out,
@@ -176,11 +176,16 @@ typedef struct {
   long long groups;    /* work groups of the decode kernel                   */
   size_t workspace_bytes; /* workspace the call needs (0: none)              */
   int balanced_groups; /* > 0: a call that passes seq_lens (with out 16-byte
-                        * aligned and this workspace) cuts each sequence's
-                        * visible rows by its own length into pieces of one
-                        * common size, over at most this many work groups,
-                        * instead of `splits` fixed pieces; 0: never (also
-                        * for rings, whose visible ranges are alike)        */
+                        * aligned and this workspace) cuts the visible rows
+                        * by their lengths over at most this many work
+                        * groups instead of `splits` fixed pieces; 0: never
+                        * (also for rings, whose visible ranges are alike)  */
+  int even_split;      /* with balanced_groups > 0: 1 = every work group
+                        * takes the same number of 32-row tiles of the
+                        * batch's rows laid end to end (a group may finish
+                        * one sequence and start the next: matrix-core
+                        * kernel); 0 = each sequence is cut into pieces of
+                        * one common size, at least one per sequence       */
 } attn_gqa_plan;
 
 /* Fills *plan for these arguments: q_len query tokens per sequence (1 for

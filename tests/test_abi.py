@@ -159,8 +159,15 @@ def test_planner(lib):
         if S > 1 and not ring and B <= 256:
             assert cap > 0
         up = lambda x: -(-x // 256) * 256
-        rows = cap * plan["heads_per_item"]
-        bal = up(rows * d * 4) + up(rows * 4) + up(B * 8) if cap else 0
+        # the even split (matrix-core kernel) keeps a slot per (group, unit)
+        # segment, at most cap + B * units, and a pair per unit; the
+        # per-sequence list a slot per group and a pair per sequence
+        units = H_kv * -(-H_q // H_kv // plan["heads_per_item"])
+        assert plan["even_split"] == (cap > 0 and plan["kernel"] == "mfma")
+        slots = cap + B * units if plan["even_split"] else cap
+        pairs = B * units if plan["even_split"] else B
+        rows = slots * plan["heads_per_item"]
+        bal = up(rows * d * 4) + up(rows * 4) + up(pairs * 8) if cap else 0
         assert ws == max(fixed, bal) == plan["workspace_bytes"]
     for S in (1, 2, 7, 64, 1024):
         got = lib.attn_decode_gqa_splits(4, 16, 4, 2000, 128, 1, 0, 0, S)

@@ -2,9 +2,12 @@
 
 When the library picks the splits and a batch has fewer (sequence, KV head)
 units than work groups, a call that passes lengths cuts each sequence's
-visible rows by its own length (pieces of one common size, at least one per
-sequence) instead of cutting every sequence into the same number of fixed
-pieces.  The list is derived on the device from seq_lens, so these tests
+visible rows by its own length instead of cutting every sequence into the
+same number of fixed pieces: the vector kernel takes pieces of one common
+size (at least one per sequence); the matrix-core kernel lays the units'
+32-row tiles end to end and gives every work group the same number of them
+(the even split), so one group may finish a sequence and start the next
+ones.  The lists are derived on the device from seq_lens, so these tests
 cover its edges: empty and one-row sequences, a single long sequence among
 empty ones, every sequence in one piece, the most sequences the list takes
 (four per lane), two head chunks per KV head, several query tokens, global
@@ -62,6 +65,8 @@ def test_length_mixes(d, H_q, H_kv, mix):
     T = 2048
     assert _balanced(len(lens), H_q, H_kv, T, d)
     q, k, v, sl = _inputs(lens, H_q, H_kv, T, d, 12000 + d + H_q + len(mix))
+    plan = L.attn_decode_gqa_plan(len(lens), H_q, H_kv, T, d, 1)
+    assert plan["even_split"] == (plan["kernel"] == "mfma")
     out, lse = L.attn_decode_gqa(q, k, v, sl)
     torch.cuda.synchronize()
     ro, rl = oracle.gqa_decode_ref(q, k, v, sl)
@@ -74,6 +79,45 @@ def test_length_mixes(d, H_q, H_kv, mix):
     out2, _ = L.attn_decode_gqa(q, k, v, sl, num_splits=S)
     torch.cuda.synchronize()
     assert_parity(out2, ro, f"fixed {mix}")
+
+
+EVEN_MIXES = {
+    # groups that cross many short units, units that span many groups
+    "short_and_long": [3000, 5, 0, 40, 2500, 31, 32, 33, 1, 4096, 64, 65] * 4,
+    # every unit a single tile: each group covers several whole units
+    "one_tile_each": [32] * 40 + [1] * 20 + [0] * 4,
+    # one unit over every group but a few empty ones
+    "one_over_all": [0, 0, 4096, 0, 0],
+}
+
+
+@pytest.mark.parametrize("mix", list(EVEN_MIXES))
+@pytest.mark.parametrize("H_q,H_kv,d", [(32, 2, 128), (64, 1, 64)],
+                         ids=["16x2-d128", "64x1-d64-two-chunks"])
+def test_even_split_segments(mix, H_q, H_kv, d):
+    """The even split's segments: one work group computes pieces of several
+    (sequence, KV head, head chunk) units, each into its own slot, and a long
+    unit's pieces come from consecutive groups; a second call on the same
+    workspace with other lengths must not see the first call's slots or
+    pairs."""
+    lens = EVEN_MIXES[mix]
+    B, T = len(lens), 4096
+    plan = L.attn_decode_gqa_plan(B, H_q, H_kv, T, d, 1)
+    assert plan["kernel"] == "mfma" and plan["even_split"] and plan["balanced_groups"] > 0
+    q, k, v, sl = _inputs(lens, H_q, H_kv, T, d, 31000 + B + H_q + d)
+    ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=DEV)
+    out, lse = L.attn_decode_gqa(q, k, v, sl, workspace=ws)
+    torch.cuda.synchronize()
+    ro, rl = oracle.gqa_decode_ref(q, k, v, sl)
+    assert_parity(out, ro, f"even split {mix}")
+    assert_lse(lse, rl, f"even split {mix}")
+    # other lengths, same workspace
+    sl2 = torch.flip(sl, [0]).contiguous()
+    out2, lse2 = L.attn_decode_gqa(q, k, v, sl2, workspace=ws)
+    torch.cuda.synchronize()
+    ro2, rl2 = oracle.gqa_decode_ref(q, k, v, sl2)
+    assert_parity(out2, ro2, f"even split {mix}, second call")
+    assert_lse(lse2, rl2, f"even split {mix}, second call")
 
 
 def test_fp32_vector_kernel():
