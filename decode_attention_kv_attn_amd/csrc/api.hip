@@ -175,7 +175,9 @@ int plan_gqa(int B, int H_q, int H_kv, int T_cap, int d, int dtype, int window,
   // the even split numbers tiles of 32 rows with ints: B * units * line
   // positions per unit (at most T_cap / 32 + 1 tiles plus the lead) must stay
   // below 2^31
-  p->even = p->mfma && (long long)B * p->units *
+  // (d = 256 keeps the per-sequence list: the segment loop would push that
+  // instantiation, already at the register limit, into spills)
+  p->even = p->mfma && d <= 128 && (long long)B * p->units *
                                (T_cap / mfma_tile_rows() + 1 + even_lead(d)) <
                            (1LL << 31);
   if (num_splits == 0 && p->S > 1 && !ring && B >= 1 && B <= kBalanceMaxB &&

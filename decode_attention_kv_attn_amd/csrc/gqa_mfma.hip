@@ -525,10 +525,13 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
 
 template <int DK, int DV, int NH, int MODE>
 hipError_t launch_one(const GqaArgs& a, int grid, hipStream_t st) {
-  if (a.balanced == 2)
-    hipLaunchKernelGGL((gqa_decode_mfma<DK, DV, NH, MODE, 2>), dim3(grid),
-                       dim3(kNW * 64), 0, st, a);
-  else if (a.balanced)
+  if (a.balanced == 2) {
+    // the even split runs at d <= 128 only (the planner's choice)
+    if constexpr (DK > 128) return hipErrorInvalidValue;
+    else
+      hipLaunchKernelGGL((gqa_decode_mfma<DK, DV, NH, MODE, 2>), dim3(grid),
+                         dim3(kNW * 64), 0, st, a);
+  } else if (a.balanced)
     hipLaunchKernelGGL((gqa_decode_mfma<DK, DV, NH, MODE, 1>), dim3(grid),
                        dim3(kNW * 64), 0, st, a);
   else

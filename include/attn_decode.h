@@ -184,8 +184,9 @@ typedef struct {
                         * takes the same number of 32-row tiles of the
                         * batch's rows laid end to end (a group may finish
                         * one sequence and start the next: matrix-core
-                        * kernel); 0 = each sequence is cut into pieces of
-                        * one common size, at least one per sequence       */
+                        * kernel, d <= 128); 0 = each sequence is cut into
+                        * pieces of one common size, at least one per
+                        * sequence                                         */
 } attn_gqa_plan;
 
 /* Fills *plan for these arguments: q_len query tokens per sequence (1 for

@@ -163,7 +163,7 @@ def test_planner(lib):
         # segment, at most cap + B * units, and a pair per unit; the
         # per-sequence list a slot per group and a pair per sequence
         units = H_kv * -(-H_q // H_kv // plan["heads_per_item"])
-        assert plan["even_split"] == (cap > 0 and plan["kernel"] == "mfma")
+        assert plan["even_split"] == (cap > 0 and plan["kernel"] == "mfma" and d <= 128)
         slots = cap + B * units if plan["even_split"] else cap
         pairs = B * units if plan["even_split"] else B
         rows = slots * plan["heads_per_item"]

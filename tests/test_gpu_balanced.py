@@ -66,7 +66,7 @@ def test_length_mixes(d, H_q, H_kv, mix):
     assert _balanced(len(lens), H_q, H_kv, T, d)
     q, k, v, sl = _inputs(lens, H_q, H_kv, T, d, 12000 + d + H_q + len(mix))
     plan = L.attn_decode_gqa_plan(len(lens), H_q, H_kv, T, d, 1)
-    assert plan["even_split"] == (plan["kernel"] == "mfma")
+    assert plan["even_split"] == (plan["kernel"] == "mfma" and d <= 128)
     out, lse = L.attn_decode_gqa(q, k, v, sl)
     torch.cuda.synchronize()
     ro, rl = oracle.gqa_decode_ref(q, k, v, sl)
