@@ -259,11 +259,6 @@ ATTN_DEV int even_start(const EvenPlan& p, int w) {
   return (int)((long long)w * p.total / p.groups);
 }
 
-// The range holding line position x: the largest w with even_start(w) <= x.
-ATTN_DEV int even_group_of(const EvenPlan& p, int x) {
-  return (int)(((long long)(x + 1) * p.groups - 1) / p.total);
-}
-
 struct EvenSeg {
   int b, len;      // sequence and its stored length
   int u;           // unit of the sequence
@@ -272,13 +267,15 @@ struct EvenSeg {
   int first, last; // the ranges holding the unit's first and last tiles
 };
 
+// The segment of sequence b (its first unit at line position pre, et tiles
+// per unit) that starts at line position x, inside a range ending at x1.
+ATTN_DEV EvenSeg even_cut(int groups, int total, int lead, int b, int len, int pre,
+                          int et, int x, int x1);
+
 // The segment that starts at line position x, inside a range ending at x1.
-ATTN_DEV EvenSeg even_segment(const EvenPlan& p, int U, int x, int x1) {
+ATTN_DEV EvenSeg even_segment(const EvenPlan& p, int x, int x1) {
   constexpr int kPer = kBalanceMaxB / 64;
-  EvenSeg sg;
-  sg.b = 0;
-  sg.len = 0;
-  int pre = 0, et = 1;
+  int b = 0, len = 0, pre = 0, et = 1;
   // the starts grow with b, so the sequences starting at or before x are a
   // prefix: the last one holds x
 #pragma unroll
@@ -287,24 +284,87 @@ ATTN_DEV EvenSeg even_segment(const EvenPlan& p, int U, int x, int x1) {
       const unsigned long long bal = __ballot(p.et[i] >= 0 && p.pre[i] <= x);
       if (bal) {
         const int src = 63 - __clzll((long long)bal);
-        sg.b = 64 * i + src;
+        b = 64 * i + src;
         pre = __builtin_amdgcn_readlane(p.pre[i], src);
         et = __builtin_amdgcn_readlane(p.et[i], src);
-        sg.len = __builtin_amdgcn_readlane(p.len[i], src);
+        len = __builtin_amdgcn_readlane(p.len[i], src);
       }
     }
   }
-  const int span = et + p.lead;  // line positions per unit
+  return even_cut(p.groups, p.total, p.lead, b, len, pre, et, x, x1);
+}
+
+// The same plan with its per-sequence arrays in LDS, for kernels whose
+// registers are taken: 3 * kBalanceMaxB ints (tiles per unit, first line
+// position, stored length).  Every wave writes the same values and reads back
+// only what it wrote itself, so no barrier is needed.
+struct EvenPlanLds {
+  const int* lds;
+  int B, rounds, lead, total, groups;
+};
+
+ATTN_DEV EvenPlanLds even_plan_lds(const int32_t* seq_lens, int B, int T_cap, int window,
+                                   const int32_t* gpos, int n_global, int U, int cap,
+                                   int tile, int lead, int min_tiles, int* lds) {
+  constexpr int kPer = kBalanceMaxB / 64;
+  const EvenPlan p = even_plan(seq_lens, B, T_cap, window, gpos, n_global, U, cap, tile,
+                               lead, min_tiles);
+  const int lane = __lane_id();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (i < p.rounds) {
+      lds[64 * i + lane] = p.et[i];
+      lds[kBalanceMaxB + 64 * i + lane] = p.pre[i];
+      lds[2 * kBalanceMaxB + 64 * i + lane] = p.len[i];
+    }
+  }
+  return EvenPlanLds{lds, B, p.rounds, p.lead, p.total, p.groups};
+}
+
+ATTN_DEV int even_start(const EvenPlanLds& p, int w) {
+  return (int)((long long)w * p.total / p.groups);
+}
+
+ATTN_DEV EvenSeg even_segment(const EvenPlanLds& p, int x, int x1) {
+  constexpr int kPer = kBalanceMaxB / 64;
+  const int lane = __lane_id();
+  int b = 0, len = 0, pre = 0, et = 1;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (i < p.rounds) {
+      const int e = p.lds[64 * i + lane];
+      const int pr = p.lds[kBalanceMaxB + 64 * i + lane];
+      const unsigned long long bal = __ballot(e >= 0 && pr <= x);
+      if (bal) {
+        const int src = 63 - __clzll((long long)bal);
+        b = 64 * i + src;
+        pre = __builtin_amdgcn_readlane(pr, src);
+        et = __builtin_amdgcn_readlane(e, src);
+        len = __builtin_amdgcn_readlane(p.lds[2 * kBalanceMaxB + 64 * i + lane], src);
+      }
+    }
+  }
+  return even_cut(p.groups, p.total, p.lead, b, len, pre, et, x, x1);
+}
+
+ATTN_DEV EvenSeg even_cut(int groups, int total, int lead, int b, int len, int pre,
+                          int et, int x, int x1) {
+  // the range holding line position y: the largest w with start(w) <= y
+  auto group_of = [&](int y) { return (int)(((long long)(y + 1) * groups - 1) / total); };
+  EvenSeg sg;
+  sg.b = b;
+  sg.len = len;
+  const int span = et + lead;  // line positions per unit
   const int off = x - pre;
   sg.u = off / span;
   const int ustart = pre + sg.u * span;  // the unit's lead tiles start here
-  const int rstart = ustart + p.lead;    // its tiles start here
+  const int rstart = ustart + lead;      // its tiles start here
   const int uend = ustart + span;
   sg.next = min(x1, uend);
   sg.t0 = max(x, rstart) - rstart;
   sg.t1 = max(sg.next, rstart) - rstart;
-  sg.first = even_group_of(p, rstart);
-  sg.last = even_group_of(p, uend - 1);
+  sg.first = group_of(rstart);
+  sg.last = group_of(uend - 1);
   return sg;
 }
 

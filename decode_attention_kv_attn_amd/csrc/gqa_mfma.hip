@@ -454,7 +454,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_mfma(GqaArgs a) {
     int x = even_start(ep, item);
     bool first = true;
     while (x < x1) {
-      const EvenSeg sg = even_segment(ep, U, x, x1);
+      const EvenSeg sg = even_segment(ep, x, x1);
       x = sg.next;
       if (sg.t1 == sg.t0) continue;  // only lead tiles of this unit
       if (!first) __syncthreads();  // the last segment's merge reads are done

@@ -92,13 +92,17 @@ bool mla_half_parts(int d_c);
 // DK = d_c + 64; block_table == nullptr: dense latent [B, T_cap, DK]; else a
 // page pool [num_pages, 2^page_shift, DK] with T_cap = max_pages <<
 // page_shift, and `chunk` a multiple of the tile rows.
+// balanced: 0 fixed splits, 1 the per-sequence list, 2 the even split
+// (only where mla_even_split(d_c); even_lead as GqaArgs::even_lead).
 hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
                            float* lse, float* o_part, float* lse_part,
                            const int32_t* seq_lens, const int32_t* block_table,
                            int max_pages, int page_shift, int num_pages, int B,
                            int L, int H, int T_cap, int d_c, int S, int chunk,
                            int head_chunks, int balanced, int cap, int* meta,
-                           float scale_log2, hipStream_t stream);
+                           int even_lead, float scale_log2, hipStream_t stream);
+// true where the geometry of latent width d_c runs the even split
+bool mla_even_split(int d_c);
 
 }  // namespace attn
 

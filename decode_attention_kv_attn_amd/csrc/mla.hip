@@ -24,16 +24,41 @@ struct MlaPlan {
   size_t ws_bytes;  // the larger of the two workspaces below
   size_t ws_fixed;  // fixed splits
   int cap;          // > 0: groups of the balanced list (calls with lengths)
+  int even;         // 1: the list is the even split (one unit per head chunk)
 };
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Balanced list over `cap` groups of hg columns: o_part, lse_part and the
-// per-sequence (first item, pieces) pairs.
-size_t mla_balanced_bytes(int cap, int hg, int d_c, int B) {
-  const size_t rows = (size_t)cap * hg;
+// Lead tiles per unit of the MLA even split: a segment's start (the query
+// fragments of 128 heads, three tiles of loads before the first tile can be
+// computed, the merge-ready partials at its end), and the cost of segments
+// only a few tiles long.  Swept on B=64 with lengths 1k..8k (us per step):
+// lead 0 138.0, 2 135.9, 4 132.2, 8 128.6, 12 128.0, 16 130.2, 24 133.1,
+// against 131.4 for the per-sequence list (overridable for tuning sweeps
+// through ATTN_DECODE_MLA_EVEN_LEAD).
+int mla_even_lead() {
+  static const int v = [] {
+    const char* e = getenv("ATTN_DECODE_MLA_EVEN_LEAD");
+    const int x = e ? atoi(e) : -1;
+    return x >= 0 && x <= 256 ? x : 12;
+  }();
+  return v;
+}
+
+// Partial slots of the balanced list: one per group of the per-sequence
+// list; one per (group, unit) segment of the even split, at most cap + B
+// units.
+size_t mla_slots(const MlaPlan& p, int B) {
+  return p.even ? (size_t)p.cap + (size_t)B * p.head_chunks : (size_t)p.cap;
+}
+
+// Balanced list: o_part, lse_part (hg rows per slot) and the (first slot,
+// pieces) pairs, per sequence or, for the even split, per unit.
+size_t mla_balanced_bytes(const MlaPlan& p, int hg, int d_c, int B) {
+  const size_t rows = mla_slots(p, B) * hg;
+  const size_t pairs = p.even ? (size_t)B * p.head_chunks : (size_t)B;
   return round_up(rows * d_c * sizeof(float), 256) + round_up(rows * sizeof(float), 256) +
-         round_up((size_t)B * 2 * sizeof(int), 256);
+         round_up(pairs * 2 * sizeof(int), 256);
 }
 
 int plan_mla(int B, int H, int T_cap, int d_c, int d_rope, int num_splits,
@@ -69,11 +94,15 @@ int plan_mla(int B, int H, int T_cap, int d_c, int d_rope, int num_splits,
   // balanced list: when the fixed plan splits, a call with lengths cuts each
   // sequence by its own length into pieces of one common size (balance.h)
   p->cap = 0;
+  // the even split (where the geometry runs it) numbers 32-row tiles plus
+  // lead tiles of every unit with ints
+  p->even = attn::mla_even_split(d_c) &&
+            (long long)B * p->head_chunks * (T_cap / tr + 1 + mla_even_lead()) < (1LL << 31);
   const int cap = attn::kNumCUs * attn::mla_groups_per_cu(d_c);
   if (num_splits == 0 && p->S > 1 && B >= 1 && B <= attn::kBalanceMaxB &&
       (long long)B * p->head_chunks < cap && cap <= ATTN_MAX_SPLITS) {
     p->cap = cap;
-    const size_t bb = mla_balanced_bytes(cap, hg, d_c, B);
+    const size_t bb = mla_balanced_bytes(*p, hg, d_c, B);
     if (bb > p->ws_bytes) p->ws_bytes = bb;
   }
   return ATTN_OK;
@@ -123,10 +152,13 @@ int decode_mla(const void* q, const void* latent, float* out, float* lse_out,
   int* meta = nullptr;
   const int hg = attn::mla_heads_per_group(d_c);
   // balanced list: lengths given and room for its parts; else fixed splits
+  // the even split takes one query token per sequence; several tokens keep
+  // the per-sequence list, whose parts fit in the same workspace
+  if (L > 1) p.even = 0;
   const bool bal = p.cap > 0 && seq_lens && workspace && aligned(workspace, 16) &&
-                   workspace_bytes >= mla_balanced_bytes(p.cap, hg, d_c, B);
+                   workspace_bytes >= mla_balanced_bytes(p, hg, d_c, B);
   if (bal) {
-    const size_t rows = (size_t)p.cap * hg;
+    const size_t rows = mla_slots(p, B) * hg;
     o_part = (float*)workspace;
     lse_part = (float*)((char*)workspace + round_up(rows * d_c * sizeof(float), 256));
     meta = (int*)((char*)lse_part + round_up(rows * sizeof(float), 256));
@@ -141,15 +173,16 @@ int decode_mla(const void* q, const void* latent, float* out, float* lse_out,
   hipStream_t s = (hipStream_t)stream;
   if (attn::launch_mla_mfma(q, latent, out, lse_out, o_part, lse_part, seq_lens,
                             block_table, max_pages, page_shift, num_pages, B, L, H,
-                            T_cap, d_c, p.S, p.chunk, p.head_chunks, bal ? 1 : 0,
-                            bal ? p.cap : 0, meta, scale * 1.4426950408889634f,
+                            T_cap, d_c, p.S, p.chunk, p.head_chunks,
+                            bal ? (p.even ? 2 : 1) : 0, bal ? p.cap : 0, meta,
+                            mla_even_lead(), scale * 1.4426950408889634f,
                             s) != hipSuccess)
     return ATTN_ERR_HIP;
   const bool half = attn::mla_half_parts(d_c);
   if (bal) {
     // columns are (head, token) pairs of one latent: n = H heads share it
     if (attn::launch_combine_balanced(o_part, half, lse_part, meta, out, lse_out, B, L,
-                                      H, H, p.head_chunks, hg, d_c, false,
+                                      H, H, p.head_chunks, hg, d_c, p.even != 0,
                                       s) != hipSuccess)
       return ATTN_ERR_HIP;
   } else if (p.S > 1) {

@@ -371,6 +371,39 @@ def test_mla_length_mixes(d_c, H, mix):
     assert_parity(zf, rz, f"mla fixed {mix}")
 
 
+@pytest.mark.parametrize("mix", list(EVEN_MIXES))
+def test_mla_even_split_segments(mix):
+    """The (512, 64) geometry runs the even split for one token per sequence:
+    a group may compute pieces of several sequences, each restarting the
+    group's tile pipeline; dense and paged pools give the same bits, and a
+    second call on the same workspace with other lengths must not see the
+    first call's slots or pairs."""
+    from test_gpu_paged import _latent_pool
+    lens = EVEN_MIXES[mix]
+    B, T, H, dk = len(lens), 4096, 128, 576
+    q = synth.draw((B, H, dk), 13200 + B, "bf16", DEV, dk ** -0.5)
+    lat = synth.draw((B, T, dk), 13201 + B, "bf16", DEV, dk ** -0.5)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    scale = 192 ** -0.5
+    ws = torch.empty(L.attn_decode_mla_workspace_bytes(B, H, T, 512, 64),
+                     dtype=torch.uint8, device=DEV)
+    z, lse = L.attn_decode_mla(q, lat, 512, scale, sl, workspace=ws)
+    torch.cuda.synchronize()
+    rz, rl = oracle.mla_decode_ref(q, lat, 512, scale, sl)
+    assert_parity(z, rz, f"mla even split {mix}")
+    assert_lse(lse, rl, f"mla even split {mix}")
+    pool, table = _latent_pool(lat, 64, 13202 + B, poison=True)
+    zp, lp = L.attn_decode_mla_paged(q, pool, table, 512, scale, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(zp, z) and torch.equal(lp, lse)
+    sl2 = torch.flip(sl, [0]).contiguous()
+    z2, l2 = L.attn_decode_mla(q, lat, 512, scale, sl2, workspace=ws)
+    torch.cuda.synchronize()
+    rz2, rl2 = oracle.mla_decode_ref(q, lat, 512, scale, sl2)
+    assert_parity(z2, rz2, f"mla even split {mix}, second call")
+    assert_lse(l2, rl2, f"mla even split {mix}, second call")
+
+
 def test_mla_paged_and_multi_token():
     """Paged latent pool (16-position pages): the same bits as the dense
     cache; three query tokens per sequence (three head chunks at 128 heads)
