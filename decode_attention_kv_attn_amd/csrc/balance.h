@@ -190,7 +190,8 @@ ATTN_DEV WorkItem balanced_item(const int32_t* seq_lens, const int32_t* ring_hea
   return it;
 }
 
-// Even split (GqaArgs::balanced == 2, the matrix-core GQA kernel).  The
+// Even split (balanced == 2: the matrix-core GQA kernel at d <= 128, and the
+// MLA kernel's 512 + 64 geometry for one query token).  The
 // units' tiles are laid end to end -- sequence after sequence, the U units
 // of a sequence one after another, each unit max(1, ceil(n_b / tile))
 // tiles preceded by `lead` tiles that stand for the fixed cost of starting a
@@ -300,7 +301,7 @@ ATTN_DEV EvenSeg even_segment(const EvenPlan& p, int x, int x1) {
 // only what it wrote itself, so no barrier is needed.
 struct EvenPlanLds {
   const int* lds;
-  int B, rounds, lead, total, groups;
+  int rounds, lead, total, groups;
 };
 
 ATTN_DEV EvenPlanLds even_plan_lds(const int32_t* seq_lens, int B, int T_cap, int window,
@@ -318,7 +319,7 @@ ATTN_DEV EvenPlanLds even_plan_lds(const int32_t* seq_lens, int B, int T_cap, in
       lds[2 * kBalanceMaxB + 64 * i + lane] = p.len[i];
     }
   }
-  return EvenPlanLds{lds, B, p.rounds, p.lead, p.total, p.groups};
+  return EvenPlanLds{lds, p.rounds, p.lead, p.total, p.groups};
 }
 
 ATTN_DEV int even_start(const EvenPlanLds& p, int w) {
