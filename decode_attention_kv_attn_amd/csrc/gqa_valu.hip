@@ -50,7 +50,7 @@
 #define ATTN_VALU_E_SMALL 16
 #endif
 #ifndef ATTN_VALU_WAVES  // waves per work group (upper bound)
-#define ATTN_VALU_WAVES 8
+#define ATTN_VALU_WAVES 4
 #endif
 #ifndef ATTN_VALU_NONTEMPORAL  // K/V are read once: stream past the caches
 #define ATTN_VALU_NONTEMPORAL 1
