@@ -38,13 +38,18 @@ int even_lead(int d) {
   return v >= 0 ? v : max(1, 1536 / d);
 }
 
-int target_groups() {
+// Work groups a split plan (and a balanced list) aims for: one per CU for
+// the matrix-core kernel, whose registers hold one group per CU; two per CU
+// for the vector kernel, whose groups of four waves leave room for two
+// (MHA B=1, 32768 rows: 85.0 us at one group per CU, 83.8 at two).
+// Overridable for tuning sweeps through ATTN_DECODE_TARGET_GROUPS.
+int target_groups(bool mfma) {
   static const int v = [] {
     const char* e = getenv("ATTN_DECODE_TARGET_GROUPS");
     const int x = e ? atoi(e) : 0;
-    return x > 0 ? x : kNumCUs;
+    return x > 0 ? x : 0;
   }();
-  return v;
+  return v > 0 ? v : (mfma ? kNumCUs : 2 * kNumCUs);
 }
 
 struct GqaPlan {
@@ -152,7 +157,7 @@ int plan_gqa(int B, int H_q, int H_kv, int T_cap, int d, int dtype, int window,
     S = num_splits;
   } else {
     const long long units = (long long)(B > 0 ? B : 1) * H_kv * p->head_chunks;
-    S = (target_groups() + units - 1) / units;
+    S = (target_groups(p->mfma) + units - 1) / units;
     // keep at least two tiles per wave
     long long smax = mv / ((long long)geo.waves * geo.tile_rows * 2);
     if (smax < 1) smax = 1;
@@ -181,8 +186,8 @@ int plan_gqa(int B, int H_q, int H_kv, int T_cap, int d, int dtype, int window,
                                (T_cap / mfma_tile_rows() + 1 + even_lead(d)) <
                            (1LL << 31);
   if (num_splits == 0 && p->S > 1 && !ring && B >= 1 && B <= kBalanceMaxB &&
-      target_groups() <= ATTN_MAX_SPLITS) {
-    p->cap = target_groups();
+      target_groups(p->mfma) <= ATTN_MAX_SPLITS) {
+    p->cap = target_groups(p->mfma);
     const size_t bb = balanced_bytes(*p, d, B);
     if (bb > p->ws_bytes) p->ws_bytes = bb;
   }
