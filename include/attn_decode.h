@@ -165,7 +165,9 @@ size_t attn_decode_gqa_workspace_bytes(int B, int H_q, int H_kv, int T_cap,
 
 /* How attn_decode_gqa and its _global / _paged / _multi forms would run a
  * call: which kernel, how the visible range is split, the launch shape and
- * the workspace it needs. */
+ * the workspace it needs.  The library fills the whole struct as declared
+ * here: a caller must use this header with the library built from it (new
+ * fields are added at the end). */
 typedef struct {
   int kernel;          /* 0 = vector-ALU kernel, 1 = matrix-core kernel      */
   int splits;          /* pieces of each visible range (1 = no combine pass) */
