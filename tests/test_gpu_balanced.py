@@ -120,6 +120,43 @@ def test_even_split_segments(mix, H_q, H_kv, d):
     assert_lse(lse2, rl2, f"even split {mix}, second call")
 
 
+def _random_case(rng):
+    """One random ragged batch that the planner sends to the matrix-core
+    kernel's even split (shapes are drawn again until it does)."""
+    while True:
+        d = int(rng.choice([64, 128]))
+        H_kv = int(rng.choice([1, 2, 4]))
+        n = int(rng.choice([3, 4, 8, 16, 32, 48]))
+        B = int(rng.choice([1, 2, 7, 33, 64, 130, 250]))
+        T = int(rng.choice([1000, 2048, 4096]))
+        plan = L.attn_decode_gqa_plan(B, H_kv * n, H_kv, T, d, 1)
+        if plan["even_split"]:
+            break
+    kinds = rng.integers(0, 4, size=B)
+    lens = np.where(kinds == 0, 0, np.where(kinds == 1, rng.integers(1, 40, size=B),
+                                            rng.integers(1, T + 1, size=B)))
+    return d, H_kv * n, H_kv, T, lens.astype(int).tolist()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_even_split_random(seed):
+    """Seeded random ragged batches (empty, one-row and long sequences mixed;
+    1 to 250 sequences, group sizes 3..48 -- one or two head chunks, d = 64
+    or 128) on the even split, against the oracle."""
+    rng = np.random.default_rng(32000 + seed)
+    d, H_q, H_kv, T, lens = _random_case(rng)
+    B = len(lens)
+    plan = L.attn_decode_gqa_plan(B, H_q, H_kv, T, d, 1)
+    q, k, v, sl = _inputs(lens, H_q, H_kv, T, d, 32100 + 7 * seed)
+    out, lse = L.attn_decode_gqa(q, k, v, sl)
+    torch.cuda.synchronize()
+    ro, rl = oracle.gqa_decode_ref(q, k, v, sl)
+    what = f"seed {seed}: B={B} {H_q}/{H_kv} d={d} T={T} plan={plan}"
+    print(what, flush=True)
+    assert_parity(out, ro, what)
+    assert_lse(lse, rl, what)
+
+
 def test_fp32_vector_kernel():
     """float32 data always takes the vector kernel: the same list, MQA-sized
     group of 8 columns per item (four items per KV head)."""
@@ -402,6 +439,30 @@ def test_mla_even_split_segments(mix):
     rz2, rl2 = oracle.mla_decode_ref(q, lat, 512, scale, sl2)
     assert_parity(z2, rz2, f"mla even split {mix}, second call")
     assert_lse(l2, rl2, f"mla even split {mix}, second call")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_mla_even_split_random(seed):
+    """Seeded random ragged batches on the (512, 64) geometry's even split
+    (1 to 130 sequences, empty and one-row ones mixed, 32 or 128 heads)."""
+    rng = np.random.default_rng(33000 + seed)
+    B = int(rng.choice([1, 3, 17, 64, 130]))
+    H = int(rng.choice([32, 128]))
+    T, dk = 2048, 576
+    kinds = rng.integers(0, 4, size=B)
+    lens = np.where(kinds == 0, 0, np.where(kinds == 1, rng.integers(1, 40, size=B),
+                                            rng.integers(1, T + 1, size=B))).astype(int)
+    q = synth.draw((B, H, dk), 33100 + seed, "bf16", DEV, dk ** -0.5)
+    lat = synth.draw((B, T, dk), 33200 + seed, "bf16", DEV, dk ** -0.5)
+    sl = torch.tensor(lens.tolist(), dtype=torch.int32, device=DEV)
+    scale = 192 ** -0.5
+    z, lse = L.attn_decode_mla(q, lat, 512, scale, sl)
+    torch.cuda.synchronize()
+    rz, rl = oracle.mla_decode_ref(q, lat, 512, scale, sl)
+    what = f"mla seed {seed}: B={B} H={H}"
+    print(what, flush=True)
+    assert_parity(z, rz, what)
+    assert_lse(lse, rl, what)
 
 
 def test_mla_paged_and_multi_token():
