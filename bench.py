@@ -41,8 +41,8 @@ SETTLE_S = 0.3  # seconds of untimed calls before the warmup (clock ramp-up)
 CPU_SAMPLE_BYTES = 2 << 30  # host copy of the CPU baseline's sample, at most
 KERNEL_SOURCES = {"gqa": ["gqa_valu.hip", "gqa_mfma.hip", "combine.hip", "balance.h",
                           "visible.h", "device_common.h", "internal.h"],
-                  "mla": ["mla_mfma.hip", "combine.hip", "balance.h", "visible.h",
-                          "device_common.h", "internal.h"]}
+                  "mla": ["mla_mfma.hip", "mla_pair.hip", "mla_common.h", "combine.hip",
+                          "balance.h", "visible.h", "device_common.h", "internal.h"]}
 MERGE_KERNEL = "lse_combine"
 
 
@@ -291,7 +291,7 @@ def record_traffic(args):
     import synth
     w = synth.workload(args.workload)
     kind = "mla" if w["kind"] == "mla" else "gqa"
-    decode = "mla_decode_mfma" if kind == "mla" else "gqa_decode_"
+    decode = "mla_" if kind == "mla" else "gqa_decode_"  # mla_pair_decode, mla_decode_mfma
     d = args.record_traffic
     if not args.copy_dir:
         sys.exit("--record-traffic needs --copy-dir: the --pmc runs of the plain copy")
@@ -511,6 +511,15 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def mla_kernel_name(w, inp, args):
+    """The decode kernel a call runs: the 512 + 64 latent's fixed splits go to
+    the role-split kernel, ragged batches (the balanced list) and the 256 + 64
+    latent to the shared-latent kernel."""
+    shared = os.environ.get("ATTN_DECODE_MLA_KERNEL", "")[:1] == "s"
+    fixed = inp["seq_lens"] is None or args.num_splits > 0 or w["B"] > 256
+    return "mla_pair_decode" if w["d_c"] == 512 and fixed and not shared else "mla_decode_mfma"
+
+
 def bench_mla(args, w, dev):
     """The absorbed-MLA workload: latent bytes (d_c + d_rope) * s per visible
     position (attention-head section 5.4, Bytes_MLA), both rooflines."""
@@ -554,7 +563,8 @@ def bench_mla(args, w, dev):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(value / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(w["name"], "mla"),
-                     "kernel": "mla_decode_mfma" + ("" if S == 1 else f" + {MERGE_KERNEL}_rows"),
+                     "kernel": mla_kernel_name(w, inp, args) +
+                               ("" if S == 1 else f" + {MERGE_KERNEL}_rows"),
                      "launches_per_step": 1 if S == 1 else 2,
                      "step_us": round(ms * 1e3, 2)},
         "mfma_roofline": {"achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,

@@ -25,7 +25,7 @@ OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn_decode.so")
 
 SOURCES = ["api.hip", "gqa_valu.hip", "gqa_valu_global.hip", "gqa_valu_paged.hip",
-           "gqa_mfma.hip", "combine.hip", "mla.hip", "mla_mfma.hip", "append.hip",
+           "gqa_mfma.hip", "combine.hip", "mla.hip", "mla_mfma.hip", "mla_pair.hip", "append.hip",
            "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

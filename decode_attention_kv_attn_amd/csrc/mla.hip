@@ -20,7 +20,10 @@ int check_mla(int B, int H, int T_cap, int d_c, int d_rope) {
 }
 
 struct MlaPlan {
-  int head_chunks, S, chunk;
+  int head_chunks;  // column chunks of the balanced list (shared-latent kernel)
+  int pair;         // 1: fixed splits run the role-split kernel (512 + 64)
+  int fixed_chunks; // column chunks of the fixed splits
+  int S, chunk;
   size_t ws_bytes;  // the larger of the two workspaces below
   size_t ws_fixed;  // fixed splits
   int cap;          // > 0: groups of the balanced list (calls with lengths)
@@ -28,6 +31,14 @@ struct MlaPlan {
 };
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Fixed splits of the 512 + 64 latent run the role-split kernel (64 columns
+// per group); ATTN_DECODE_MLA_KERNEL=shared keeps them on the shared-latent
+// kernel (for comparisons; read at every plan, so a process can hold both).
+bool mla_use_pair(int d_c) {
+  const char* e = getenv("ATTN_DECODE_MLA_KERNEL");
+  return d_c == 512 && !(e && e[0] == 's');
+}
 
 // Lead tiles per unit of the MLA even split: a segment's start (the query
 // fragments of 128 heads, three tiles of loads before the first tile can be
@@ -68,14 +79,18 @@ int plan_mla(int B, int H, int T_cap, int d_c, int d_rope, int num_splits,
   if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_ARG;
   const int hg = attn::mla_heads_per_group(d_c);
   p->head_chunks = (H + hg - 1) / hg;
+  p->pair = mla_use_pair(d_c) ? 1 : 0;
+  const int hf = p->pair ? attn::mla_pair_columns() : hg;
+  p->fixed_chunks = (H + hf - 1) / hf;
   long long S;
   if (num_splits > 0) {
     S = num_splits;
   } else {
     // fill every CU with the groups it holds at once; keep at least two
     // tiles per group
-    const long long units = (long long)(B > 0 ? B : 1) * p->head_chunks;
-    const long long target = (long long)attn::kNumCUs * attn::mla_groups_per_cu(d_c);
+    const long long units = (long long)(B > 0 ? B : 1) * p->fixed_chunks;
+    const long long target =
+        (long long)attn::kNumCUs * (p->pair ? 1 : attn::mla_groups_per_cu(d_c));
     S = (target + units - 1) / units;
     long long smax = T_cap / (2LL * attn::mla_tile_rows());
     if (smax < 1) smax = 1;
@@ -169,8 +184,19 @@ int decode_mla(const void* q, const void* latent, float* out, float* lse_out,
     o_part = (float*)workspace;
     lse_part = (float*)((char*)workspace + round_up(rows * d_c * sizeof(float), 256));
   }
-  if ((long long)B * p.S * p.head_chunks > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  if ((long long)B * p.S * p.fixed_chunks > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
+  if (!bal && p.pair) {
+    if (attn::launch_mla_pair(q, latent, out, lse_out, o_part, lse_part, seq_lens,
+                              block_table, max_pages, page_shift, num_pages, B, L, H, T_cap,
+                              p.S, p.chunk, p.fixed_chunks, scale * 1.4426950408889634f,
+                              s) != hipSuccess)
+      return ATTN_ERR_HIP;
+    if (p.S > 1 && attn::launch_combine_half(o_part, lse_part, out, lse_out, B, H * L, p.S,
+                                             d_c, s) != hipSuccess)
+      return ATTN_ERR_HIP;
+    return ATTN_OK;
+  }
   if (attn::launch_mla_mfma(q, latent, out, lse_out, o_part, lse_part, seq_lens,
                             block_table, max_pages, page_shift, num_pages, B, L, H,
                             T_cap, d_c, p.S, p.chunk, p.head_chunks,

@@ -330,14 +330,17 @@ size_t attn_decode_gqa_global_workspace_bytes(int B, int H_q, int H_kv,
  *   scale   must be > 0 and finite: 1/sqrt(d_head_content + d_rope) with the
  *           model's per-head content width (section 5.3 keeps that
  *           denominator; the latent width r does not enter it).
- *   Precision, (512, 64): scores and values are formed on the matrix cores
- *   in fp16: every bf16 value of q and the latent with 2^-14 <= |x| <= 65504
- *   converts exactly (smaller ones with an absolute error below 2^-25);
- *   entries beyond 65504 overflow and are outside the accepted range.  The
- *   softmax weights enter the value product rounded to fp16 (11 significant
- *   bits); accumulation is float32; when the call splits, each piece's
- *   normalised partial value (a weighted mean of latent values, so inside
- *   the same range) is stored in fp16 before the merge.  (256, 64): q and
+ *   Precision, (512, 64): the value product runs on the matrix cores in
+ *   fp16: every bf16 latent value with 2^-14 <= |x| <= 65504 converts
+ *   exactly (smaller ones with an absolute error below 2^-25); entries
+ *   beyond 65504 overflow and are outside the accepted range.  The scores
+ *   are exact bf16 products on fixed splits; with lengths that take the
+ *   balanced work list they are formed in fp16 too, under the same range
+ *   condition on q.  The softmax weights enter the value product rounded to
+ *   fp16 (11 significant bits); accumulation is float32; when the call
+ *   splits, each piece's normalised partial value (a weighted mean of latent
+ *   values, so inside the same range) is stored in fp16 before the merge.
+ *   (256, 64): q and
  *   the latent stay bf16 (exact products), the weights carry about 16
  *   significant bits (a bf16 high part plus a bf16 remainder), partials are
  *   float32.

@@ -7,7 +7,7 @@ import bench
 
 CSRC = os.path.join(bench.ROOT, "decode_attention_kv_attn_amd", "csrc")
 KERNELS = {"gqa": ["gqa_valu.hip", "gqa_mfma.hip", "combine.hip"],
-           "mla": ["mla_mfma.hip", "combine.hip"]}
+           "mla": ["mla_mfma.hip", "mla_pair.hip", "combine.hip"]}
 
 
 def local_includes(name, seen=None):
@@ -51,7 +51,7 @@ def test_traffic_records_are_consistent():
         c = t["copy_calibration"]
         assert abs(c["fetch_scale"] - c["bytes"] / (c["fetch_kib_raw"] * 1024)) < 1e-3
         assert abs(c["write_scale"] - c["bytes"] / (c["write_kib_raw"] * 1024)) < 1e-3
-        assert any(k.startswith(("gqa_decode_", "mla_decode_")) for k in t["kernels"])
+        assert any(k.startswith(("gqa_decode_", "mla_")) for k in t["kernels"])
         rd_sum = wr_sum = 0
         for k in t["kernels"].values():
             rd = k["fetch_kib_per_dispatch_raw"] * 1024 * c["fetch_scale"]

@@ -1,0 +1,99 @@
+"""GPU parity of the role-split MLA kernel (fixed splits of the 512 + 64
+latent) against the float64 oracle, and against the shared-latent kernel on
+the same fixed splits.  Calls with lengths take the balanced work list (the
+shared-latent kernel) whenever it applies, so these cases force a split count
+to reach the fixed-split path."""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_kv_attn_amd as L
+import oracle
+import synth
+from helpers import assert_lse, assert_parity, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+D_C, D_R = 512, 64
+SCALE = 1.0 / math.sqrt(128 + 64)
+
+
+def _case(B, H, T_cap, seed, lens, value_scale=1.0):
+    q = synth.draw((B, H, D_C + D_R), seed, "bf16", DEV, value_scale)
+    lat = synth.draw((B, T_cap, D_C + D_R), seed + 1, "bf16", DEV, value_scale)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    return q, lat, sl
+
+
+def _run(q, lat, sl, num_splits, kernel=None):
+    """attn_decode_mla with ATTN_DECODE_MLA_KERNEL set for the call only."""
+    old = os.environ.pop("ATTN_DECODE_MLA_KERNEL", None)
+    try:
+        if kernel is not None:
+            os.environ["ATTN_DECODE_MLA_KERNEL"] = kernel
+        z, lse = L.attn_decode_mla(q, lat, D_C, SCALE, sl, num_splits)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("ATTN_DECODE_MLA_KERNEL", None)
+        if old is not None:
+            os.environ["ATTN_DECODE_MLA_KERNEL"] = old
+    return z, lse
+
+
+@pytest.mark.parametrize("num_splits", [1, 3])
+def test_ragged_edges(num_splits):
+    """Empty, one-row, tile-edge and ragged-tail sequences; an empty sequence
+    gives z = 0 and lse = -inf."""
+    lens = [0, 1, 31, 32, 33, 64, 257]
+    q, lat, sl = _case(len(lens), 128, 257, 8500 + num_splits, lens)
+    z, lse = _run(q, lat, sl, num_splits)
+    rz, rl = oracle.mla_decode_ref(q, lat, D_C, SCALE, sl)
+    assert_parity(z, rz, f"ragged edges S={num_splits}")
+    assert_lse(lse, rl, "ragged edges")
+    assert torch.all(z[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
+@pytest.mark.parametrize("H", [16, 100, 128, 192, 256])
+def test_head_counts(H):
+    """One head chunk of 64 columns (16), a partly empty second chunk (100),
+    two, three and four chunks (the XCD placement of a unit's chunks)."""
+    q, lat, sl = _case(3, H, 600, 8600 + H, [600, 255, 97])
+    z, lse = _run(q, lat, sl, 2)
+    rz, rl = oracle.mla_decode_ref(q, lat, D_C, SCALE, sl)
+    assert_parity(z, rz, f"H={H}")
+    assert_lse(lse, rl, f"H={H}")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_batches(seed):
+    """Seeded batches: 1..40 sequences, lengths from 0 to the capacity, split
+    counts from 1 to 9 (pieces that end mid-tile or hold no row)."""
+    rng = np.random.default_rng(8700 + seed)
+    B = int(rng.integers(1, 41))
+    T = int(rng.integers(40, 700))
+    lens = rng.integers(0, T + 1, size=B)
+    lens[rng.random(B) < 0.15] = 0
+    S = int(rng.integers(1, 10))
+    q, lat, sl = _case(B, 128, T, 8800 + seed, lens.tolist())
+    z, lse = _run(q, lat, sl, S)
+    rz, rl = oracle.mla_decode_ref(q, lat, D_C, SCALE, sl)
+    assert_parity(z, rz, f"seed={seed} B={B} T={T} S={S}")
+    assert_lse(lse, rl, f"seed={seed}")
+
+
+def test_matches_shared_latent_kernel():
+    """The same fixed splits on both kernels: both within the oracle's
+    tolerance, and within that tolerance of each other."""
+    q, lat, sl = _case(5, 128, 1500, 8900, [1500, 1024, 700, 33, 1])
+    zp, lp = _run(q, lat, sl, 4)
+    zs, ls = _run(q, lat, sl, 4, kernel="shared")
+    rz, rl = oracle.mla_decode_ref(q, lat, D_C, SCALE, sl)
+    assert_parity(zp, rz, "role-split kernel")
+    assert_parity(zs, rz, "shared-latent kernel")
+    assert_lse(lp, rl, "role-split kernel")
+    assert_lse(ls, rl, "shared-latent kernel")
+    assert_parity(zp, to64(zs), "role-split against shared-latent")
