@@ -19,10 +19,11 @@
 //     scores of all 32 rows on v_mfma_f32_16x16x32_bf16 (exact products),
 //     the online softmax (lazy maximum), and the tile's weights written to
 //     LDS as fp16 value-product operands, with each column's rescale factor;
+//     they also issue the tile loads, between their score MFMAs;
 //   * four value waves, 128 output columns each for all 64 columns: the
 //     transposed latent values read through ds_read_b64_tr_b16, converted
 //     bf16 -> fp16 in registers, and v_mfma_f32_16x16x32_f16 with the
-//     weights; they also issue the tile loads.
+//     weights.
 //
 // Each SIMD runs one wave of each role, so one wave's LDS reads and softmax
 // overlap the other's matrix work.  The value waves trail the score waves by
@@ -215,7 +216,6 @@ __global__ __launch_bounds__(512) void mla_pair_decode(PairArgs a) {
       dma_16B(lat_b + row * kRowB, kTileB / 2, off,
               (uint32_t)(uintptr_t)(stage(dst) + blk * 1024));
     };
-
 
     // Scores of tile t; this wave's loads of tile t + 2 (into the stage tile
     // t - 2 has left; past the end a copy of the last tile, so that every
