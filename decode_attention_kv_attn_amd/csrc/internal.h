@@ -94,6 +94,14 @@ bool mla_half_parts(int d_c);
 // page_shift, and `chunk` a multiple of the tile rows.
 // balanced: 0 fixed splits, 1 the per-sequence list, 2 the even split
 // (only where mla_even_split(d_c); even_lead as GqaArgs::even_lead).
+hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
+                           float* lse, float* o_part, float* lse_part,
+                           const int32_t* seq_lens, const int32_t* block_table,
+                           int max_pages, int page_shift, int num_pages, int B,
+                           int L, int H, int T_cap, int d_c, int S, int chunk,
+                           int head_chunks, int balanced, int cap, int* meta,
+                           int even_lead, float scale_log2, hipStream_t stream);
+
 // The 512 + 64 latent with fixed splits: work groups of 64 (head, token)
 // columns split into score and value waves (mla_pair.hip); o_part holds fp16
 // partials [B * L * H, S, 512].
@@ -103,14 +111,6 @@ hipError_t launch_mla_pair(const void* q, const void* latent, float* out, float*
                            const int32_t* block_table, int max_pages, int page_shift,
                            int num_pages, int B, int L, int H, int T_cap, int S, int chunk,
                            int head_chunks, float scale_log2, hipStream_t stream);
-
-hipError_t launch_mla_mfma(const void* q, const void* latent, float* out,
-                           float* lse, float* o_part, float* lse_part,
-                           const int32_t* seq_lens, const int32_t* block_table,
-                           int max_pages, int page_shift, int num_pages, int B,
-                           int L, int H, int T_cap, int d_c, int S, int chunk,
-                           int head_chunks, int balanced, int cap, int* meta,
-                           int even_lead, float scale_log2, hipStream_t stream);
 // true where the geometry of latent width d_c runs the even split
 bool mla_even_split(int d_c);
 
