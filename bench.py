@@ -104,6 +104,8 @@ def traffic_from_profile(workload, kind="gqa"):
         return None
     rec = json.load(open(path))
     if rec.get("kernel_source_hash") != kernel_source_hash(kind):
+        print(f"bench: traffic_{workload}.json was taken on other kernel sources; "
+              "traffic is null until it is recorded again", file=sys.stderr, flush=True)
         return None
     return rec.get("bytes_per_step")
 

@@ -87,3 +87,11 @@ def test_sample_stride_bounds_the_host_copy():
     assert bench.sample_stride(2048, 16 << 20) == 16      # 128 units of 16 MiB
     assert bench.sample_stride(256, 4 << 20) == 1         # 1 GiB: all of it
     assert bench.sample_stride(1, 64 << 30) == 1
+
+
+def test_headline_traffic_record_is_current():
+    """The default workload's bench line reports HBM traffic only from a
+    record taken on the current kernel sources; any edit to a source the
+    hash covers must be followed by new counter passes (or, where the
+    compiled code is unchanged, a re-keyed record)."""
+    assert bench.traffic_from_profile(bench.DEFAULT_WORKLOAD, "gqa") is not None
