@@ -137,3 +137,18 @@ def test_graph_replays(num_splits):
         rz, rl = oracle.mla_decode_ref(q, lat, D_C, SCALE, sl)
         assert_parity(out, rz, f"replay {trial}")
         assert_lse(lse, rl, f"replay {trial}")
+
+
+def test_many_sequences():
+    """300 sequences (more than the balanced list takes, so ragged lengths
+    run fixed splits too): 600 work groups over 256 CUs, several rounds, and
+    a grid that is not a whole number of XCD rounds (the placement's tail)."""
+    rng = np.random.default_rng(9300)
+    B, T = 300, 96
+    lens = rng.integers(0, T + 1, size=B)
+    q, lat, sl = _case(B, 128, T, 9301, lens.tolist())
+    assert L.attn_decode_mla_splits(B, 128, T, D_C, D_R, 0) == 1
+    z, lse = _run(q, lat, sl, 0)
+    rz, rl = oracle.mla_decode_ref(q, lat, D_C, SCALE, sl)
+    assert_parity(z, rz, "B=300")
+    assert_lse(lse, rl, "B=300")
