@@ -152,3 +152,20 @@ def test_many_sequences():
     rz, rl = oracle.mla_decode_ref(q, lat, D_C, SCALE, sl)
     assert_parity(z, rz, "B=300")
     assert_lse(lse, rl, "B=300")
+
+
+def test_queries_beyond_fp16_range():
+    """On fixed splits the scores are exact bf16 products summed in fp32, so
+    query entries far outside fp16's range (here ~3e5) are accepted: the
+    softmax is then nearly one-hot and the output is the winning row's
+    values.  (Only the latent must lie in fp16's range.)"""
+    B, H, T = 2, 128, 700
+    q = synth.draw((B, H, D_C + D_R), 9400, "bf16", DEV, 3.0e5)
+    lat = synth.draw((B, T, D_C + D_R), 9401, "bf16", DEV, 1.0 / math.sqrt(576))
+    sl = torch.tensor([700, 333], dtype=torch.int32, device=DEV)
+    assert float(q.float().abs().max()) > 65504.0
+    z, lse = _run(q, lat, sl, 2)
+    rz, rl = oracle.mla_decode_ref(q, lat, D_C, SCALE, sl)
+    assert_parity(z, rz, "queries beyond fp16")
+    # lse ~ 1e5 in magnitude: fp32 holds it to about 1e-2
+    assert_lse(lse, rl, "queries beyond fp16", atol=5e-2)
